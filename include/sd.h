@@ -1,0 +1,203 @@
+/*
+ * sd.h - C ABI of the sparse-KV self-speculative decoding hot path (gfx950).
+ *
+ * The method is MagicDec's self-speculation with a compressed draft KV cache
+ * ("MagicDec: Breaking the Latency-Throughput Tradeoff for Long Context
+ * Generation with Speculative Decoding", deep notes on papercache.org) plus the
+ * modified rejection sampling round described in "Wann beschleunigt
+ * spekulatives Decoding das LLM-Serving?" (slavadubrov.com). Per round the
+ * draft attends over a budget of K selected cached tokens for gamma steps, the
+ * target verifies the gamma+1 candidate positions against the full cache in one
+ * batched pass, and acceptance keeps a prefix of the drafts plus one
+ * correction or bonus token.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. Shapes are listed
+ *    row-major; every tensor is dense in the layout given.
+ *  - Each call validates its arguments on the host, then enqueues kernels on
+ *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *    returns without synchronising. A failed validation returns a non-zero
+ *    status before any launch and before any write.
+ *  - The library allocates no memory and keeps no mutable global state; calls
+ *    are thread-safe and re-entrant. Scratch space is the caller's
+ *    `workspace` of at least the size its *_workspace_size function returns;
+ *    concurrent calls need distinct workspaces.
+ *  - Device-resident integers (page_table, kv_lens, idx, sel_lens,
+ *    draft_tokens) are the caller's responsibility and are not validated;
+ *    kernels clamp them into range so that bad values give wrong numbers,
+ *    not out-of-bounds accesses.
+ *  - Random numbers are inputs: the library draws none.
+ *  - Results are bitwise reproducible for a given input and shape.
+ *  - Errors from the HIP runtime at launch return SD_ERR_HIP; faults inside
+ *    kernels surface at the caller's next synchronisation.
+ */
+#ifndef SD_H_
+#define SD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SD_OK = 0,
+  SD_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size */
+  SD_ERR_UNSUPPORTED = 2, /* valid but not implemented (head_dim, dtype, rows) */
+  SD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  SD_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} sd_status;
+
+typedef enum { SD_BF16 = 0, SD_F32 = 1 } sd_dtype;
+
+/*
+ * One layer's paged KV cache, read-only for every call here.
+ * k_pages, v_pages: [num_pages, num_kv_heads, page_size, head_dim] of dtype;
+ *   each (page, head) block of page_size * head_dim elements is contiguous.
+ * page_table: int32 [batch, max_pages]; token t of sequence b lives in page
+ *   page_table[b*max_pages + t/page_size] at slot t % page_size.
+ * kv_lens: int32 [batch] valid tokens per sequence (for verify this count
+ *   includes the n_q tokens being verified).
+ * page_size must be a multiple of 16; head_dim 64 or 128.
+ */
+typedef struct {
+  const void *k_pages;
+  const void *v_pages;
+  const int32_t *page_table;
+  const int32_t *kv_lens;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* sd_dtype */
+} sd_kv_cache;
+
+/*
+ * Verify attention (MagicDec notes, §3.1-§3.2: the target scores the gamma
+ * drafted positions plus one in a single batched pass over the full KV cache,
+ * so verification and decoding share the same KV loading cost).
+ *
+ * q: [batch, n_q, num_q_heads, head_dim] of kv->dtype, n_q = gamma + 1; the
+ *   n_q verify tokens are the last n_q tokens of each sequence's cache and
+ *   query i (0-based) attends causally to positions 0 .. kv_len - n_q + i.
+ * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * softmax_scale multiplies q.k (pass 1.0 when the scale is folded into q).
+ * max_kv_len: an upper bound on kv_lens (sizes the split-KV plan; must not
+ *   exceed max_pages * page_size).
+ * out: [batch, n_q, num_q_heads, head_dim] of kv->dtype (bf16 results are
+ *   rounded to nearest even). lse: [batch, n_q, num_q_heads] float32 natural-
+ *   log log-sum-exp of the scaled scores, or NULL. A row that sees no key gets
+ *   out = 0 and lse = -inf.
+ * Limits: (num_q_heads / num_kv_heads) * n_q <= 64.
+ */
+sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
+                         int32_t num_q_heads, int32_t max_kv_len, float softmax_scale,
+                         void *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+size_t sd_verify_attn_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_kv_len);
+
+/*
+ * Draft attention over a compressed KV budget (MagicDec notes, §3.3 and §4.1:
+ * the self-speculative draft is the target model attending to a sparse subset
+ * of its own KV cache, at a cost that grows with the budget K, not with the
+ * context).
+ *
+ * idx: int32 [batch, idx_heads, max_sel] cached positions; idx_heads is 1 (one
+ *   set for all KV heads, as StreamingLLM selects) or num_kv_heads (one set per
+ *   KV head, as SnapKV selects). Sequence b, KV head g uses the first
+ *   sel_lens[b] entries of idx[b, idx_heads > 1 ? g : 0, :].
+ * Every query row attends to every selected position (q: [batch, n_q,
+ *   num_q_heads, head_dim], normally n_q = 1). out/lse as for verify.
+ * Limits: (num_q_heads / num_kv_heads) * n_q <= 64.
+ */
+sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
+                               int32_t num_q_heads, const int32_t *idx, const int32_t *sel_lens,
+                               int32_t idx_heads, int32_t max_sel, float softmax_scale, void *out,
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+size_t sd_draft_attn_sparse_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_sel);
+
+/*
+ * StreamingLLM draft set (named as a static KV selection in the MagicDec
+ * notes, §4.4 and §5.2): the first `sink` positions and the last `recent`
+ * positions of each sequence, ascending, without duplicates:
+ *   [0, min(sink, L)) U [max(sink, L - recent), L).
+ * idx: int32 [batch, 1, sink + recent] (entries past sel_lens[b] are -1);
+ * sel_lens: int32 [batch] = min(L, sink + recent).
+ */
+sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, int32_t sink,
+                              int32_t recent, int32_t *idx, int32_t *sel_lens, void *stream);
+
+/*
+ * SnapKV draft set (named as the best static KV selection in the MagicDec
+ * notes, §4.4 and §5.2; built once at prefill and reused for drafting,
+ * Appendix A.1). Per (sequence b, KV head g) with L = kv_lens[b]:
+ *  1. the last `window` prompt positions are the observation window;
+ *     q_obs[b, w, h] (w < window, h in g's query-head group) attends causally
+ *     to keys 0 .. L - window + w with softmax weights p;
+ *  2. vote_j = sum over the group's heads and the window rows of p, j < L - window;
+ *  3. votes are max-pooled with odd kernel `pool_kernel`, stride 1, clipped;
+ *  4. the budget - window prefix positions with the largest pooled value are
+ *     kept, ties toward the lower position;
+ *  5. idx[b, g, :] = ascending union of those and the window (budget entries).
+ *  If L <= budget every position 0..L-1 is kept (rest -1).
+ * q_obs: [batch, window, num_q_heads, head_dim] of kv->dtype.
+ * idx: int32 [batch, num_kv_heads, budget]; sel_lens: int32 [batch] = min(L, budget).
+ * Limits: budget > window >= 1; (num_q_heads / num_kv_heads) * window <= 128;
+ *   pool_kernel odd and >= 1; max_kv_len bounds kv_lens.
+ */
+sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                           int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                           int32_t budget, int32_t max_kv_len, float softmax_scale,
+                           int32_t *idx, int32_t *sel_lens, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t max_kv_len);
+
+/*
+ * Modified rejection sampling for one verification round ("Wann beschleunigt
+ * spekulatives Decoding das LLM-Serving?", section on a verification round):
+ * per sequence, with p_i = softmax(target_logits[b, i] / temperature) and
+ * q_i = softmax(draft_logits[b, i] / temperature):
+ *  - for i = 0..gamma-1, draft token x_i is accepted iff
+ *    u_accept[b, i] * q_i(x_i) < p_i(x_i); stop at the first rejection; n = count;
+ *  - the emitted token y is drawn from max(0, p_n - q_n) normalised (or from
+ *    p_n if that is identically zero) when n < gamma, else from p_gamma (bonus):
+ *    y = smallest t with cumulative weight > u_sample[b, n] * total.
+ * target_logits: float32 [batch, gamma+1, vocab]; draft_logits: float32
+ *   [batch, gamma, vocab]; draft_tokens: int32 [batch, gamma];
+ *   u_accept: float32 [batch, gamma], u_sample: float32 [batch, gamma+1],
+ *   uniforms in [0, 1).
+ * n_accepted: int32 [batch]; out_tokens: int32 [batch, gamma+1] =
+ *   [x_0 .. x_{n-1}, y, -1 ...].
+ * Softmax exponentials are float32; normalisers and cumulative sums are
+ *   accumulated in float64.
+ * Limits: gamma >= 0, vocab >= 1, temperature > 0.
+ */
+sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
+                         const int32_t *draft_tokens, const float *u_accept,
+                         const float *u_sample, int32_t batch, int32_t gamma, int32_t vocab,
+                         float temperature, int32_t *n_accepted, int32_t *out_tokens,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab);
+
+/* Static string for a status code (never NULL). */
+const char *sd_status_string(sd_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t sd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H_ */

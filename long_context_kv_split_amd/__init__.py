@@ -1,0 +1,35 @@
+"""MI355X (gfx950) hot path of MagicDec-style sparse-KV self-speculative decoding.
+
+The computation lives in libsdkv.so, a HIP library with the C ABI of
+include/sd.h: verify attention over a paged bf16 KV cache (split-KV MFMA
+kernel plus combine), sparse draft attention over gathered positions,
+StreamingLLM and SnapKV draft-KV selection, and modified-rejection speculative
+acceptance. This package is its ctypes binding (argument marshalling only) and
+its build script; importing it never computes anything on the CPU.
+"""
+from long_context_kv_split_amd.binding import (  # noqa: F401
+    KVCache,
+    LIB_PATH,
+    SD_BF16,
+    SD_ERR_HIP,
+    SD_ERR_INVALID_ARG,
+    SD_ERR_UNSUPPORTED,
+    SD_ERR_WORKSPACE,
+    SD_F32,
+    SD_OK,
+    SdError,
+    lib,
+    sd_draft_attn_sparse,
+    sd_draft_attn_sparse_workspace_size,
+    sd_kv_cache,
+    sd_snapkv_select,
+    sd_snapkv_select_workspace_size,
+    sd_spec_accept,
+    sd_spec_accept_workspace_size,
+    sd_streaming_select,
+    sd_verify_attn,
+    sd_verify_attn_workspace_size,
+    status_string,
+    version,
+    workspace,
+)

@@ -1,0 +1,88 @@
+// Device helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// bf16 packing and wave-level reductions. Only the HIP library includes this.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdk {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short short4v;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// 16x16x32 bf16 MFMA: lane l supplies A[m = l%16][8 k-values] and
+// B[8 k-values][n = l%16]; both operands use the same lane->k assignment, so
+// any consistent split of the reduction axis over lanes is valid.
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16x16x16 bf16 MFMA: lane l supplies A[m = l%16][k = 4(l/16) .. +3] and
+// B[k = 4(l/16) .. +3][n = l%16] (element e of the packed pair-of-dwords is k = 4(l/16)+e).
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+
+// 16x16x4 f32 MFMA: lane l supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16].
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// In all three, the accumulator of lane l holds C[m = 4(l/16) + e][n = l%16], e = 0..3.
+
+// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Pack two floats as bf16 (lo in bits 0-15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+// Two 16-bit halves taken from two dwords: the low halves (hi_half=false) or
+// the high halves (hi_half=true); x supplies bits 0-15 of the result, y 16-31.
+__device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, bool hi_half) {
+  return __builtin_amdgcn_perm(y, x, hi_half ? 0x07060302u : 0x05040100u);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// Sum over the 16 lanes of each row of the wave (lanes 16k .. 16k+15).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace sdk

@@ -1,0 +1,499 @@
+// Static draft-KV selection on gfx950: StreamingLLM window and SnapKV.
+//
+// MagicDec (deep notes on papercache.org, §4.4, §5.2, Appendix A.1) drafts
+// with a static compressed KV cache built once at prefill, chosen by
+// StreamingLLM (sink + recent tokens) or SnapKV (observation-window attention
+// votes). SnapKV runs in three kernels:
+//   1. snap_stats:  per (sequence, KV head, chunk of keys) the online max and
+//      sum of exp2 of every window row's scaled scores (causal over the last
+//      W keys), S^T = K Q^T on 16x16x32 bf16 MFMA, one wave per unit;
+//   2. snap_votes:  merge the chunk statistics into each row's (max, 1/sum),
+//      recompute the scores of the prefix keys, normalise, and sum the
+//      probabilities over the window rows of the group (in-lane over row
+//      tiles, then over the 16 lanes of each MFMA column group);
+//   3. snap_topk:   one 1024-thread block per (sequence, KV head): clipped
+//      max-pool of the votes, 4-pass 8-bit radix select of the
+//      (budget - W)-th largest pooled value (non-negative floats order as
+//      their bit patterns), an order-preserving block compaction that takes
+//      every value above the threshold and the lowest positions among the
+//      ties, then the window positions appended (already ascending).
+#include "sd_device.h"
+#include "sd_host.h"
+
+#include <algorithm>
+
+using namespace sdk;
+
+namespace {
+
+constexpr int kStepTokens = 16;
+constexpr int kSnapTargetWaves = 8192;
+constexpr int kTopkThreads = 1024;
+
+// ---------------------------------------------------------------- StreamingLLM
+__global__ __launch_bounds__(256) void streaming_select_kernel(const int32_t *kv_lens, int sink,
+                                                               int recent, int32_t *idx,
+                                                               int32_t *sel_lens) {
+  const int b = blockIdx.x;
+  const int L = max(0, kv_lens[b]);
+  const int n_sink = min(sink, L);
+  const int start_recent = max(sink, L - recent);
+  const int n_recent = max(0, L - start_recent);
+  const int n = n_sink + n_recent;
+  const int cap = sink + recent;
+  for (int t = threadIdx.x; t < cap; t += blockDim.x) {
+    int v = -1;
+    if (t < n_sink)
+      v = t;
+    else if (t < n)
+      v = start_recent + (t - n_sink);
+    idx[(size_t)b * cap + t] = v;
+  }
+  if (threadIdx.x == 0) sel_lens[b] = n;
+}
+
+// ---------------------------------------------------------------- SnapKV
+struct SnapParams {
+  const void *k_pages;
+  const int32_t *page_table;
+  const int32_t *kv_lens;
+  const void *q_obs;  // [B, W, Hq, D]
+  float *stats;       // [B*Hkv*max_chunks, rows, 2]  (m, l) log2 domain
+  float *votes;       // [B*Hkv, vote_stride]
+  float *pooled;      // [B*Hkv, vote_stride]
+  int32_t *idx;       // [B, Hkv, budget]
+  int32_t *sel_lens;  // [B]
+  int32_t W, Hq, Hkv, G, rows;
+  int32_t num_pages, page_size, max_pages;
+  int32_t len_cap, vote_stride;
+  int32_t chunk_steps, max_chunks;
+  int32_t pool_kernel, budget;
+  float scale_log2;
+};
+
+template <int D>
+__device__ __forceinline__ void snap_load_k(const SnapParams &a, int b, int kvh, int s,
+                                            u32x4 (&k)[D / 32]) {
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const int pos = s * kStepTokens + r;
+  int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
+  page = clampi(page, 0, a.num_pages - 1);
+  const size_t row = ((size_t)page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
+  const char *kb = reinterpret_cast<const char *>(a.k_pages) + row * D * 2;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    k[kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void snap_load_q(const SnapParams &a, int b, int kvh,
+                                            u32x4 (&q)[NB][D / 32]) {
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int R = rb * 16 + r;  // row R = w * G + hl
+    const bool live = R < a.rows;
+    const int w = live ? R / a.G : 0, hl = live ? R % a.G : 0;
+    const char *qb = reinterpret_cast<const char *>(a.q_obs) +
+                     ((((size_t)b * a.W + w) * a.Hq + (size_t)kvh * a.G + hl) * D) * 2;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (live) v = *reinterpret_cast<const u32x4 *>(qb + (32 * kk + 8 * g) * 2);
+      q[rb][kk] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void merge_ml(float &m, float &l, float m2, float l2) {
+  const float M = fmaxf(m, m2);
+  if (M == kNegInf) return;
+  l = (m == kNegInf ? 0.f : l * __builtin_amdgcn_exp2f(m - M)) +
+      (m2 == kNegInf ? 0.f : l2 * __builtin_amdgcn_exp2f(m2 - M));
+  m = M;
+}
+
+// Pass 1: per (b, kvh, chunk) row statistics over keys [0, L).
+template <int D, int NB>
+__global__ __launch_bounds__(64) void snap_stats_kernel(SnapParams a) {
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  int unit = blockIdx.x;
+  const int chunk = unit % a.max_chunks;
+  unit /= a.max_chunks;
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  if (L <= a.budget) return;  // everything is kept; no scoring needed
+  const int n_steps = (L + kStepTokens - 1) / kStepTokens;
+  const int s_begin = chunk * a.chunk_steps;
+  if (s_begin >= n_steps) return;
+  const int s_end = min(n_steps, s_begin + a.chunk_steps);
+
+  u32x4 q[NB][D / 32];
+  snap_load_q<D, NB>(a, b, kvh, q);
+  int lim[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int R = rb * 16 + r;
+    lim[rb] = R < a.rows ? L - a.W + R / a.G : L - 1;
+  }
+  const int lim_min = L - a.W;
+
+  float m[NB], l[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
+  }
+  u32x4 cur[D / 32], nxt[D / 32];
+  snap_load_k<D>(a, b, kvh, s_begin, cur);
+  for (int s = s_begin; s < s_end; ++s) {
+    if (s + 1 < s_end) snap_load_k<D>(a, b, kvh, s + 1, nxt);
+    const int tok0 = s * kStepTokens;
+    const bool boundary = tok0 + kStepTokens - 1 > lim_min;
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(cur[kk], q[rb][kk], sc);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = sc[e] * a.scale_log2;
+      if (boundary) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tok0 + 4 * g + e > lim[rb]) p[e] = kNegInf;
+      }
+      const float pm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+      if (pm > m[rb]) {
+        l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
+        m[rb] = pm;
+      }
+      if (m[rb] != kNegInf) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(p[e] - m[rb]);
+      }
+    }
+    if (s + 1 < s_end) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
+    }
+  }
+  const size_t uc = ((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk;
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    float mm = m[rb], ll = l[rb];
+    merge_ml(mm, ll, __shfl_xor(mm, 16, 64), __shfl_xor(ll, 16, 64));
+    merge_ml(mm, ll, __shfl_xor(mm, 32, 64), __shfl_xor(ll, 32, 64));
+    const int R = rb * 16 + r;
+    if (g == 0 && R < a.rows) {
+      a.stats[(uc * a.rows + R) * 2 + 0] = mm;
+      a.stats[(uc * a.rows + R) * 2 + 1] = ll;
+    }
+  }
+}
+
+// Pass 2: votes for the prefix keys [0, L - W).
+template <int D, int NB>
+__global__ __launch_bounds__(64) void snap_votes_kernel(SnapParams a) {
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  int unit = blockIdx.x;
+  const int chunk = unit % a.max_chunks;
+  unit /= a.max_chunks;
+  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  if (L <= a.budget) return;
+  const int npre = L - a.W;
+  const int n_steps = (npre + kStepTokens - 1) / kStepTokens;
+  const int s_begin = chunk * a.chunk_steps;
+  if (s_begin >= n_steps) return;
+  const int s_end = min(n_steps, s_begin + a.chunk_steps);
+
+  // Global row statistics from pass 1 (its chunks cover [0, L)).
+  const int n_chunks1 = ((L + kStepTokens - 1) / kStepTokens + a.chunk_steps - 1) / a.chunk_steps;
+  const size_t uc0 = ((size_t)b * a.Hkv + kvh) * a.max_chunks;
+  float mrow[NB], inv_l[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int R = rb * 16 + r;
+    float mm = kNegInf, ll = 0.f;
+    if (R < a.rows) {
+      for (int c = 0; c < n_chunks1; ++c)
+        merge_ml(mm, ll, a.stats[((uc0 + c) * a.rows + R) * 2], a.stats[((uc0 + c) * a.rows + R) * 2 + 1]);
+    }
+    mrow[rb] = (mm == kNegInf) ? 0.f : mm;
+    inv_l[rb] = (ll > 0.f) ? 1.f / ll : 0.f;
+  }
+
+  u32x4 q[NB][D / 32];
+  snap_load_q<D, NB>(a, b, kvh, q);
+  float *vrow = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  u32x4 cur[D / 32], nxt[D / 32];
+  snap_load_k<D>(a, b, kvh, s_begin, cur);
+  for (int s = s_begin; s < s_end; ++s) {
+    if (s + 1 < s_end) snap_load_k<D>(a, b, kvh, s + 1, nxt);
+    float colsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(cur[kk], q[rb][kk], sc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        colsum[e] += __builtin_amdgcn_exp2f(sc[e] * a.scale_log2 - mrow[rb]) * inv_l[rb];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) colsum[e] = row16_sum(colsum[e]);
+    const int tok = s * kStepTokens + 4 * g + r;  // lanes r = 0..3 of group g write token 4g+r
+    if (r < 4 && tok < npre) vrow[tok] = colsum[r];
+    if (s + 1 < s_end) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
+    }
+  }
+}
+
+// Block-wide exclusive scan of one uint32 per thread (1024 threads); returns the
+// exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *lds_waves,
+                                                         uint32_t *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < kTopkThreads / 64 ? lds_waves[lane] : 0u;
+    uint32_t ws = w;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint32_t y = __shfl_up(ws, o, 64);
+      if (lane >= o) ws += y;
+    }
+    if (lane < kTopkThreads / 64) lds_waves[16 + lane] = ws - w;  // exclusive wave offsets
+    if (lane == kTopkThreads / 64 - 1) lds_waves[32] = ws;
+  }
+  __syncthreads();
+  const uint32_t res = lds_waves[16 + wave] + x - v;
+  *total = lds_waves[32];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void snap_topk_kernel(SnapParams a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scan_tmp[40];
+  __shared__ uint32_t sel_digit, sel_above;
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
+  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
+  if (L <= a.budget) {
+    for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
+    return;
+  }
+  const int npre = L - a.W;
+  const int keep = a.budget - a.W;
+  const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  float *pooled = a.pooled + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  const int half = a.pool_kernel / 2;
+
+  for (int j = tid; j < npre; j += kTopkThreads) {
+    const int lo = max(0, j - half), hi = min(npre - 1, j + half);
+    float v = votes[lo];
+    for (int t = lo + 1; t <= hi; ++t) v = fmaxf(v, votes[t]);
+    pooled[j] = v;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // Radix select of the keep-th largest key (bit pattern of a non-negative float).
+  uint32_t prefix = 0, mask = 0;
+  uint32_t k_rem = (uint32_t)keep;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < npre; j += kTopkThreads) {
+      const uint32_t key = __float_as_uint(pooled[j]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane owns bins 4*lane .. 4*lane+3; count of keys in bins above each
+      uint32_t c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = hist[4 * tid + e];
+      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+      uint32_t incl = mine;  // inclusive suffix sum over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(incl, o, 64);
+        if (tid + o < 64) incl += y;
+      }
+      uint32_t above = incl - mine;  // keys in bins of higher lanes
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        if (above < k_rem && above + c[e] >= k_rem) {
+          sel_digit = 4 * tid + e;
+          sel_above = above;
+        }
+        above += c[e];
+      }
+    }
+    __syncthreads();
+    prefix |= sel_digit << shift;
+    mask |= 255u << shift;
+    k_rem -= sel_above;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // key of the keep-th largest value
+  const uint32_t need_eq = k_rem;  // how many keys equal to thr are taken
+
+  // Order-preserving compaction: every key > thr, and the first need_eq keys == thr.
+  uint32_t eq_carry = 0, out_carry = 0;
+  for (int base = 0; base < npre; base += kTopkThreads) {
+    const int j = base + tid;
+    const uint32_t key = j < npre ? __float_as_uint(pooled[j]) : 0u;
+    const bool valid = j < npre;
+    const bool gt = valid && key > thr;
+    const bool eq = valid && key == thr;
+    uint32_t eq_total;
+    const uint32_t eq_rank = block_exclusive_scan(eq ? 1u : 0u, scan_tmp, &eq_total) + eq_carry;
+    const bool take = gt || (eq && eq_rank < need_eq);
+    uint32_t take_total;
+    const uint32_t pos = block_exclusive_scan(take ? 1u : 0u, scan_tmp, &take_total) + out_carry;
+    if (take && pos < (uint32_t)keep) out[pos] = j;
+    eq_carry += eq_total;
+    out_carry += take_total;
+  }
+  for (int w = tid; w < a.W; w += kTopkThreads) out[keep + w] = npre + w;
+}
+
+struct SnapPlan {
+  int chunk_steps, max_chunks, vote_stride;
+  size_t stats_bytes, votes_bytes, pooled_bytes, ws_bytes;
+};
+
+SnapPlan plan_snap(int64_t B, int64_t Hkv, int64_t rows, int64_t max_len) {
+  SnapPlan p;
+  const int64_t steps = std::max<int64_t>(1, sdh::ceil_div(max_len, kStepTokens));
+  const int64_t units = B * Hkv;
+  int64_t cs = sdh::ceil_div(steps * units, kSnapTargetWaves);
+  cs = std::max<int64_t>(cs, 16);
+  cs = std::min<int64_t>(cs, steps);
+  p.chunk_steps = (int)cs;
+  p.max_chunks = (int)sdh::ceil_div(steps, cs);
+  p.vote_stride = (int)std::max<int64_t>(1, max_len);
+  p.stats_bytes = sdh::align_up((size_t)units * p.max_chunks * rows * 2 * 4);
+  p.votes_bytes = sdh::align_up((size_t)units * p.vote_stride * 4);
+  p.pooled_bytes = p.votes_bytes;
+  p.ws_bytes = p.stats_bytes + p.votes_bytes + p.pooled_bytes;
+  return p;
+}
+
+template <int D, int NB>
+void launch_snap_pair(const SnapParams &a, unsigned grid, hipStream_t st) {
+  snap_stats_kernel<D, NB><<<grid, 64, 0, st>>>(a);
+  snap_votes_kernel<D, NB><<<grid, 64, 0, st>>>(a);
+}
+
+template <int D>
+sd_status launch_snap(const SnapParams &a, int B, hipStream_t st) {
+  const unsigned grid = (unsigned)((size_t)B * a.Hkv * a.max_chunks);
+  switch ((a.rows + 15) / 16) {
+    case 1: launch_snap_pair<D, 1>(a, grid, st); break;
+    case 2: launch_snap_pair<D, 2>(a, grid, st); break;
+    case 3: launch_snap_pair<D, 3>(a, grid, st); break;
+    case 4: launch_snap_pair<D, 4>(a, grid, st); break;
+    case 5: launch_snap_pair<D, 5>(a, grid, st); break;
+    case 6: launch_snap_pair<D, 6>(a, grid, st); break;
+    case 7: launch_snap_pair<D, 7>(a, grid, st); break;
+    case 8: launch_snap_pair<D, 8>(a, grid, st); break;
+    default: return SD_ERR_UNSUPPORTED;
+  }
+  snap_topk_kernel<<<(unsigned)(B * a.Hkv), kTopkThreads, 0, st>>>(a);
+  return sdh::launch_status();
+}
+
+}  // namespace
+
+extern "C" sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, int32_t sink,
+                                         int32_t recent, int32_t *idx, int32_t *sel_lens,
+                                         void *stream) {
+  SD_REQUIRE(kv_lens != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(batch > 0 && sink >= 0 && recent >= 0 && sink + recent > 0, SD_ERR_INVALID_ARG);
+  streaming_select_kernel<<<(unsigned)batch, 256, 0, sdh::as_stream(stream)>>>(kv_lens, sink, recent,
+                                                                              idx, sel_lens);
+  return sdh::launch_status();
+}
+
+extern "C" size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window,
+                                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t max_kv_len) {
+  if (batch <= 0 || window <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_kv_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int rows = num_q_heads / num_kv_heads * window;
+  return plan_snap(batch, num_kv_heads, rows, max_kv_len).ws_bytes;
+}
+
+extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                                      int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                                      int32_t budget, int32_t max_kv_len, float softmax_scale,
+                                      int32_t *idx, int32_t *sel_lens, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  sd_status s = sdh::check_kv(kv, false);
+  if (s != SD_OK) return s;
+  SD_REQUIRE(q_obs != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(batch > 0 && window >= 1 && num_q_heads > 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(budget > window, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(pool_kernel >= 1 && (pool_kernel & 1) == 1, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
+             SD_ERR_INVALID_ARG);
+  SD_REQUIRE(softmax_scale == softmax_scale, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(kv->dtype == SD_BF16, SD_ERR_UNSUPPORTED);
+  const int G = num_q_heads / kv->num_kv_heads;
+  SD_REQUIRE((int64_t)G * window <= 128, SD_ERR_UNSUPPORTED);
+  const int rows = G * window;
+  SnapPlan p = plan_snap(batch, kv->num_kv_heads, rows, max_kv_len);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
+
+  SnapParams a{};
+  a.k_pages = kv->k_pages;
+  a.page_table = kv->page_table;
+  a.kv_lens = kv->kv_lens;
+  a.q_obs = q_obs;
+  char *ws = reinterpret_cast<char *>(workspace);
+  a.stats = reinterpret_cast<float *>(ws);
+  a.votes = reinterpret_cast<float *>(ws + p.stats_bytes);
+  a.pooled = reinterpret_cast<float *>(ws + p.stats_bytes + p.votes_bytes);
+  a.idx = idx;
+  a.sel_lens = sel_lens;
+  a.W = window;
+  a.Hq = num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = G;
+  a.rows = rows;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages;
+  a.len_cap = max_kv_len;
+  a.vote_stride = p.vote_stride;
+  a.chunk_steps = p.chunk_steps;
+  a.max_chunks = p.max_chunks;
+  a.pool_kernel = pool_kernel;
+  a.budget = budget;
+  a.scale_log2 = softmax_scale * kLog2e;
+  hipStream_t st = sdh::as_stream(stream);
+  if (kv->head_dim == 128) return launch_snap<128>(a, batch, st);
+  return launch_snap<64>(a, batch, st);
+}

@@ -1,0 +1,191 @@
+"""CPU checks of the C ABI: the library loads, exports every function sd.h
+declares, and rejects invalid arguments on the host before any launch.
+
+Every call below carries at least one argument the host validation rejects,
+so no kernel is ever launched (the argument checks run before any HIP call).
+The validation cases only run where no GPU is visible, so a validation bug can
+never send the fake pointers used here to a real device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import long_context_kv_split_amd as sd
+from long_context_kv_split_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="host-validation cases run only where no GPU is visible")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from long_context_kv_split_amd.build import build
+        build()
+    return sd.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sd_status|size_t|const char \*|int32_t)\s*\*?\s*(sd_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    assert names == sorted(binding._SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert sd.version() == 100
+    for code in range(5):
+        assert sd.status_string(code).startswith("SD_")
+    assert "UNKNOWN" in sd.status_string(99)
+
+
+def test_workspace_sizes_are_host_only_and_consistent(L):
+    v = sd.sd_verify_attn_workspace_size(128, 5, 32, 8, 128, 32768)
+    assert v > 0 and v % 256 == 0
+    # partial outputs stay a small fraction of the 17.2 GB of KV this shape reads
+    assert v < 0.03 * 128 * 32768 * 8 * 128 * 2 * 2
+    assert sd.sd_verify_attn_workspace_size(0, 5, 32, 8, 128, 32768) == 0
+    assert sd.sd_verify_attn_workspace_size(2, 4, 9, 2, 64, 256) == 0   # Hq % Hkv != 0
+    assert sd.sd_draft_attn_sparse_workspace_size(32, 1, 32, 8, 128, 512) > 0
+    s = sd.sd_snapkv_select_workspace_size(128, 32, 32, 8, 32768)
+    assert s >= 2 * 128 * 8 * 32768 * 4          # votes + pooled values
+    assert sd.sd_snapkv_select_workspace_size(1, 0, 32, 8, 100) == 0
+    a = sd.sd_spec_accept_workspace_size(64, 4, 128256)
+    assert a > 0 and sd.sd_spec_accept_workspace_size(64, -1, 10) == 0
+
+
+def _kv(**over):
+    s = binding.sd_kv_cache()
+    s.k_pages = 0x1000
+    s.v_pages = 0x2000
+    s.page_table = 0x3000
+    s.kv_lens = 0x4000
+    s.num_pages, s.page_size, s.max_pages, s.num_kv_heads, s.head_dim = 10, 16, 4, 2, 128
+    s.dtype = binding.SD_BF16
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = ctypes.c_void_p(0x5000)
+WS = ctypes.c_void_p(0x6000)
+
+
+@no_gpu
+@pytest.mark.parametrize("over,args,want", [
+    ({}, dict(q=None), sd.SD_ERR_INVALID_ARG),
+    ({"k_pages": None}, {}, sd.SD_ERR_INVALID_ARG),
+    ({"head_dim": 96}, {}, sd.SD_ERR_UNSUPPORTED),
+    ({"page_size": 8}, {}, sd.SD_ERR_UNSUPPORTED),
+    ({"dtype": 7}, {}, sd.SD_ERR_UNSUPPORTED),
+    ({"num_pages": 0}, {}, sd.SD_ERR_INVALID_ARG),
+    ({}, dict(hq=9), sd.SD_ERR_INVALID_ARG),          # Hq % Hkv != 0
+    ({}, dict(n_q=40), sd.SD_ERR_UNSUPPORTED),        # G * n_q > 64
+    ({}, dict(batch=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(max_len=65), sd.SD_ERR_INVALID_ARG),    # > max_pages * page_size
+    ({}, dict(ws=None), sd.SD_ERR_WORKSPACE),
+    ({}, dict(ws_bytes=1), sd.SD_ERR_WORKSPACE),
+    ({}, dict(scale=float("nan")), sd.SD_ERR_INVALID_ARG),
+])
+def test_verify_rejects_invalid_arguments(L, over, args, want):
+    kv = _kv(**over)
+    a = dict(q=FAKE, batch=2, n_q=4, hq=8, max_len=64, scale=1.0, out=FAKE, ws=WS, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_verify_attn(ctypes.byref(kv), a["q"], a["batch"], a["n_q"], a["hq"], a["max_len"],
+                          a["scale"], a["out"], None, a["ws"], a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(idx=None), sd.SD_ERR_INVALID_ARG),
+    (dict(idx_heads=3), sd.SD_ERR_INVALID_ARG),
+    (dict(max_sel=0), sd.SD_ERR_INVALID_ARG),
+    (dict(ws_bytes=0), sd.SD_ERR_WORKSPACE),
+])
+def test_draft_rejects_invalid_arguments(L, args, want):
+    kv = _kv()
+    a = dict(idx=FAKE, idx_heads=1, max_sel=64, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_draft_attn_sparse(ctypes.byref(kv), FAKE, 2, 1, 8, a["idx"], FAKE, a["idx_heads"],
+                                a["max_sel"], 1.0, FAKE, None, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(lens=None), sd.SD_ERR_INVALID_ARG),
+    (dict(sink=-1), sd.SD_ERR_INVALID_ARG),
+    (dict(sink=0, recent=0), sd.SD_ERR_INVALID_ARG),
+    (dict(batch=0), sd.SD_ERR_INVALID_ARG),
+])
+def test_streaming_rejects_invalid_arguments(L, args, want):
+    a = dict(lens=FAKE, batch=2, sink=4, recent=8)
+    a.update(args)
+    assert L.sd_streaming_select(a["lens"], a["batch"], a["sink"], a["recent"], FAKE, FAKE, None) == want
+
+
+@no_gpu
+@pytest.mark.parametrize("over,args,want", [
+    ({}, dict(budget=8), sd.SD_ERR_INVALID_ARG),      # budget <= window
+    ({}, dict(pool=4), sd.SD_ERR_INVALID_ARG),        # even pool kernel
+    ({}, dict(pool=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(window=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(window=40, budget=64), sd.SD_ERR_UNSUPPORTED),  # G * window > 128
+    ({"dtype": binding.SD_F32}, {}, sd.SD_ERR_UNSUPPORTED),
+    ({}, dict(ws_bytes=16), sd.SD_ERR_WORKSPACE),
+    ({}, dict(max_len=1000), sd.SD_ERR_INVALID_ARG),
+])
+def test_snapkv_rejects_invalid_arguments(L, over, args, want):
+    kv = _kv(**over)
+    a = dict(window=8, pool=7, budget=32, max_len=64, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_snapkv_select(ctypes.byref(kv), FAKE, 2, a["window"], 8, a["pool"], a["budget"],
+                            a["max_len"], 1.0, FAKE, FAKE, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(zt=None), sd.SD_ERR_INVALID_ARG),
+    (dict(zd=None), sd.SD_ERR_INVALID_ARG),
+    (dict(gamma=-1), sd.SD_ERR_INVALID_ARG),
+    (dict(gamma=65), sd.SD_ERR_UNSUPPORTED),
+    (dict(temp=0.0), sd.SD_ERR_INVALID_ARG),
+    (dict(temp=float("inf")), sd.SD_ERR_INVALID_ARG),
+    (dict(vocab=0), sd.SD_ERR_INVALID_ARG),
+    (dict(ws_bytes=8), sd.SD_ERR_WORKSPACE),
+])
+def test_accept_rejects_invalid_arguments(L, args, want):
+    a = dict(zt=FAKE, zd=FAKE, gamma=3, vocab=1000, temp=1.0, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_spec_accept(a["zt"], a["zd"], FAKE, FAKE, FAKE, 4, a["gamma"], a["vocab"], a["temp"],
+                          FAKE, FAKE, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+def test_binding_refuses_host_tensors(L):
+    k = torch.zeros((2, 1, 16, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sd.KVCache(k, k, torch.zeros((1, 2), dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "long_context_kv_split_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -1,0 +1,159 @@
+"""GPU parity of verify and sparse draft attention against the CPU oracle.
+
+Small seeded cases that span several 16-token steps, several split-KV chunks,
+ragged and shuffled pages, partial last pages (NaN-poisoned tails), every
+query-row tile count (NB = 1..4), head_dim 64/128, bf16 and fp32, page size 32,
+and the degenerate lengths (kv_len == n_q, kv_len < n_q, empty sequences,
+empty selections).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import paged_kv, queries
+from tests.gpu_helpers import compare_attn, ensure_lib, run_draft, run_verify, say
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+    torch.cuda.set_device(0)
+
+
+VERIFY_CASES = [
+    # name, dtype, Hq, Hkv, d, lens, n_q, shuffle, page_size
+    ("tiny-f32-b2-l256", F32, 8, 2, 64, [256, 256], 4, False, 16),
+    ("bf16-ragged-multichunk", BF16, 8, 2, 128, [37, 300, 1029], 4, True, 16),
+    ("bf16-rows20", BF16, 32, 8, 128, [700, 1500], 5, True, 16),
+    ("bf16-rows40", BF16, 16, 2, 128, [900, 333], 5, True, 16),
+    ("bf16-rows64", BF16, 16, 1, 128, [600], 4, False, 16),
+    ("bf16-d64", BF16, 8, 2, 64, [513, 77], 3, True, 16),
+    ("f32-d128", F32, 8, 2, 128, [200, 1111], 2, True, 16),
+    ("f32-d64-rows40", F32, 16, 2, 64, [450, 97], 5, True, 16),
+    ("bf16-page32", BF16, 8, 2, 128, [100, 1000], 4, True, 32),
+    ("bf16-short", BF16, 8, 2, 128, [4, 3, 0, 1], 4, False, 16),
+    ("bf16-decode-exact-pages", BF16, 8, 2, 128, [512, 1024], 1, True, 16),
+]
+
+
+@pytest.mark.parametrize("case", VERIFY_CASES, ids=[c[0] for c in VERIFY_CASES])
+def test_verify_parity(case):
+    name, dtype, Hq, Hkv, d, lens, n_q, shuffle, P = case
+    say(f"verify {name}: lens={lens} n_q={n_q} Hq={Hq} Hkv={Hkv} d={d} {dtype}")
+    seed = zlib.crc32(name.encode()) % 10000
+    kv_t = paged_kv(seed, lens, Hkv, d, dtype, "cuda", shuffle=shuffle, page_size=P)
+    q = queries(seed, 1, (len(lens), n_q, Hq, d), dtype, "cuda", scale=d ** -0.5)
+    out, lse = run_verify(kv_t, q, n_q, Hq, scale=1.0)
+    o_ref, l_ref = oracle.verify_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens, 1.0)
+    err = compare_attn(out, lse, o_ref, l_ref, dtype)
+    say(f"  max|dO|={err[0]:.3e} norm={err[1]:.3e} lse={err[2]:.3e}")
+
+
+def test_verify_softmax_scale_argument():
+    lens = [333, 800]
+    kv_t = paged_kv(5, lens, 2, 128, BF16, "cuda", shuffle=True)
+    q = queries(5, 1, (2, 4, 8, 128), BF16, "cuda", scale=1.0)
+    out, lse = run_verify(kv_t, q, 4, 8, scale=128 ** -0.5)
+    o_ref, l_ref = oracle.verify_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens,
+                                      128 ** -0.5)
+    compare_attn(out, lse, o_ref, l_ref, BF16)
+
+
+def test_verify_is_deterministic():
+    lens = [2000, 1700, 900]
+    kv_t = paged_kv(6, lens, 2, 128, BF16, "cuda", shuffle=True)
+    q = queries(6, 1, (3, 4, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    a = run_verify(kv_t, q, 4, 8)
+    b = run_verify(kv_t, q, 4, 8)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_verify_page_permutation_invariance():
+    """The same tokens under two physical page orders give identical bits."""
+    lens = [700, 1200]
+    kv1 = paged_kv(7, lens, 2, 128, BF16, "cuda", shuffle=False)
+    perm = torch.randperm(kv1.k_pages.shape[0], generator=torch.Generator().manual_seed(3))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel())
+    kv2 = paged_kv(7, lens, 2, 128, BF16, "cuda", shuffle=False)
+    kv2.k_pages = kv1.k_pages[perm.cuda()].contiguous()
+    kv2.v_pages = kv1.v_pages[perm.cuda()].contiguous()
+    kv2.page_table = inv.cuda()[kv1.page_table.long()].to(torch.int32).contiguous()
+    q = queries(7, 1, (2, 4, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    a = run_verify(kv1, q, 4, 8)
+    b = run_verify(kv2, q, 4, 8)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _random_sets(seed, lens, heads, max_sel, min_frac=0.05):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    idx = np.full((B, heads, max_sel), -1, dtype=np.int32)
+    sel = np.zeros(B, dtype=np.int32)
+    for b, L in enumerate(lens):
+        n = int(min(L, rng.integers(max(1, int(min_frac * max_sel)), max_sel + 1)))
+        sel[b] = n
+        for g in range(heads):
+            pos = np.sort(rng.choice(L, size=n, replace=False)) if n else np.zeros(0, np.int64)
+            if g % 2 == 1:
+                pos = pos[::-1]          # order is irrelevant to the result
+            idx[b, g, :n] = pos
+    return torch.tensor(idx).cuda(), torch.tensor(sel).cuda()
+
+
+DRAFT_CASES = [
+    # name, dtype, Hq, Hkv, d, lens, n_q, idx_heads ("shared" or "per-head"), max_sel
+    ("stream-shared-bf16", BF16, 8, 2, 128, [300, 50, 2000], 1, "streaming", 64),
+    ("stream-tiny-f32", F32, 8, 2, 64, [256, 256], 1, "streaming", 64),
+    ("per-head-bf16", BF16, 8, 2, 128, [1500, 800, 40], 1, "per-head", 256),
+    ("per-head-bf16-nq2", BF16, 32, 8, 128, [3000, 700], 2, "per-head", 600),
+    ("shared-bf16-d64", BF16, 8, 2, 64, [999, 1234], 1, "shared", 333),
+    ("per-head-f32-d128", F32, 16, 2, 128, [777, 1500], 1, "per-head", 200),
+    ("per-head-rows64", BF16, 16, 1, 128, [1800], 4, "per-head", 700),
+]
+
+
+@pytest.mark.parametrize("case", DRAFT_CASES, ids=[c[0] for c in DRAFT_CASES])
+def test_draft_parity(case):
+    name, dtype, Hq, Hkv, d, lens, n_q, kind, max_sel = case
+    say(f"draft {name}: lens={lens} n_q={n_q} {kind} max_sel={max_sel} {dtype}")
+    seed = zlib.crc32(name.encode()) % 10000
+    kv_t = paged_kv(seed, lens, Hkv, d, dtype, "cuda", shuffle=True)
+    q = queries(seed, 1, (len(lens), n_q, Hq, d), dtype, "cuda", scale=d ** -0.5)
+    if kind == "streaming":
+        idx_np = np.full((len(lens), 1, max_sel), -1, dtype=np.int32)
+        sel_np = np.zeros(len(lens), dtype=np.int32)
+        for b, L in enumerate(lens):
+            keep = sorted(set(range(min(16, L))) | set(range(max(0, L - (max_sel - 16)), L)))
+            idx_np[b, 0, :len(keep)] = keep
+            sel_np[b] = len(keep)
+        idx, sel = torch.tensor(idx_np).cuda(), torch.tensor(sel_np).cuda()
+    else:
+        idx, sel = _random_sets(seed, lens, Hkv if kind == "per-head" else 1, max_sel)
+    out, lse = run_draft(kv_t, q, n_q, Hq, idx, sel)
+    o_ref, l_ref = oracle.sparse_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, idx, sel, 1.0)
+    err = compare_attn(out, lse, o_ref, l_ref, dtype)
+    say(f"  max|dO|={err[0]:.3e} norm={err[1]:.3e} lse={err[2]:.3e}")
+
+
+def test_draft_empty_selection_and_full_budget_equals_verify_decode():
+    lens = [500, 640]
+    kv_t = paged_kv(9, lens, 2, 128, BF16, "cuda", shuffle=True)
+    q = queries(9, 1, (2, 1, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    idx = torch.full((2, 1, 700), -1, dtype=torch.int32, device="cuda")
+    idx[0, 0, :500] = torch.arange(500, dtype=torch.int32)
+    idx[1, 0, :640] = torch.arange(640, dtype=torch.int32)
+    sel = torch.tensor([500, 0], dtype=torch.int32, device="cuda")
+    out, lse = run_draft(kv_t, q, 1, 8, idx, sel)
+    assert (out[1] == 0).all() and torch.isneginf(lse[1]).all()
+    ref, lref = run_verify(kv_t, q, 1, 8)
+    o_ref, l_ref = oracle.verify_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens, 1.0)
+    compare_attn(out[:1], lse[:1], o_ref[:1], l_ref[:1], BF16)
+    compare_attn(ref, lref, o_ref, l_ref, BF16)
