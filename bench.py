@@ -1,0 +1,305 @@
+"""Benchmark of the sparse-KV self-speculative decoding hot path on one MI355X.
+
+Workload (Llama-3.1-8B attention shapes, synthetic bf16 inputs resident in
+HBM): batch 128, context 32768, 32 query / 8 KV heads, head_dim 128,
+gamma = 4; SnapKV draft set with a 32-query observation window, max-pool 7,
+budget 2048 per KV head, keys with 10% of positions boosted 4x; acceptance over
+Llama-3.1's 128256-token vocabulary with draft logits = target + N(0, 0.5).
+
+One step = one pass of every kernel of the hot path, in call order:
+  sd_snapkv_select, sd_streaming_select (64 + 448), gamma x sd_draft_attn_sparse
+  (n_q = 1 over the SnapKV set), sd_verify_attn (n_q = gamma + 1), sd_spec_accept.
+`value` = draft+verify KV token reads per step / step time (selection counted
+as overhead). Per-call HIP event times, verify GB/s against the 8 TB/s HBM
+peak, and the CPU oracle's rate on a bounded sample are reported beside it.
+
+python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KV_BYTES_PER_TOKEN = 8 * 128 * 2 * 2       # Hkv * d * (K+V) * bf16
+METRIC = "verify-attn KV GB/s and % HBM roofline; draft+verify KV tokens/s at B=128 ctx=32k"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-units", type=int, default=0,
+                    help="(sequence, kv head) units the oracle runs (0 = auto, ~15 s)")
+    ap.add_argument("--copy-probe", action="store_true")
+    return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_bytes_each_way": n, "reps": 5, "ms": dt * 1e3,
+                      "read_plus_write_GBps": 2 * n / dt / 1e9}))
+
+
+class Workload:
+    """Inputs, outputs and workspaces of one step, allocated once."""
+
+    def __init__(self, dev):
+        import torch
+
+        import long_context_kv_split_amd as sd
+        from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries, workload_lens
+
+        w = WORKLOADS["llama8b-b128-l32k-snapkv"]
+        self.w = w
+        B, Hq, Hkv, d, g = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.gamma
+        self.B, self.Hq, self.Hkv, self.d, self.gamma = B, Hq, Hkv, d, g
+        self.n_q = g + 1
+        self.V = 128256
+        lens = workload_lens(w)
+        self.lens = lens
+        self.L = max(lens)
+        t0 = time.perf_counter()
+        self.kv_t = paged_kv(w.seed, lens, Hkv, d, torch.bfloat16, dev, spike_frac=w.spike_frac)
+        self.kv = sd.KVCache(self.kv_t.k_pages, self.kv_t.v_pages, self.kv_t.page_table, self.kv_t.kv_lens)
+        s = d ** -0.5
+        self.q = queries(w.seed, 1, (B, self.n_q, Hq, d), torch.bfloat16, dev, scale=s)
+        self.q_obs = queries(w.seed, 4, (B, w.window, Hq, d), torch.bfloat16, dev, scale=s)
+        self.q_draft = [queries(w.seed, 100 + i, (B, 1, Hq, d), torch.bfloat16, dev, scale=s)
+                        for i in range(g)]
+        self.zt = logits(w.seed, 8, (B, g + 1, self.V), 2.0, dev)
+        self.zd = logits(w.seed, 9, (B, g, self.V), 0.5, dev, base=self.zt[:, :g]).contiguous()
+        self.x = gumbel_tokens(w.seed, self.zd)
+        self.ua = dyadic_uniforms(w.seed, 11, (B, g), dev)
+        self.us = dyadic_uniforms(w.seed, 12, (B, g + 1), dev)
+        torch.cuda.synchronize()
+        log(f"generated inputs in {time.perf_counter() - t0:.1f}s")
+
+        i32 = torch.int32
+        self.idx = torch.empty((B, Hkv, w.budget), dtype=i32, device=dev)
+        self.sel = torch.empty((B,), dtype=i32, device=dev)
+        self.s_idx = torch.empty((B, 1, 512), dtype=i32, device=dev)
+        self.s_sel = torch.empty((B,), dtype=i32, device=dev)
+        self.o_draft = [torch.empty_like(qd) for qd in self.q_draft]
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, self.n_q, Hq), dtype=torch.float32, device=dev)
+        self.n_acc = torch.empty((B,), dtype=i32, device=dev)
+        self.toks = torch.empty((B, g + 1), dtype=i32, device=dev)
+        self.ws_snap = sd.workspace(sd.sd_snapkv_select_workspace_size(B, w.window, Hq, Hkv, self.L), dev)
+        self.ws_draft = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, w.budget), dev)
+        self.ws_ver = sd.workspace(sd.sd_verify_attn_workspace_size(B, self.n_q, Hq, Hkv, d, self.L), dev)
+        self.ws_acc = sd.workspace(sd.sd_spec_accept_workspace_size(B, g, self.V), dev)
+        self.sd = sd
+
+    def step(self, ev=None):
+        """One pass of the hot path; with `ev`, records events between calls."""
+        sd, w = self.sd, self.w
+
+        def mark(k):
+            if ev is not None:
+                ev[k].record()
+
+        mark(0)
+        sd.sd_snapkv_select(self.kv, self.q_obs, w.window, self.Hq, w.pool_kernel, w.budget, self.L, 1.0,
+                            self.idx, self.sel, self.ws_snap)
+        sd.sd_streaming_select(self.kv_t.kv_lens, 64, 448, self.s_idx, self.s_sel)
+        mark(1)
+        for i in range(self.gamma):
+            sd.sd_draft_attn_sparse(self.kv, self.q_draft[i], 1, self.Hq, self.idx, self.sel, self.Hkv,
+                                    w.budget, 1.0, self.o_draft[i], None, self.ws_draft)
+        mark(2)
+        sd.sd_verify_attn(self.kv, self.q, self.n_q, self.Hq, self.L, 1.0, self.o, self.lse, self.ws_ver)
+        mark(3)
+        sd.sd_spec_accept(self.zt, self.zd, self.x, self.ua, self.us, self.gamma, self.V, 1.0, self.n_acc,
+                          self.toks, self.ws_acc)
+        mark(4)
+
+    # algorithmic work
+    def verify_bytes(self):
+        kv = sum(self.lens) * KV_BYTES_PER_TOKEN
+        qo = 2 * self.B * self.n_q * self.Hq * self.d * 2
+        return kv + qo
+
+    def draft_tokens(self):
+        return self.gamma * self.B * self.w.budget
+
+    def verify_tokens(self):
+        return sum(self.lens)
+
+
+def unit_cache(kv_t, b, g):
+    """One (sequence b, KV head g) of the paged cache copied to the host, with
+    its pages in table order and an identity page table."""
+    import numpy as np
+
+    L = int(kv_t.lens[b])
+    npg = max(1, -(-L // kv_t.page_size))
+    pages = kv_t.page_table[b, :npg].long()
+    k = kv_t.k_pages[pages][:, g:g + 1].cpu()
+    v = kv_t.v_pages[pages][:, g:g + 1].cpu()
+    return k, v, np.arange(npg, dtype=np.int64)[None, :], np.array([L])
+
+
+def cpu_baseline(wl, n_units):
+    """Time the oracle (verify + gamma sparse drafts) on a bounded sample of
+    (sequence, KV head) units of the same workload; returns KV tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    G = wl.Hq // wl.Hkv
+    units = [((7 * i) % wl.B, (3 * i) % wl.Hkv) for i in range(n_units)]
+    # host copies are made before the clock starts
+    prepared = []
+    idx = wl.idx.cpu().numpy()
+    sel = wl.sel.cpu().numpy()
+    for b, g in units:
+        k, v, table, lens = unit_cache(wl.kv_t, b, g)
+        heads = slice(g * G, (g + 1) * G)
+        q = wl.q[b:b + 1, :, heads].cpu()
+        qd = [x[b:b + 1, :, heads].cpu() for x in wl.q_draft]
+        prepared.append((k, v, table, lens, q, qd, idx[b:b + 1, g:g + 1], sel[b:b + 1]))
+    t0 = time.perf_counter()
+    toks = 0
+    for k, v, table, lens, q, qd, ix, sl in prepared:
+        oracle.verify_attn(q, k, v, table, lens, 1.0)
+        toks += int(lens[0])
+        for x in qd:
+            oracle.sparse_attn(x, k, v, table, ix, sl, 1.0)
+            toks += int(sl[0])
+    dt = time.perf_counter() - t0
+    # tokens here are per (sequence, KV head) unit; a KV token of the metric
+    # spans all KV heads, so divide by Hkv to use the same unit.
+    return {"value": toks / wl.Hkv / dt, "unit": "KV tokens/s", "cores": int(min(cores, max(blas_threads, 1))),
+            "host_cores_available": cores, "blas_threads": blas_threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{n_units} (sequence, KV head) units of the same workload: fp64 verify over "
+                      f"{wl.L} tokens + {wl.gamma} sparse drafts over {wl.w.budget} SnapKV tokens each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not implemented", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    from __graft_entry__ import _ensure_built
+
+    _ensure_built()
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    wl = Workload(dev)
+
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    # timed region: K steps, with per-call events on the stream the library uses
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(K):
+        wl.step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    parts = {"select_ms": [], "draft_ms": [], "verify_ms": [], "accept_ms": []}
+    for e in evs:
+        parts["select_ms"].append(e[0].elapsed_time(e[1]))
+        parts["draft_ms"].append(e[1].elapsed_time(e[2]) / wl.gamma)
+        parts["verify_ms"].append(e[2].elapsed_time(e[3]))
+        parts["accept_ms"].append(e[3].elapsed_time(e[4]))
+    avg = {k: sum(v) / len(v) for k, v in parts.items()}
+    log(f"timed {K} steps: {ms_step:.3f} ms/step (host wall {wall * 1e3 / K:.3f} ms/step); " +
+        ", ".join(f"{k}={v:.3f}" for k, v in avg.items()))
+
+    v_bytes = wl.verify_bytes()
+    v_gbps = v_bytes / (avg["verify_ms"] * 1e-3) / 1e9
+    step_tokens = wl.verify_tokens() + wl.draft_tokens()
+    value = step_tokens / (ms_step * 1e-3)
+    round_ms = avg["verify_ms"] + wl.gamma * avg["draft_ms"]
+    draft_gbps = wl.B * wl.w.budget * KV_BYTES_PER_TOKEN / (avg["draft_ms"] * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_units = args.cpu_sample_units or 48
+        log(f"cpu baseline: oracle on {n_units} units ...")
+        cpu = cpu_baseline(wl, n_units)
+        log(f"cpu baseline {cpu['value']:.3e} KV tokens/s in {cpu['seconds']} s")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.w.name, "batch": wl.B, "context": wl.L, "gamma": wl.gamma,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d, "page_size": 16,
+                   "draft": f"snapkv window={wl.w.window} pool={wl.w.pool_kernel} budget={wl.w.budget}",
+                   "accept_vocab": wl.V, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "sd_verify_attn (split + combine)",
+                     "achieved": v_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": v_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": v_bytes,
+                     "avg_launch_ms": avg["verify_ms"]},
+        "verify_kv_GBps": v_gbps,
+        "verify_pct_hbm_peak": 100.0 * v_gbps / HBM_PEAK_GBPS,
+        "round_kv_tokens_per_s": step_tokens / (round_ms * 1e-3),
+        "draft_kv_GBps": draft_gbps,
+        "per_call_ms": avg,
+        "mean_accepted": float(wl.n_acc.float().mean().item()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
