@@ -7,18 +7,25 @@
 // a "step" is 16 cached tokens, taken from consecutive positions of one page
 // (verify) or from 16 entries of a selection list (draft).
 //
-// Work split (split-KV): one wavefront per (sequence, KV head, chunk of
-// steps). The G*n_q query rows that share the KV head are padded to NB tiles
-// of 16 rows. Per step the wave computes S^T = K Q^T with 16x16x32 bf16 MFMA
-// (tokens on M, query rows on N), applies the mask and an online softmax in
-// the log2 domain, and accumulates O^T += V^T P^T with 16x16x16 bf16 MFMA.
-// The accumulator layout of the first product is exactly the B-operand layout
-// of the second, so P never leaves registers. V^T is formed from plain 16-byte
-// row loads: lane (g, r) loads d-range [DPL*r, DPL*r+DPL) of tokens 4g..4g+3 and
-// builds the A operand of d-tile dt from element dt of those four rows
-// (v_perm), which assigns head-dim index DPL*m + dt to MFMA row m.
-// A combine kernel merges the per-chunk (m, l, o) partials by log-sum-exp.
-// float32 caches use the same structure with 16x16x4 f32 MFMA.
+// Schedule (persistent split-KV): the launch has exactly as many waves as the
+// chip keeps resident for the instantiation. A plan kernel turns the device
+// lengths into prefix sums; wave w then takes the w-th equal share of the
+// flattened (sequence, KV head, step) space, so the work is balanced to one
+// step whatever the length mix, and writes one (m, l, o) partial per unit
+// segment it covers into a slot table of at most waves + units entries. The
+// assignment depends only on shapes and lengths, so results are bitwise
+// reproducible. A combine kernel merges each unit's partials by log-sum-exp.
+//
+// Per step a wave computes S^T = K Q^T with 16x16x32 bf16 MFMA (tokens on M,
+// the G*n_q query rows of the KV head on N, padded to NB tiles of 16), applies
+// the mask and an online softmax in the log2 domain, and accumulates
+// O^T += V^T P^T with 16x16x16 bf16 MFMA. The accumulator layout of the first
+// product is exactly the B-operand layout of the second, so P never leaves
+// registers. V^T is formed from plain 16-byte row loads: lane (g, r) loads
+// d-range [DPL*r, DPL*r+DPL) of tokens 4g..4g+3 and builds the A operand of
+// d-tile dt from element dt of those four rows (v_perm), which assigns
+// head-dim index DPL*m + dt to MFMA row m. float32 caches use the same
+// structure with 16x16x4 f32 MFMA.
 #include "sd_device.h"
 #include "sd_host.h"
 
@@ -29,7 +36,12 @@ using namespace sdk;
 namespace {
 
 constexpr int kStepTokens = 16;
-constexpr int kTargetWaves = 16384;
+constexpr int kMaxChunkSteps = 128;  // sub-chunk: LDS row-id table of 128 steps x 16 tokens x 4 B = 8 KB
+constexpr int kNumCUs = 256;         // MI355X
+constexpr int kSimdsPerCU = 4;
+constexpr int kMaxWaves = kNumCUs * kSimdsPerCU * 8;  // bound used to size the slot table
+constexpr int kPlanThreads = 1024;
+constexpr int kMinStepsPerWave = 8;  // a partial covers at least 128 tokens (when there is work)
 
 struct AttnParams {
   const void *k_pages;
@@ -38,13 +50,15 @@ struct AttnParams {
   const int32_t *lens;  // kv_lens (verify) or sel_lens (draft)
   const int32_t *idx;   // draft: [B, idx_heads, max_sel]
   const void *q;        // [B, n_q, Hq, D]
-  float *part_o;        // [B*Hkv*max_chunks, rows, D]
-  float *part_ml;       // [B*Hkv*max_chunks, rows, 2]
-  int32_t n_q, Hq, Hkv, G, rows;
+  int32_t *seq_prefix;  // [B + 1]: prefix sums of steps per sequence (plan kernel)
+  int32_t *slot_base;   // [B*Hkv + 1]: first partial slot of each unit (plan kernel)
+  float *part_o;        // [slots, rows, D]
+  float *part_ml;       // [slots, rows, 2]
+  int32_t B, n_q, Hq, Hkv, G, rows;
   int32_t num_pages, page_size, max_pages;
   int32_t idx_heads, max_sel;
   int32_t len_cap;  // upper clamp of lens
-  int32_t chunk_steps, max_chunks;
+  int32_t waves;    // waves launched by the split kernel
   float scale_log2;
 };
 
@@ -87,33 +101,33 @@ __device__ __forceinline__ void load_dwords(uint32_t (&dst)[N], const char *p) {
   }
 }
 
-// Row index (page*Hkv + kvh)*P + slot of the cached token this lane's K load
-// and the four V loads use, for step s.
+// Row id (page*Hkv + kvh)*P + slot of cached token `t` of the chunk's token
+// list: position t (verify) or idx_row[t] (draft), through the page table.
 template <bool SPARSE>
-__device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, int s, int len,
-                                         const int32_t *idx_row, int t_in_step) {
+__device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, int t, int len,
+                                         const int32_t *idx_row) {
   int pos;
   if constexpr (SPARSE) {
-    int t = clampi(s * kStepTokens + t_in_step, 0, len - 1);
-    pos = clampi(idx_row[t], 0, a.max_pages * a.page_size - 1);
+    pos = clampi(idx_row[clampi(t, 0, len - 1)], 0, a.max_pages * a.page_size - 1);
   } else {
-    pos = s * kStepTokens + t_in_step;
+    pos = t;
   }
   int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
   page = clampi(page, 0, a.num_pages - 1);
   return (page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
 }
 
-template <typename T, int D, bool SPARSE>
-__device__ __forceinline__ void load_step(const AttnParams &a, int b, int kvh, int s, int len,
-                                          const int32_t *idx_row, StepRegs<T, D> &R) {
+// Issue the K and V loads of one 16-token step whose row ids sit in LDS at
+// rows[0..15]: K of token r for this lane's MFMA A operand, V of tokens
+// 4g..4g+3 (the four ids are one 16-byte LDS read).
+template <typename T, int D>
+__device__ __forceinline__ void load_step(const AttnParams &a, const int *rows, StepRegs<T, D> &R) {
   constexpr int EB = EltInfo<T>::bytes;
   constexpr int DPL = D / 16;
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  // K: token r of the step; V: tokens 4g..4g+3 (their row ids come from the
-  // lanes that computed them).
-  int rowK = token_row<SPARSE>(a, b, kvh, s, len, idx_row, r);
+  const int rowK = rows[r];
+  const int4 rowV = *reinterpret_cast<const int4 *>(rows + 4 * g);
   const char *kb = reinterpret_cast<const char *>(a.k_pages) + (size_t)rowK * D * EB;
   if constexpr (EB == 2) {
 #pragma unroll
@@ -124,196 +138,357 @@ __device__ __forceinline__ void load_step(const AttnParams &a, int b, int kvh, i
     for (int c = 0; c < D / 16; ++c)
       R.k[c] = *reinterpret_cast<const u32x4 *>(kb + ((D / 4) * g + 4 * c) * EB);
   }
+  const int rv[4] = {rowV.x, rowV.y, rowV.z, rowV.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int rowV = __shfl(rowK, 4 * g + j, 64);
-    const char *vb = reinterpret_cast<const char *>(a.v_pages) + ((size_t)rowV * D + DPL * r) * EB;
+    const char *vb = reinterpret_cast<const char *>(a.v_pages) + ((size_t)rv[j] * D + DPL * r) * EB;
     load_dwords(R.v[j], vb);
   }
 }
 
-template <typename T, int D, int NB, bool SPARSE>
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnParams a) {
-  constexpr int EB = EltInfo<T>::bytes;
-  constexpr int DPL = D / 16;  // head-dim values per lane per token row of V
-  const int lane = lane_id();
-  const int g = lane >> 4, r = lane & 15;
+// max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows)
+__device__ __forceinline__ float rows4_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
-  int unit = blockIdx.x;
-  const int chunk = unit % a.max_chunks;
-  unit /= a.max_chunks;
-  const int kvh = unit % a.Hkv;
-  const int b = unit / a.Hkv;
-  const int len = clampi(a.lens[b], 0, a.len_cap);
-  const int n_steps = (len + kStepTokens - 1) / kStepTokens;
-  const int s_begin = chunk * a.chunk_steps;
-  if (s_begin >= n_steps) return;
-  const int s_end = min(n_steps, s_begin + a.chunk_steps);
-  const int32_t *idx_row = nullptr;
-  if constexpr (SPARSE)
-    idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
-
-  // Query operands and each row's last visible position.
-  constexpr int QV = StepRegs<T, D>::kVec;
-  u32x4 qreg[NB][QV];
+// Per-wave state of the online softmax and the output accumulators.
+template <typename T, int D, int NB>
+struct AttnState {
+  static constexpr int DPL = D / 16;
+  static constexpr int QV = StepRegs<T, D>::kVec;
+  u32x4 q[NB][QV];
   int lim[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int R = rb * 16 + r;
-    int i = 0, hl = 0;
-    bool live = R < a.rows;
-    if (live) {
-      i = R / a.G;
-      hl = R % a.G;
-    }
-    lim[rb] = SPARSE ? len - 1 : (live ? len - a.n_q + i : len - 1);
-    const char *qb = reinterpret_cast<const char *>(a.q) +
-                     ((((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl) * D) * EB;
-#pragma unroll
-    for (int c = 0; c < QV; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (live) {
-        if constexpr (EB == 2)
-          v = *reinterpret_cast<const u32x4 *>(qb + (32 * c + 8 * g) * EB);
-        else
-          v = *reinterpret_cast<const u32x4 *>(qb + ((D / 4) * g + 4 * c) * EB);
-      }
-      qreg[rb][c] = v;
-    }
-  }
-  const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
+  f32x4 o[NB][DPL];
+  float m[NB], l[NB];
+};
 
-  f32x4 acc_o[NB][DPL];
-  float m_run[NB], l_run[NB];
+// One 16-token step: scores, mask, online softmax, P V.
+// MASK = false is only used for steps whose every token is visible to every
+// query row (no causal limit, no tail of the sequence inside the step).
+template <typename T, int D, int NB, bool SPARSE, bool MASK>
+__device__ __forceinline__ void compute_step(const AttnParams &a, AttnState<T, D, NB> &st,
+                                             StepRegs<T, D> &cur, int s, int len) {
+  constexpr int EB = EltInfo<T>::bytes;
+  constexpr int DPL = D / 16;
+  constexpr int QV = StepRegs<T, D>::kVec;
+  const int g = lane_id() >> 4;
+  const int tok0 = s * kStepTokens;
+
+  if constexpr (MASK) {  // zero V rows of tokens no row may see (they can hold NaN)
 #pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
+    for (int j = 0; j < 4; ++j)
+      if (tok0 + 4 * g + j >= len)
 #pragma unroll
-    for (int dt = 0; dt < DPL; ++dt) acc_o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < StepRegs<T, D>::kVDwords; ++w) cur.v[j][w] = 0u;
   }
 
-  StepRegs<T, D> cur, nxt;
-  load_step<T, D, SPARSE>(a, b, kvh, s_begin, len, idx_row, cur);
-
-  for (int s = s_begin; s < s_end; ++s) {
-    if (s + 1 < s_end) load_step<T, D, SPARSE>(a, b, kvh, s + 1, len, idx_row, nxt);
-    const int tok0 = s * kStepTokens;
-    const bool boundary = tok0 + kStepTokens - 1 > lim_min;
-
-    if (boundary) {  // zero V rows of tokens no row may see (they can hold NaN)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (tok0 + 4 * g + j >= len)
-#pragma unroll
-          for (int w = 0; w < StepRegs<T, D>::kVDwords; ++w) cur.v[j][w] = 0u;
-    }
-
-    // V^T operands, shared by all row tiles.
-    constexpr int NA = (EB == 2) ? DPL : DPL * 4;
-    uint32_t va[NA][EB == 2 ? 2 : 1];
+  for (int rb = 0; rb < NB; ++rb) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (EB == 2) {
+#pragma unroll
+      for (int c = 0; c < QV; ++c) sc = mfma_16x16x32_bf16(cur.k[c], st.q[rb][c], sc);
+    } else {
+      // (__uint_as_float, not __builtin_bit_cast: the latter applied to an
+      // ext-vector element miscompiles to the first element with this clang)
+#pragma unroll
+      for (int c = 0; c < QV; ++c) {
+        sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].x), __uint_as_float(st.q[rb][c].x), sc);
+        sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].y), __uint_as_float(st.q[rb][c].y), sc);
+        sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].z), __uint_as_float(st.q[rb][c].z), sc);
+        sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].w), __uint_as_float(st.q[rb][c].w), sc);
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = sc[e] * a.scale_log2;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (tok0 + 4 * g + e > st.lim[rb]) p[e] = kNegInf;
+    }
+    const float mx = rows4_max(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])));
+    const float m_new = fmaxf(st.m[rb], mx);
+    if (__ballot(m_new > st.m[rb]) != 0) {
+      const float alpha = (m_new == st.m[rb]) ? 1.f : __builtin_amdgcn_exp2f(st.m[rb] - m_new);
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DPL; ++dt) st.o[rb][dt] *= alpha;
+      st.m[rb] = m_new;
+    }
+    const float mu = (st.m[rb] == kNegInf) ? 0.f : st.m[rb];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] - mu);
+    st.l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+
+    if constexpr (EB == 2) {
+      const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
 #pragma unroll
       for (int dt = 0; dt < DPL; ++dt) {
         const bool hi = dt & 1;
-        va[dt][0] = pick_halves(cur.v[0][dt / 2], cur.v[1][dt / 2], hi);
-        va[dt][1] = pick_halves(cur.v[2][dt / 2], cur.v[3][dt / 2], hi);
+        const u32x2 av = {pick_halves(cur.v[0][dt / 2], cur.v[1][dt / 2], hi),
+                          pick_halves(cur.v[2][dt / 2], cur.v[3][dt / 2], hi)};
+        st.o[rb][dt] = mfma_16x16x16_bf16(av, pb, st.o[rb][dt]);
       }
-    }
-
+    } else {
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (EB == 2) {
+      for (int dt = 0; dt < DPL; ++dt)
 #pragma unroll
-        for (int c = 0; c < QV; ++c) sc = mfma_16x16x32_bf16(cur.k[c], qreg[rb][c], sc);
-      } else {
-        // (__uint_as_float, not __builtin_bit_cast: the latter applied to an
-        // ext-vector element miscompiles to the first element with this clang)
-#pragma unroll
-        for (int c = 0; c < QV; ++c) {
-          sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].x),
-                                __uint_as_float(qreg[rb][c].x), sc);
-          sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].y),
-                                __uint_as_float(qreg[rb][c].y), sc);
-          sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].z),
-                                __uint_as_float(qreg[rb][c].z), sc);
-          sc = mfma_16x16x4_f32(__uint_as_float(cur.k[c].w),
-                                __uint_as_float(qreg[rb][c].w), sc);
-        }
-      }
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = sc[e] * a.scale_log2;
-      if (boundary) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tok0 + 4 * g + e > lim[rb]) p[e] = kNegInf;
-      }
-      float mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run[rb], mx);
-      if (__ballot(m_new > m_run[rb]) != 0) {
-        const float alpha = (m_new == m_run[rb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DPL; ++dt) acc_o[rb][dt] *= alpha;
-        m_run[rb] = m_new;
-      }
-      const float mu = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] - mu);
-      l_run[rb] += (p[0] + p[1]) + (p[2] + p[3]);
-
-      if constexpr (EB == 2) {
-        u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-#pragma unroll
-        for (int dt = 0; dt < DPL; ++dt) {
-          u32x2 av = {va[dt][0], va[dt][1]};
-          acc_o[rb][dt] = mfma_16x16x16_bf16(av, pb, acc_o[rb][dt]);
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < DPL; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc_o[rb][dt] = mfma_16x16x4_f32(__uint_as_float(cur.v[j][dt]), p[j],
-                                             acc_o[rb][dt]);
-      }
-    }
-    if (s + 1 < s_end) cur = nxt;
-  }
-
-  // Partials: unnormalised o (relative to m), and (m, l) in the log2 domain.
-  const size_t uc = ((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk;
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int R = rb * 16 + r;
-    float l = l_run[rb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (R < a.rows) {
-      float *dst = a.part_o + (uc * a.rows + R) * D + 4 * DPL * g;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float vals[DPL];
-#pragma unroll
-        for (int dt = 0; dt < DPL; ++dt) vals[dt] = acc_o[rb][dt][e];
-#pragma unroll
-        for (int w = 0; w < DPL; w += 4)
-          *reinterpret_cast<f32x4 *>(dst + DPL * e + w) =
-              f32x4{vals[w], vals[w + 1], vals[w + 2], vals[w + 3]};
-      }
-      if (g == 0) {
-        a.part_ml[(uc * a.rows + R) * 2 + 0] = m_run[rb];
-        a.part_ml[(uc * a.rows + R) * 2 + 1] = l;
-      }
+        for (int j = 0; j < 4; ++j)
+          st.o[rb][dt] = mfma_16x16x4_f32(__uint_as_float(cur.v[j][dt]), p[j], st.o[rb][dt]);
     }
   }
 }
 
-// One wave per output row (b, kvh, R): merge chunk partials by log-sum-exp.
+// Buffers in flight and occupancy per instantiation: bf16 with up to two row
+// tiles keeps three steps of K/V in registers at two waves per SIMD; three row
+// tiles keep two steps at two waves; larger tiles or fp32 run one wave.
+template <typename T, int NB>
+struct AttnTuning {
+  static constexpr bool kBf16 = EltInfo<T>::bytes == 2;
+  static constexpr int kBufs = (kBf16 && NB <= 2) ? 3 : 2;
+  static constexpr int kWavesPerEU = (kBf16 && NB <= 3) ? 2 : 1;
+};
+
+
+__device__ __forceinline__ int unit_steps(const AttnParams &a, int b) {
+  return (clampi(a.lens[b], 0, a.len_cap) + kStepTokens - 1) / kStepTokens;
+}
+
+// Waves that get work: at most the launched waves and never more than total
+// steps / kMinStepsPerWave, so W <= T and every wave in [lo, hi] of a unit
+// owns at least one of its steps (the slot index w - lo is then dense).
+__device__ __forceinline__ int64_t working_waves(const AttnParams &a, int64_t T) {
+  return max<int64_t>(1, min<int64_t>(a.waves, (T + kMinStepsPerWave - 1) / kMinStepsPerWave));
+}
+
+// First and last wave (inclusive) that own steps of a unit whose flattened
+// steps are [A, A + n), n >= 1, when wave w owns {t : floor(t * W / T) == w}.
+__device__ __forceinline__ void unit_waves(int64_t A, int64_t n, int64_t T, int64_t W, int64_t &lo,
+                                           int64_t &hi) {
+  lo = A * W / T;
+  hi = (A + n - 1) * W / T;
+}
+
+// Block-wide exclusive scan (kPlanThreads threads) with a carried offset.
+__device__ __forceinline__ int64_t plan_scan(int64_t v, int64_t *lds, int64_t &carry) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int64_t before = carry;
+  for (int w = 0; w < wave; ++w) before += lds[w];
+  int64_t total = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) total += lds[w];
+  __syncthreads();
+  carry += total;
+  return before + x - v;
+}
+
+// Plan: seq_prefix[b] = sum of steps of sequences < b; slot_base[u] = first
+// partial slot of unit u = b*Hkv + kvh (units are flattened b-major).
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams a) {
+  __shared__ int64_t lds[kPlanThreads / 64];
+  int64_t carry = 0;
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int b = base + threadIdx.x;
+    const int64_t n = b < a.B ? unit_steps(a, b) : 0;
+    const int64_t ex = plan_scan(n, lds, carry);
+    if (b < a.B) a.seq_prefix[b] = (int32_t)ex;
+  }
+  if (threadIdx.x == 0) a.seq_prefix[a.B] = (int32_t)carry;
+  __syncthreads();
+  const int64_t T = (int64_t)a.Hkv * carry;
+  const int64_t W = working_waves(a, T);
+  const int U = a.B * a.Hkv;
+  int64_t slots = 0;
+  for (int base = 0; base < U; base += kPlanThreads) {
+    const int u = base + threadIdx.x;
+    int64_t cnt = 0;
+    if (u < U) {
+      const int b = u / a.Hkv, kvh = u % a.Hkv;
+      const int64_t n = unit_steps(a, b);
+      if (n > 0) {
+        const int64_t A = (int64_t)a.Hkv * a.seq_prefix[b] + (int64_t)kvh * n;
+        int64_t lo, hi;
+        unit_waves(A, n, T, W, lo, hi);
+        cnt = hi - lo + 1;
+      }
+    }
+    const int64_t ex = plan_scan(cnt, lds, slots);
+    if (u < U) a.slot_base[u] = (int32_t)ex;
+  }
+  if (threadIdx.x == 0) a.slot_base[U] = (int32_t)slots;
+}
+
+// Largest b in [0, B) with seq_prefix[b] <= q (64-way search, one load per round).
+__device__ __forceinline__ int find_seq(const AttnParams &a, int64_t q) {
+  int lo = 0, hi = a.B;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int i = lo + lane_id() * step;
+    const bool ok = i < hi && (int64_t)a.seq_prefix[i] <= q;
+    const int cnt = __popcll(__ballot(ok));
+    const int nlo = lo + (cnt - 1) * step;
+    hi = min(hi, nlo + step);
+    lo = nlo;
+  }
+  return lo;
+}
+
+template <typename T, int D, int NB, bool SPARSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(AttnTuning<T, NB>::kWavesPerEU)))
+void attn_split_kernel(AttnParams a) {
+  constexpr int EB = EltInfo<T>::bytes;
+  constexpr int DPL = D / 16;
+  constexpr int QV = StepRegs<T, D>::kVec;
+  constexpr int NBUF = AttnTuning<T, NB>::kBufs;
+  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+
+  const int64_t TT = (int64_t)a.Hkv * a.seq_prefix[a.B];  // total steps
+  if (TT == 0) return;
+  const int64_t W = working_waves(a, TT);
+  const int64_t w = blockIdx.x;
+  if (w >= W) return;
+  const int64_t t_begin = (w * TT + W - 1) / W;        // ceil(w TT / W)
+  const int64_t t_end = ((w + 1) * TT + W - 1) / W;    // ceil((w+1) TT / W)
+  if (t_begin >= t_end) return;
+
+  int b = find_seq(a, t_begin / a.Hkv);
+  int64_t t = t_begin;
+  while (t < t_end) {
+    const int n_b = a.seq_prefix[b + 1] - a.seq_prefix[b];
+    const int64_t base_b = (int64_t)a.Hkv * a.seq_prefix[b];
+    if (n_b == 0 || t >= base_b + (int64_t)a.Hkv * n_b) {  // next sequence with steps
+      ++b;
+      continue;
+    }
+    const int kvh = (int)((t - base_b) / n_b);
+    const int64_t A_u = base_b + (int64_t)kvh * n_b;
+    const int s_begin = (int)(t - A_u);
+    const int64_t seg_end = min(t_end, A_u + n_b);
+    const int s_end = (int)(seg_end - A_u);
+    const int len = clampi(a.lens[b], 0, a.len_cap);
+    const int32_t *idx_row = nullptr;
+    if constexpr (SPARSE)
+      idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
+
+    AttnState<T, D, NB> st;
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int R = rb * 16 + r;
+      int i = 0, hl = 0;
+      const bool live = R < a.rows;
+      if (live) {
+        i = R / a.G;
+        hl = R % a.G;
+      }
+      st.lim[rb] = SPARSE ? len - 1 : (live ? len - a.n_q + i : len - 1);
+      const char *qb = reinterpret_cast<const char *>(a.q) +
+                       ((((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl) * D) * EB;
+#pragma unroll
+      for (int c = 0; c < QV; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (live) {
+          if constexpr (EB == 2)
+            v = *reinterpret_cast<const u32x4 *>(qb + (32 * c + 8 * g) * EB);
+          else
+            v = *reinterpret_cast<const u32x4 *>(qb + ((D / 4) * g + 4 * c) * EB);
+        }
+        st.q[rb][c] = v;
+      }
+      st.m[rb] = kNegInf;
+      st.l[rb] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DPL; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
+
+    // The segment is processed in sub-chunks of at most kMaxChunkSteps steps:
+    // the row ids of every token of a sub-chunk are resolved into LDS first, so
+    // that no K/V load of the main loop waits on a dependent vector load.
+    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
+      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
+      const int n_tok = (sc_end - sc_begin) * kStepTokens;
+      __syncthreads();  // the previous sub-chunk's table reads are done
+      for (int tt = lane; tt < n_tok; tt += 64)
+        rows_lds[tt] = token_row<SPARSE>(a, b, kvh, sc_begin * kStepTokens + tt, len, idx_row);
+      __syncthreads();
+      // Main loop: groups of NBUF steps that need no mask, with a ring of NBUF
+      // step buffers unrolled so every buffer has a fixed role and the loop
+      // body is straight-line code (exact wait counts, NBUF-1 steps in flight).
+      // Loads past the sub-chunk end repeat its last step (in bounds, cached).
+      const int last = sc_end - sc_begin - 1;
+      const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
+      const int n_plain = max(0, min(sc_end, first_masked) - sc_begin);
+      const int n_groups = n_plain / NBUF;
+      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
+      StepRegs<T, D> buf[NBUF];
+      if (n_groups > 0) {
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k) load_step<T, D>(a, rows_of(k), buf[k]);
+        for (int k0 = 0; k0 < n_groups * NBUF; k0 += NBUF) {
+#pragma unroll
+          for (int j = 0; j < NBUF; ++j) {
+            load_step<T, D>(a, rows_of(k0 + j + NBUF - 1), buf[(j + NBUF - 1) % NBUF]);
+            compute_step<T, D, NB, SPARSE, false>(a, st, buf[j], sc_begin + k0 + j, len);
+          }
+        }
+      }
+      // Tail: the remaining steps, one at a time, with the mask.
+      for (int k = n_groups * NBUF; k <= last; ++k) {
+        load_step<T, D>(a, rows_of(k), buf[0]);
+        compute_step<T, D, NB, SPARSE, true>(a, st, buf[0], sc_begin + k, len);
+      }
+    }
+
+    // Partial of this segment: unnormalised o (relative to m), (m, l) in log2 units.
+    int64_t w_lo, w_hi;
+    unit_waves(A_u, n_b, TT, W, w_lo, w_hi);
+    const size_t slot = (size_t)a.slot_base[b * a.Hkv + kvh] + (size_t)(w - w_lo);
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int R = rb * 16 + r;
+      const float l = rows4_sum(st.l[rb]);
+      if (R < a.rows) {
+        float *dst = a.part_o + (slot * a.rows + R) * D + 4 * DPL * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float vals[DPL];
+#pragma unroll
+          for (int dt = 0; dt < DPL; ++dt) vals[dt] = st.o[rb][dt][e];
+#pragma unroll
+          for (int v4 = 0; v4 < DPL; v4 += 4)
+            *reinterpret_cast<f32x4 *>(dst + DPL * e + v4) =
+                f32x4{vals[v4], vals[v4 + 1], vals[v4 + 2], vals[v4 + 3]};
+        }
+        if (g == 0) {
+          a.part_ml[(slot * a.rows + R) * 2 + 0] = st.m[rb];
+          a.part_ml[(slot * a.rows + R) * 2 + 1] = l;
+        }
+      }
+    }
+    t = seg_end;
+  }
+}
+
+// One wave per output row (b, kvh, R): merge the unit's partials by log-sum-exp.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *out, float *lse,
                                                            int total_rows) {
@@ -321,30 +496,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
   if (wave >= total_rows) return;
   const int lane = lane_id();
   const int R = wave % a.rows;
-  const int bk = wave / a.rows;
-  const int kvh = bk % a.Hkv;
-  const int b = bk / a.Hkv;
-  const int len = clampi(a.lens[b], 0, a.len_cap);
-  const int n_steps = (len + kStepTokens - 1) / kStepTokens;
-  const int n_chunks = min(a.max_chunks, (n_steps + a.chunk_steps - 1) / a.chunk_steps);
-  const size_t uc0 = ((size_t)b * a.Hkv + kvh) * a.max_chunks;
+  const int u = wave / a.rows;
+  const int kvh = u % a.Hkv;
+  const int b = u / a.Hkv;
+  const int s0 = a.slot_base[u], s1 = a.slot_base[u + 1];
 
   float M = kNegInf;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, a.part_ml[((uc0 + c) * a.rows + R) * 2]);
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_ml[((size_t)s * a.rows + R) * 2]);
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const size_t base = (uc0 + c) * a.rows + R;
+    for (int s = s0; s < s1; ++s) {
+      const size_t base = (size_t)s * a.rows + R;
       const float mc = a.part_ml[base * 2];
       if (mc == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(mc - M);
-      L += w * a.part_ml[base * 2 + 1];
+      const float wgt = __builtin_amdgcn_exp2f(mc - M);
+      L += wgt * a.part_ml[base * 2 + 1];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += w * a.part_o[base * D + lane * PER + k];
+      for (int k = 0; k < PER; ++k) o[k] += wgt * a.part_o[base * D + lane * PER + k];
     }
   }
   const int i = R / a.G, hl = R % a.G;
@@ -362,63 +534,109 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
   if (lse != nullptr && lane == 0) lse[orow] = empty ? kNegInf : (M + __log2f(L)) * kLn2;
 }
 
-struct SplitPlan {
-  int chunk_steps;
-  int max_chunks;
-  size_t o_bytes, ml_bytes, ws_bytes;
+// Workspace: prefix tables, then the partial slots. Sized for the largest
+// launch (kMaxWaves) so that the size depends on shapes only.
+struct WsLayout {
+  size_t prefix_off, base_off, ml_off, o_off, bytes;
 };
 
-SplitPlan plan_split(int64_t B, int64_t Hkv, int64_t rows, int64_t D, int64_t max_len) {
-  SplitPlan p;
-  const int64_t steps = std::max<int64_t>(1, sdh::ceil_div(max_len, kStepTokens));
-  const int64_t units = B * Hkv;
-  int64_t cs = sdh::ceil_div(steps * units, kTargetWaves);
-  cs = std::max<int64_t>(cs, std::max<int64_t>(8, 2 * rows));
-  cs = std::min<int64_t>(cs, steps);
-  p.chunk_steps = (int)cs;
-  p.max_chunks = (int)sdh::ceil_div(steps, cs);
-  const int64_t slots = units * p.max_chunks * rows;
-  p.o_bytes = sdh::align_up((size_t)slots * D * 4);
-  p.ml_bytes = sdh::align_up((size_t)slots * 2 * 4);
-  p.ws_bytes = p.o_bytes + p.ml_bytes;
-  return p;
+WsLayout ws_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t D) {
+  WsLayout l;
+  const int64_t slots = kMaxWaves + B * Hkv;
+  l.prefix_off = 0;
+  l.base_off = sdh::align_up((size_t)(B + 1) * 4);
+  l.ml_off = l.base_off + sdh::align_up((size_t)(B * Hkv + 1) * 4);
+  l.o_off = l.ml_off + sdh::align_up((size_t)slots * rows * 2 * 4);
+  l.bytes = l.o_off + sdh::align_up((size_t)slots * rows * D * 4);
+  return l;
 }
 
-template <typename T, int D, bool SPARSE>
-sd_status launch_attn(AttnParams &a, int B, int NB, void *out, float *lse, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)B * a.Hkv * a.max_chunks);
-  switch (NB) {
-    case 1: attn_split_kernel<T, D, 1, SPARSE><<<grid, 64, 0, st>>>(a); break;
-    case 2: attn_split_kernel<T, D, 2, SPARSE><<<grid, 64, 0, st>>>(a); break;
-    case 3: attn_split_kernel<T, D, 3, SPARSE><<<grid, 64, 0, st>>>(a); break;
-    case 4: attn_split_kernel<T, D, 4, SPARSE><<<grid, 64, 0, st>>>(a); break;
-    default: return SD_ERR_UNSUPPORTED;
+// Resident waves of one split-kernel instantiation (64-thread blocks).
+template <typename T, int D, int NB, bool SPARSE>
+int resident_waves() {
+  static int cached = 0;  // written once per process; a race writes the same value
+  int w = __atomic_load_n(&cached, __ATOMIC_RELAXED);
+  if (w > 0) return w;
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<T, D, NB, SPARSE>, 64, 0) !=
+          hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    per_cu = kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU;
+    cus = kNumCUs;
   }
-  const int total_rows = B * a.Hkv * a.rows;
+  w = std::min(per_cu * cus, kMaxWaves);
+  __atomic_store_n(&cached, w, __ATOMIC_RELAXED);
+  return w;
+}
+
+template <typename T, int D, int NB, bool SPARSE>
+sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
+  a.waves = resident_waves<T, D, NB, SPARSE>();
+  attn_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+  attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.waves, 64, 0, st>>>(a);
+  const int total_rows = a.B * a.Hkv * a.rows;
   attn_combine_kernel<T, D><<<(total_rows + 3) / 4, 256, 0, st>>>(a, out, lse, total_rows);
   return sdh::launch_status();
 }
 
-template <bool SPARSE>
-sd_status run_attn(AttnParams &a, int B, int D, int dtype, void *out, float *lse, hipStream_t st) {
-  const int NB = (a.rows + 15) / 16;
-  if (dtype == SD_BF16) {
-    if (D == 128) return launch_attn<__bf16, 128, SPARSE>(a, B, NB, out, lse, st);
-    return launch_attn<__bf16, 64, SPARSE>(a, B, NB, out, lse, st);
+template <typename T, int D, bool SPARSE>
+sd_status launch_attn(AttnParams &a, void *out, float *lse, hipStream_t st) {
+  switch ((a.rows + 15) / 16) {
+    case 1: return launch_nb<T, D, 1, SPARSE>(a, out, lse, st);
+    case 2: return launch_nb<T, D, 2, SPARSE>(a, out, lse, st);
+    case 3: return launch_nb<T, D, 3, SPARSE>(a, out, lse, st);
+    case 4: return launch_nb<T, D, 4, SPARSE>(a, out, lse, st);
+    default: return SD_ERR_UNSUPPORTED;
   }
-  if (D == 128) return launch_attn<float, 128, SPARSE>(a, B, NB, out, lse, st);
-  return launch_attn<float, 64, SPARSE>(a, B, NB, out, lse, st);
+}
+
+template <bool SPARSE>
+sd_status run_attn(AttnParams &a, int D, int dtype, void *out, float *lse, hipStream_t st) {
+  if (dtype == SD_BF16) {
+    if (D == 128) return launch_attn<__bf16, 128, SPARSE>(a, out, lse, st);
+    return launch_attn<__bf16, 64, SPARSE>(a, out, lse, st);
+  }
+  if (D == 128) return launch_attn<float, 128, SPARSE>(a, out, lse, st);
+  return launch_attn<float, 64, SPARSE>(a, out, lse, st);
 }
 
 sd_status common_checks(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
-                        int32_t num_q_heads, void *out) {
+                        int32_t num_q_heads, float softmax_scale, void *out) {
   sd_status s = sdh::check_kv(kv, true);
   if (s != SD_OK) return s;
   SD_REQUIRE(q != nullptr && out != nullptr, SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && n_q > 0 && num_q_heads > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)(num_q_heads / kv->num_kv_heads) * n_q <= 64, SD_ERR_UNSUPPORTED);
+  SD_REQUIRE(softmax_scale > 0.f && softmax_scale < __builtin_inff(), SD_ERR_INVALID_ARG);
+  SD_REQUIRE((int64_t)batch * kv->num_kv_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
   return SD_OK;
+}
+
+void fill_common(AttnParams &a, const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
+                 int32_t num_q_heads, float softmax_scale, void *workspace, const WsLayout &l) {
+  char *ws = reinterpret_cast<char *>(workspace);
+  a.k_pages = kv->k_pages;
+  a.v_pages = kv->v_pages;
+  a.page_table = kv->page_table;
+  a.q = q;
+  a.seq_prefix = reinterpret_cast<int32_t *>(ws + l.prefix_off);
+  a.slot_base = reinterpret_cast<int32_t *>(ws + l.base_off);
+  a.part_ml = reinterpret_cast<float *>(ws + l.ml_off);
+  a.part_o = reinterpret_cast<float *>(ws + l.o_off);
+  a.B = batch;
+  a.n_q = n_q;
+  a.Hq = num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = num_q_heads / kv->num_kv_heads;
+  a.rows = a.G * n_q;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages;
+  a.scale_log2 = softmax_scale * kLog2e;
 }
 
 }  // namespace
@@ -429,48 +647,27 @@ extern "C" size_t sd_verify_attn_workspace_size(int32_t batch, int32_t n_q, int3
   if (batch <= 0 || n_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_kv_len < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int rows = num_q_heads / num_kv_heads * n_q;
-  return plan_split(batch, num_kv_heads, rows, head_dim, max_kv_len).ws_bytes;
+  return ws_layout(batch, num_kv_heads, num_q_heads / num_kv_heads * n_q, head_dim).bytes;
 }
 
 extern "C" sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
                                     int32_t num_q_heads, int32_t max_kv_len, float softmax_scale,
                                     void *out, float *lse, void *workspace, size_t workspace_bytes,
                                     void *stream) {
-  sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, out);
+  sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, softmax_scale, out);
   if (s != SD_OK) return s;
   SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
              SD_ERR_INVALID_ARG);
-  SD_REQUIRE(softmax_scale == softmax_scale, SD_ERR_INVALID_ARG);
-  const int G = num_q_heads / kv->num_kv_heads;
-  const int rows = G * n_q;
-  SplitPlan p = plan_split(batch, kv->num_kv_heads, rows, kv->head_dim, max_kv_len);
-  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
-
+  const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
-  a.k_pages = kv->k_pages;
-  a.v_pages = kv->v_pages;
-  a.page_table = kv->page_table;
+  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l);
   a.lens = kv->kv_lens;
   a.idx = nullptr;
-  a.q = q;
-  a.part_o = reinterpret_cast<float *>(workspace);
-  a.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.o_bytes);
-  a.n_q = n_q;
-  a.Hq = num_q_heads;
-  a.Hkv = kv->num_kv_heads;
-  a.G = G;
-  a.rows = rows;
-  a.num_pages = kv->num_pages;
-  a.page_size = kv->page_size;
-  a.max_pages = kv->max_pages;
   a.idx_heads = 1;
   a.max_sel = 0;
   a.len_cap = max_kv_len;
-  a.chunk_steps = p.chunk_steps;
-  a.max_chunks = p.max_chunks;
-  a.scale_log2 = softmax_scale * kLog2e;
-  return run_attn<false>(a, batch, kv->head_dim, kv->dtype, out, lse, sdh::as_stream(stream));
+  return run_attn<false>(a, kv->head_dim, kv->dtype, out, lse, sdh::as_stream(stream));
 }
 
 extern "C" size_t sd_draft_attn_sparse_workspace_size(int32_t batch, int32_t n_q,
@@ -485,39 +682,19 @@ extern "C" sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, 
                                           int32_t max_sel, float softmax_scale, void *out,
                                           float *lse, void *workspace, size_t workspace_bytes,
                                           void *stream) {
-  sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, out);
+  sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, softmax_scale, out);
   if (s != SD_OK) return s;
   SD_REQUIRE(idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
   SD_REQUIRE(idx_heads == 1 || idx_heads == kv->num_kv_heads, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_sel > 0, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(softmax_scale == softmax_scale, SD_ERR_INVALID_ARG);
-  const int G = num_q_heads / kv->num_kv_heads;
-  const int rows = G * n_q;
-  SplitPlan p = plan_split(batch, kv->num_kv_heads, rows, kv->head_dim, max_sel);
-  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
-
+  const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
-  a.k_pages = kv->k_pages;
-  a.v_pages = kv->v_pages;
-  a.page_table = kv->page_table;
+  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l);
   a.lens = sel_lens;
   a.idx = idx;
-  a.q = q;
-  a.part_o = reinterpret_cast<float *>(workspace);
-  a.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + p.o_bytes);
-  a.n_q = n_q;
-  a.Hq = num_q_heads;
-  a.Hkv = kv->num_kv_heads;
-  a.G = G;
-  a.rows = rows;
-  a.num_pages = kv->num_pages;
-  a.page_size = kv->page_size;
-  a.max_pages = kv->max_pages;
   a.idx_heads = idx_heads;
   a.max_sel = max_sel;
   a.len_cap = max_sel;
-  a.chunk_steps = p.chunk_steps;
-  a.max_chunks = p.max_chunks;
-  a.scale_log2 = softmax_scale * kLog2e;
-  return run_attn<true>(a, batch, kv->head_dim, kv->dtype, out, lse, sdh::as_stream(stream));
+  return run_attn<true>(a, kv->head_dim, kv->dtype, out, lse, sdh::as_stream(stream));
 }

@@ -24,6 +24,14 @@ BF16_ABS, BF16_NORM, BF16_LSE = 2e-2, 1e-2, 1e-4
 F32_NORM, F32_LSE = 1e-5, 1e-5
 
 
+def dirty_workspace(nbytes, device):
+    """Workspace pre-filled with 0xFF bytes (NaN as float): a kernel that reads
+    scratch it did not write in the same call shows it in the outputs."""
+    ws = sd.workspace(nbytes, device)
+    ws.fill_(255)
+    return ws
+
+
 def ensure_lib():
     if not os.path.exists(LIB_PATH):
         from long_context_kv_split_amd.build import build
@@ -41,8 +49,8 @@ def run_verify(kv_t, q, n_q, num_q_heads, scale=1.0, max_kv_len=None):
     mk = max(1, kv_t.max_kv_len) if max_kv_len is None else max_kv_len
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, n_q, num_q_heads), float("nan"), dtype=torch.float32, device=q.device)
-    ws = sd.workspace(sd.sd_verify_attn_workspace_size(B, n_q, num_q_heads, kv.num_kv_heads,
-                                                       kv.head_dim, mk), q.device)
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, n_q, num_q_heads, kv.num_kv_heads,
+                                                          kv.head_dim, mk), q.device)
     sd.sd_verify_attn(kv, q, n_q, num_q_heads, mk, scale, out, lse, ws)
     torch.cuda.synchronize()
     return out, lse
@@ -54,8 +62,8 @@ def run_draft(kv_t, q, n_q, num_q_heads, idx, sel_lens, scale=1.0):
     idx_heads, max_sel = int(idx.shape[1]), int(idx.shape[2])
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, n_q, num_q_heads), float("nan"), dtype=torch.float32, device=q.device)
-    ws = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, n_q, num_q_heads, kv.num_kv_heads,
-                                                             kv.head_dim, max_sel), q.device)
+    ws = dirty_workspace(sd.sd_draft_attn_sparse_workspace_size(B, n_q, num_q_heads, kv.num_kv_heads,
+                                                                kv.head_dim, max_sel), q.device)
     sd.sd_draft_attn_sparse(kv, q, n_q, num_q_heads, idx, sel_lens, idx_heads, max_sel, scale, out,
                             lse, ws)
     torch.cuda.synchronize()

@@ -14,7 +14,7 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import dyadic_uniforms, gumbel_tokens, logits
-from tests.gpu_helpers import ensure_lib, say
+from tests.gpu_helpers import dirty_workspace, ensure_lib, say
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "accept_cases.json")
@@ -31,7 +31,7 @@ def run_accept(zt, zd, x, ua, us, temperature=1.0):
     gamma = g1 - 1
     n = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     out = torch.full((B, g1), -7, dtype=torch.int32, device="cuda")
-    ws = sd.workspace(sd.sd_spec_accept_workspace_size(B, gamma, V), "cuda")
+    ws = dirty_workspace(sd.sd_spec_accept_workspace_size(B, gamma, V), "cuda")
     sd.sd_spec_accept(zt, zd, x, ua, us, gamma, V, temperature, n, out, ws)
     torch.cuda.synchronize()
     return n.cpu().numpy(), out.cpu().numpy()

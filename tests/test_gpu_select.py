@@ -15,7 +15,7 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import paged_kv, queries
-from tests.gpu_helpers import ensure_lib, say
+from tests.gpu_helpers import dirty_workspace, ensure_lib, say
 
 pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
@@ -47,7 +47,7 @@ def run_snapkv(kv_t, q_obs, window, Hq, pool, budget):
     mk = max(1, kv_t.max_kv_len)
     idx = torch.full((B, kv.num_kv_heads, budget), 7, dtype=torch.int32, device="cuda")
     sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
-    ws = sd.workspace(sd.sd_snapkv_select_workspace_size(B, window, Hq, kv.num_kv_heads, mk), "cuda")
+    ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, window, Hq, kv.num_kv_heads, mk), "cuda")
     sd.sd_snapkv_select(kv, q_obs, window, Hq, pool, budget, mk, 1.0, idx, sel, ws)
     torch.cuda.synchronize()
     return idx, sel
