@@ -150,6 +150,23 @@ class Workload:
         return sum(self.lens)
 
 
+def measured_traffic():
+    """HBM bytes per verify launch from the committed counter runs, or None if
+    the verify kernel's source changed since they were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "verify_attn_b128_l32k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def unit_cache(kv_t, b, g):
     """One (sequence b, KV head g) of the paged cache copied to the host, with
     its pages in table order and an identity page table."""
@@ -287,7 +304,7 @@ def main():
                    "accept_vocab": wl.V, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "sd_verify_attn (split + combine)",
                      "achieved": v_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": v_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": v_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": v_bytes,
                      "avg_launch_ms": avg["verify_ms"]},
         "verify_kv_GBps": v_gbps,
