@@ -28,6 +28,7 @@
 // structure with 16x16x4 f32 MFMA.
 #include "sd_device.h"
 #include "sd_host.h"
+#include "sd_sched.h"
 
 #include <algorithm>
 
@@ -37,11 +38,6 @@ namespace {
 
 constexpr int kStepTokens = 16;
 constexpr int kMaxChunkSteps = 128;  // sub-chunk: LDS row-id table of 128 steps x 16 tokens x 4 B = 8 KB
-constexpr int kNumCUs = 256;         // MI355X
-constexpr int kSimdsPerCU = 4;
-constexpr int kMaxWaves = kNumCUs * kSimdsPerCU * 8;  // bound used to size the slot table
-constexpr int kPlanThreads = 1024;
-constexpr int kMinStepsPerWave = 8;  // a partial covers at least 128 tokens (when there is work)
 
 struct AttnParams {
   const void *k_pages;
@@ -50,15 +46,13 @@ struct AttnParams {
   const int32_t *lens;  // kv_lens (verify) or sel_lens (draft)
   const int32_t *idx;   // draft: [B, idx_heads, max_sel]
   const void *q;        // [B, n_q, Hq, D]
-  int32_t *seq_prefix;  // [B + 1]: prefix sums of steps per sequence (plan kernel)
-  int32_t *slot_base;   // [B*Hkv + 1]: first partial slot of each unit (plan kernel)
+  Sched sc;             // persistent schedule tables (written by the plan kernel)
   float *part_o;        // [slots, rows, D]
   float *part_ml;       // [slots, rows, 2]
   int32_t B, n_q, Hq, Hkv, G, rows;
   int32_t num_pages, page_size, max_pages;
   int32_t idx_heads, max_sel;
   int32_t len_cap;  // upper clamp of lens
-  int32_t waves;    // waves launched by the split kernel
   float scale_log2;
 };
 
@@ -264,90 +258,8 @@ __device__ __forceinline__ int unit_steps(const AttnParams &a, int b) {
   return (clampi(a.lens[b], 0, a.len_cap) + kStepTokens - 1) / kStepTokens;
 }
 
-// Waves that get work: at most the launched waves and never more than total
-// steps / kMinStepsPerWave, so W <= T and every wave in [lo, hi] of a unit
-// owns at least one of its steps (the slot index w - lo is then dense).
-__device__ __forceinline__ int64_t working_waves(const AttnParams &a, int64_t T) {
-  return max<int64_t>(1, min<int64_t>(a.waves, (T + kMinStepsPerWave - 1) / kMinStepsPerWave));
-}
-
-// First and last wave (inclusive) that own steps of a unit whose flattened
-// steps are [A, A + n), n >= 1, when wave w owns {t : floor(t * W / T) == w}.
-__device__ __forceinline__ void unit_waves(int64_t A, int64_t n, int64_t T, int64_t W, int64_t &lo,
-                                           int64_t &hi) {
-  lo = A * W / T;
-  hi = (A + n - 1) * W / T;
-}
-
-// Block-wide exclusive scan (kPlanThreads threads) with a carried offset.
-__device__ __forceinline__ int64_t plan_scan(int64_t v, int64_t *lds, int64_t &carry) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) lds[wave] = x;
-  __syncthreads();
-  int64_t before = carry;
-  for (int w = 0; w < wave; ++w) before += lds[w];
-  int64_t total = 0;
-  for (int w = 0; w < kPlanThreads / 64; ++w) total += lds[w];
-  __syncthreads();
-  carry += total;
-  return before + x - v;
-}
-
-// Plan: seq_prefix[b] = sum of steps of sequences < b; slot_base[u] = first
-// partial slot of unit u = b*Hkv + kvh (units are flattened b-major).
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams a) {
-  __shared__ int64_t lds[kPlanThreads / 64];
-  int64_t carry = 0;
-  for (int base = 0; base < a.B; base += kPlanThreads) {
-    const int b = base + threadIdx.x;
-    const int64_t n = b < a.B ? unit_steps(a, b) : 0;
-    const int64_t ex = plan_scan(n, lds, carry);
-    if (b < a.B) a.seq_prefix[b] = (int32_t)ex;
-  }
-  if (threadIdx.x == 0) a.seq_prefix[a.B] = (int32_t)carry;
-  __syncthreads();
-  const int64_t T = (int64_t)a.Hkv * carry;
-  const int64_t W = working_waves(a, T);
-  const int U = a.B * a.Hkv;
-  int64_t slots = 0;
-  for (int base = 0; base < U; base += kPlanThreads) {
-    const int u = base + threadIdx.x;
-    int64_t cnt = 0;
-    if (u < U) {
-      const int b = u / a.Hkv, kvh = u % a.Hkv;
-      const int64_t n = unit_steps(a, b);
-      if (n > 0) {
-        const int64_t A = (int64_t)a.Hkv * a.seq_prefix[b] + (int64_t)kvh * n;
-        int64_t lo, hi;
-        unit_waves(A, n, T, W, lo, hi);
-        cnt = hi - lo + 1;
-      }
-    }
-    const int64_t ex = plan_scan(cnt, lds, slots);
-    if (u < U) a.slot_base[u] = (int32_t)ex;
-  }
-  if (threadIdx.x == 0) a.slot_base[U] = (int32_t)slots;
-}
-
-// Largest b in [0, B) with seq_prefix[b] <= q (64-way search, one load per round).
-__device__ __forceinline__ int find_seq(const AttnParams &a, int64_t q) {
-  int lo = 0, hi = a.B;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) / 64;
-    const int i = lo + lane_id() * step;
-    const bool ok = i < hi && (int64_t)a.seq_prefix[i] <= q;
-    const int cnt = __popcll(__ballot(ok));
-    const int nlo = lo + (cnt - 1) * step;
-    hi = min(hi, nlo + step);
-    lo = nlo;
-  }
-  return lo;
+  sched_plan(a.sc, [&](int b) { return unit_steps(a, b); });
 }
 
 template <typename T, int D, int NB, bool SPARSE>
@@ -361,29 +273,7 @@ void attn_split_kernel(AttnParams a) {
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
 
-  const int64_t TT = (int64_t)a.Hkv * a.seq_prefix[a.B];  // total steps
-  if (TT == 0) return;
-  const int64_t W = working_waves(a, TT);
-  const int64_t w = blockIdx.x;
-  if (w >= W) return;
-  const int64_t t_begin = (w * TT + W - 1) / W;        // ceil(w TT / W)
-  const int64_t t_end = ((w + 1) * TT + W - 1) / W;    // ceil((w+1) TT / W)
-  if (t_begin >= t_end) return;
-
-  int b = find_seq(a, t_begin / a.Hkv);
-  int64_t t = t_begin;
-  while (t < t_end) {
-    const int n_b = a.seq_prefix[b + 1] - a.seq_prefix[b];
-    const int64_t base_b = (int64_t)a.Hkv * a.seq_prefix[b];
-    if (n_b == 0 || t >= base_b + (int64_t)a.Hkv * n_b) {  // next sequence with steps
-      ++b;
-      continue;
-    }
-    const int kvh = (int)((t - base_b) / n_b);
-    const int64_t A_u = base_b + (int64_t)kvh * n_b;
-    const int s_begin = (int)(t - A_u);
-    const int64_t seg_end = min(t_end, A_u + n_b);
-    const int s_end = (int)(seg_end - A_u);
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     const int len = clampi(a.lens[b], 0, a.len_cap);
     const int32_t *idx_row = nullptr;
     if constexpr (SPARSE)
@@ -459,9 +349,6 @@ void attn_split_kernel(AttnParams a) {
     }
 
     // Partial of this segment: unnormalised o (relative to m), (m, l) in log2 units.
-    int64_t w_lo, w_hi;
-    unit_waves(A_u, n_b, TT, W, w_lo, w_hi);
-    const size_t slot = (size_t)a.slot_base[b * a.Hkv + kvh] + (size_t)(w - w_lo);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       const int R = rb * 16 + r;
@@ -484,8 +371,7 @@ void attn_split_kernel(AttnParams a) {
         }
       }
     }
-    t = seg_end;
-  }
+  });
 }
 
 // One wave per output row (b, kvh, R): merge the unit's partials by log-sum-exp.
@@ -499,7 +385,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
   const int u = wave / a.rows;
   const int kvh = u % a.Hkv;
   const int b = u / a.Hkv;
-  const int s0 = a.slot_base[u], s1 = a.slot_base[u + 1];
+  const int s0 = a.sc.slot_base[u], s1 = a.sc.slot_base[u + 1];
 
   float M = kNegInf;
   for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_ml[((size_t)s * a.rows + R) * 2]);
@@ -537,46 +423,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
 // Workspace: prefix tables, then the partial slots. Sized for the largest
 // launch (kMaxWaves) so that the size depends on shapes only.
 struct WsLayout {
-  size_t prefix_off, base_off, ml_off, o_off, bytes;
+  size_t ml_off, o_off, bytes;
 };
 
 WsLayout ws_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t D) {
   WsLayout l;
-  const int64_t slots = kMaxWaves + B * Hkv;
-  l.prefix_off = 0;
-  l.base_off = sdh::align_up((size_t)(B + 1) * 4);
-  l.ml_off = l.base_off + sdh::align_up((size_t)(B * Hkv + 1) * 4);
+  const int64_t slots = sdh::sched_max_slots(B, Hkv);
+  l.ml_off = sdh::sched_table_bytes(B, Hkv);
   l.o_off = l.ml_off + sdh::align_up((size_t)slots * rows * 2 * 4);
   l.bytes = l.o_off + sdh::align_up((size_t)slots * rows * D * 4);
   return l;
 }
 
-// Resident waves of one split-kernel instantiation (64-thread blocks).
-template <typename T, int D, int NB, bool SPARSE>
-int resident_waves() {
-  static int cached = 0;  // written once per process; a race writes the same value
-  int w = __atomic_load_n(&cached, __ATOMIC_RELAXED);
-  if (w > 0) return w;
-  int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<T, D, NB, SPARSE>, 64, 0) !=
-          hipSuccess ||
-      hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    per_cu = kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU;
-    cus = kNumCUs;
-  }
-  w = std::min(per_cu * cus, kMaxWaves);
-  __atomic_store_n(&cached, w, __ATOMIC_RELAXED);
-  return w;
-}
-
 template <typename T, int D, int NB, bool SPARSE>
 sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
-  a.waves = resident_waves<T, D, NB, SPARSE>();
+  static int cache = 0;  // resident waves of this instantiation, queried once
+  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>),
+                                   kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, &cache);
   attn_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
-  attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.waves, 64, 0, st>>>(a);
+  attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   const int total_rows = a.B * a.Hkv * a.rows;
   attn_combine_kernel<T, D><<<(total_rows + 3) / 4, 256, 0, st>>>(a, out, lse, total_rows);
   return sdh::launch_status();
@@ -623,8 +488,7 @@ void fill_common(AttnParams &a, const sd_kv_cache *kv, const void *q, int32_t ba
   a.v_pages = kv->v_pages;
   a.page_table = kv->page_table;
   a.q = q;
-  a.seq_prefix = reinterpret_cast<int32_t *>(ws + l.prefix_off);
-  a.slot_base = reinterpret_cast<int32_t *>(ws + l.base_off);
+  sdh::sched_bind(a.sc, ws, batch, kv->num_kv_heads);
   a.part_ml = reinterpret_cast<float *>(ws + l.ml_off);
   a.part_o = reinterpret_cast<float *>(ws + l.o_off);
   a.B = batch;

@@ -19,6 +19,7 @@
 //      ties, then the window positions appended (already ascending).
 #include "sd_device.h"
 #include "sd_host.h"
+#include "sd_sched.h"
 
 #include <algorithm>
 
@@ -27,7 +28,6 @@ using namespace sdk;
 namespace {
 
 constexpr int kStepTokens = 16;
-constexpr int kSnapTargetWaves = 8192;
 constexpr int kTopkThreads = 1024;
 
 // ---------------------------------------------------------------- StreamingLLM
@@ -58,7 +58,8 @@ struct SnapParams {
   const int32_t *page_table;
   const int32_t *kv_lens;
   const void *q_obs;  // [B, W, Hq, D]
-  float *stats;       // [B*Hkv*max_chunks, rows, 2]  (m, l) log2 domain
+  Sched sc;           // persistent schedule over (sequence, KV head, 16-key step)
+  float *stats;       // [slots, rows, 2]  per-segment (m, l), log2 domain
   float *votes;       // [B*Hkv, vote_stride]
   float *pooled;      // [B*Hkv, vote_stride]
   int32_t *idx;       // [B, Hkv, budget]
@@ -66,29 +67,48 @@ struct SnapParams {
   int32_t W, Hq, Hkv, G, rows;
   int32_t num_pages, page_size, max_pages;
   int32_t len_cap, vote_stride;
-  int32_t chunk_steps, max_chunks;
   int32_t pool_kernel, budget;
   float scale_log2;
 };
 
+constexpr int kMaxChunkSteps = 128;  // sub-chunk: LDS row-id table of 128 steps x 16 keys
+constexpr int kSnapBufs = 3;         // 16-key steps of K in flight
+
+// Keys scored for sequence b: every cached key when the sequence is longer
+// than the budget (shorter ones keep everything and are not scored).
+__device__ __forceinline__ int snap_steps(const SnapParams &a, int b) {
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  return L > a.budget ? (L + kStepTokens - 1) / kStepTokens : 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void snap_plan_kernel(SnapParams a) {
+  sched_plan(a.sc, [&](int b) { return snap_steps(a, b); });
+}
+
+// Row ids (page*Hkv + kvh)*P + slot of keys [s_begin*16, s_end*16) into LDS.
+__device__ __forceinline__ void snap_fill_rows(const SnapParams &a, int b, int kvh, int s_begin, int s_end,
+                                               int *rows) {
+  const int n_tok = (s_end - s_begin) * kStepTokens;
+  for (int t = lane_id(); t < n_tok; t += 64) {
+    const int pos = s_begin * kStepTokens + t;
+    int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
+    page = clampi(page, 0, a.num_pages - 1);
+    rows[t] = (page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
+  }
+}
+
+// K operand of one step: token r of the step, head-dim chunk 32*kk + 8*g.
 template <int D>
-__device__ __forceinline__ void snap_load_k(const SnapParams &a, int b, int kvh, int s,
-                                            u32x4 (&k)[D / 32]) {
+__device__ __forceinline__ void snap_load_k(const SnapParams &a, const int *rows, u32x4 (&k)[D / 32]) {
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  const int pos = s * kStepTokens + r;
-  int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
-  page = clampi(page, 0, a.num_pages - 1);
-  const size_t row = ((size_t)page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
-  const char *kb = reinterpret_cast<const char *>(a.k_pages) + row * D * 2;
+  const char *kb = reinterpret_cast<const char *>(a.k_pages) + (size_t)rows[r] * D * 2;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    k[kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+  for (int kk = 0; kk < D / 32; ++kk) k[kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
 }
 
 template <int D, int NB>
-__device__ __forceinline__ void snap_load_q(const SnapParams &a, int b, int kvh,
-                                            u32x4 (&q)[NB][D / 32]) {
+__device__ __forceinline__ void snap_load_q(const SnapParams &a, int b, int kvh, u32x4 (&q)[NB][D / 32]) {
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
@@ -107,6 +127,14 @@ __device__ __forceinline__ void snap_load_q(const SnapParams &a, int b, int kvh,
   }
 }
 
+template <int D, int NB>
+__device__ __forceinline__ f32x4 snap_scores(const u32x4 (&k)[D / 32], const u32x4 (&q)[NB][D / 32], int rb) {
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(k[kk], q[rb][kk], sc);
+  return sc;
+}
+
 __device__ __forceinline__ void merge_ml(float &m, float &l, float m2, float l2) {
   const float M = fmaxf(m, m2);
   if (M == kNegInf) return;
@@ -115,145 +143,193 @@ __device__ __forceinline__ void merge_ml(float &m, float &l, float m2, float l2)
   m = M;
 }
 
-// Pass 1: per (b, kvh, chunk) row statistics over keys [0, L).
-template <int D, int NB>
-__global__ __launch_bounds__(64) void snap_stats_kernel(SnapParams a) {
-  const int lane = lane_id();
-  const int g = lane >> 4, r = lane & 15;
-  int unit = blockIdx.x;
-  const int chunk = unit % a.max_chunks;
-  unit /= a.max_chunks;
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
-  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  if (L <= a.budget) return;  // everything is kept; no scoring needed
-  const int n_steps = (L + kStepTokens - 1) / kStepTokens;
-  const int s_begin = chunk * a.chunk_steps;
-  if (s_begin >= n_steps) return;
-  const int s_end = min(n_steps, s_begin + a.chunk_steps);
-
-  u32x4 q[NB][D / 32];
-  snap_load_q<D, NB>(a, b, kvh, q);
-  int lim[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int R = rb * 16 + r;
-    lim[rb] = R < a.rows ? L - a.W + R / a.G : L - 1;
-  }
-  const int lim_min = L - a.W;
-
-  float m[NB], l[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    m[rb] = kNegInf;
-    l[rb] = 0.f;
-  }
-  u32x4 cur[D / 32], nxt[D / 32];
-  snap_load_k<D>(a, b, kvh, s_begin, cur);
-  for (int s = s_begin; s < s_end; ++s) {
-    if (s + 1 < s_end) snap_load_k<D>(a, b, kvh, s + 1, nxt);
-    const int tok0 = s * kStepTokens;
-    const bool boundary = tok0 + kStepTokens - 1 > lim_min;
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(cur[kk], q[rb][kk], sc);
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = sc[e] * a.scale_log2;
-      if (boundary) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tok0 + 4 * g + e > lim[rb]) p[e] = kNegInf;
-      }
-      const float pm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-      if (pm > m[rb]) {
-        l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
-        m[rb] = pm;
-      }
-      if (m[rb] != kNegInf) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(p[e] - m[rb]);
-      }
-    }
-    if (s + 1 < s_end) {
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
-    }
-  }
-  const size_t uc = ((size_t)b * a.Hkv + kvh) * a.max_chunks + chunk;
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    float mm = m[rb], ll = l[rb];
-    merge_ml(mm, ll, __shfl_xor(mm, 16, 64), __shfl_xor(ll, 16, 64));
-    merge_ml(mm, ll, __shfl_xor(mm, 32, 64), __shfl_xor(ll, 32, 64));
-    const int R = rb * 16 + r;
-    if (g == 0 && R < a.rows) {
-      a.stats[(uc * a.rows + R) * 2 + 0] = mm;
-      a.stats[(uc * a.rows + R) * 2 + 1] = ll;
-    }
-  }
+// (m, l) merged over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ void rows4_merge(float &m, float &l) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+  m = __uint_as_float(a[0]);
+  l = __uint_as_float(b[0]);
+  merge_ml(m, l, __uint_as_float(a[1]), __uint_as_float(b[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+  m = __uint_as_float(c[0]);
+  l = __uint_as_float(d[0]);
+  merge_ml(m, l, __uint_as_float(c[1]), __uint_as_float(d[1]));
 }
 
-// Pass 2: votes for the prefix keys [0, L - W).
+// Sum over the 16 lanes of each row with DPP (quad xor 1, quad xor 2, half
+// mirror, mirror): every lane of the row ends with the row sum.
+__device__ __forceinline__ float row16_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Pass 1: per segment of a unit, each window row's (max, sum of exp2) of its
+// scaled scores over the segment's keys, causal over the last W keys.
 template <int D, int NB>
-__global__ __launch_bounds__(64) void snap_votes_kernel(SnapParams a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void snap_stats_kernel(SnapParams a) {
+  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  int unit = blockIdx.x;
-  const int chunk = unit % a.max_chunks;
-  unit /= a.max_chunks;
-  const int kvh = unit % a.Hkv, b = unit / a.Hkv;
-  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  if (L <= a.budget) return;
-  const int npre = L - a.W;
-  const int n_steps = (npre + kStepTokens - 1) / kStepTokens;
-  const int s_begin = chunk * a.chunk_steps;
-  if (s_begin >= n_steps) return;
-  const int s_end = min(n_steps, s_begin + a.chunk_steps);
-
-  // Global row statistics from pass 1 (its chunks cover [0, L)).
-  const int n_chunks1 = ((L + kStepTokens - 1) / kStepTokens + a.chunk_steps - 1) / a.chunk_steps;
-  const size_t uc0 = ((size_t)b * a.Hkv + kvh) * a.max_chunks;
-  float mrow[NB], inv_l[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int R = rb * 16 + r;
-    float mm = kNegInf, ll = 0.f;
-    if (R < a.rows) {
-      for (int c = 0; c < n_chunks1; ++c)
-        merge_ml(mm, ll, a.stats[((uc0 + c) * a.rows + R) * 2], a.stats[((uc0 + c) * a.rows + R) * 2 + 1]);
-    }
-    mrow[rb] = (mm == kNegInf) ? 0.f : mm;
-    inv_l[rb] = (ll > 0.f) ? 1.f / ll : 0.f;
-  }
-
-  u32x4 q[NB][D / 32];
-  snap_load_q<D, NB>(a, b, kvh, q);
-  float *vrow = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
-  u32x4 cur[D / 32], nxt[D / 32];
-  snap_load_k<D>(a, b, kvh, s_begin, cur);
-  for (int s = s_begin; s < s_end; ++s) {
-    if (s + 1 < s_end) snap_load_k<D>(a, b, kvh, s + 1, nxt);
-    float colsum[4] = {0.f, 0.f, 0.f, 0.f};
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
+    const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+    u32x4 q[NB][D / 32];
+    snap_load_q<D, NB>(a, b, kvh, q);
+    int lim[NB];
+    float m[NB], l[NB];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      const int R = rb * 16 + r;
+      lim[rb] = R < a.rows ? L - a.W + R / a.G : L - 1;
+      m[rb] = kNegInf;
+      l[rb] = 0.f;
+    }
+    const int lim_min = L - a.W;  // keys up to here are seen by every window row
+    const float c = a.scale_log2;
+    auto plain_step = [&](const u32x4 (&k)[D / 32]) {
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(cur[kk], q[rb][kk], sc);
+      for (int rb = 0; rb < NB; ++rb) {
+        const f32x4 sc = snap_scores<D, NB>(k, q, rb);
+        const float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * c;
+        if (pm > m[rb]) {
+          l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
+          m[rb] = pm;
+        }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        colsum[e] += __builtin_amdgcn_exp2f(sc[e] * a.scale_log2 - mrow[rb]) * inv_l[rb];
+        for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m[rb]));
+      }
+    };
+    auto masked_step = [&](const u32x4 (&k)[D / 32], int s) {
+      const int tok0 = s * kStepTokens;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const f32x4 sc = snap_scores<D, NB>(k, q, rb);
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = tok0 + 4 * g + e > lim[rb] ? kNegInf : sc[e] * c;
+        const float pm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+        if (pm > m[rb]) {
+          l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
+          m[rb] = pm;
+        }
+        if (m[rb] != kNegInf) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(p[e] - m[rb]);
+        }
+      }
+    };
+    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
+      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
+      __syncthreads();
+      snap_fill_rows(a, b, kvh, sc_begin, sc_end, rows_lds);
+      __syncthreads();
+      const int last = sc_end - sc_begin - 1;
+      const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
+      const int n_plain = max(0, min(sc_end, first_masked) - sc_begin);
+      const int n_groups = n_plain / kSnapBufs;
+      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
+      u32x4 buf[kSnapBufs][D / 32];
+      if (n_groups > 0) {
+#pragma unroll
+        for (int k = 0; k < kSnapBufs - 1; ++k) snap_load_k<D>(a, rows_of(k), buf[k]);
+        for (int k0 = 0; k0 < n_groups * kSnapBufs; k0 += kSnapBufs) {
+#pragma unroll
+          for (int j = 0; j < kSnapBufs; ++j) {
+            snap_load_k<D>(a, rows_of(k0 + j + kSnapBufs - 1), buf[(j + kSnapBufs - 1) % kSnapBufs]);
+            plain_step(buf[j]);
+          }
+        }
+      }
+      for (int k = n_groups * kSnapBufs; k <= last; ++k) {
+        snap_load_k<D>(a, rows_of(k), buf[0]);
+        masked_step(buf[0], sc_begin + k);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) colsum[e] = row16_sum(colsum[e]);
-    const int tok = s * kStepTokens + 4 * g + r;  // lanes r = 0..3 of group g write token 4g+r
-    if (r < 4 && tok < npre) vrow[tok] = colsum[r];
-    if (s + 1 < s_end) {
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) cur[kk] = nxt[kk];
+    for (int rb = 0; rb < NB; ++rb) {
+      float mm = m[rb], ll = l[rb];
+      rows4_merge(mm, ll);
+      const int R = rb * 16 + r;
+      if (g == 0 && R < a.rows) {
+        a.stats[(slot * a.rows + R) * 2 + 0] = mm;
+        a.stats[(slot * a.rows + R) * 2 + 1] = ll;
+      }
     }
-  }
+  });
+}
+
+// Pass 2: votes of the prefix keys [0, L - W): merge the unit's pass-1
+// statistics into each row's log2 normaliser, recompute the scores, and sum
+// the normalised weights over the window rows of the group.
+template <int D, int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void snap_votes_kernel(SnapParams a) {
+  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end_all, size_t) {
+    const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+    const int npre = L - a.W;
+    const int s_end = min(s_end_all, (npre + kStepTokens - 1) / kStepTokens);
+    if (s_begin >= s_end) return;
+    const int u = b * a.Hkv + kvh;
+    const int s0 = a.sc.slot_base[u], s1 = a.sc.slot_base[u + 1];
+    float off[NB];  // max + log2(sum): p = exp2(score*c - off); +inf for padding rows
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int R = rb * 16 + r;
+      float mm = kNegInf, ll = 0.f;
+      if (R < a.rows)
+        for (int s = s0; s < s1; ++s) merge_ml(mm, ll, a.stats[((size_t)s * a.rows + R) * 2],
+                                               a.stats[((size_t)s * a.rows + R) * 2 + 1]);
+      off[rb] = (ll > 0.f) ? mm + __log2f(ll) : __builtin_inff();
+    }
+    u32x4 q[NB][D / 32];
+    snap_load_q<D, NB>(a, b, kvh, q);
+    const float c = a.scale_log2;
+    float *vrow = a.votes + (size_t)u * a.vote_stride;
+    auto step = [&](const u32x4 (&k)[D / 32], int s) {
+      float col[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const f32x4 sc = snap_scores<D, NB>(k, q, rb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) col[e] += __builtin_amdgcn_exp2f(fmaf(sc[e], c, -off[rb]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) col[e] = row16_sum_dpp(col[e]);
+      const int tok = s * kStepTokens + 4 * g + r;  // lanes r < 4 of group g write key 4g + r
+      const float v = r == 0 ? col[0] : (r == 1 ? col[1] : (r == 2 ? col[2] : col[3]));
+      if (r < 4 && tok < npre) vrow[tok] = v;
+    };
+    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
+      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
+      __syncthreads();
+      snap_fill_rows(a, b, kvh, sc_begin, sc_end, rows_lds);
+      __syncthreads();
+      const int last = sc_end - sc_begin - 1;
+      const int n_groups = (last + 1) / kSnapBufs;
+      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
+      u32x4 buf[kSnapBufs][D / 32];
+      if (n_groups > 0) {
+#pragma unroll
+        for (int k = 0; k < kSnapBufs - 1; ++k) snap_load_k<D>(a, rows_of(k), buf[k]);
+        for (int k0 = 0; k0 < n_groups * kSnapBufs; k0 += kSnapBufs) {
+#pragma unroll
+          for (int j = 0; j < kSnapBufs; ++j) {
+            snap_load_k<D>(a, rows_of(k0 + j + kSnapBufs - 1), buf[(j + kSnapBufs - 1) % kSnapBufs]);
+            step(buf[j], sc_begin + k0 + j);
+          }
+        }
+      }
+      for (int k = n_groups * kSnapBufs; k <= last; ++k) {
+        snap_load_k<D>(a, rows_of(k), buf[0]);
+        step(buf[0], sc_begin + k);
+      }
+    }
+  });
 }
 
 // Block-wide exclusive scan of one uint32 per thread (1024 threads); returns the
@@ -377,46 +453,42 @@ __global__ __launch_bounds__(kTopkThreads) void snap_topk_kernel(SnapParams a) {
   for (int w = tid; w < a.W; w += kTopkThreads) out[keep + w] = npre + w;
 }
 
-struct SnapPlan {
-  int chunk_steps, max_chunks, vote_stride;
-  size_t stats_bytes, votes_bytes, pooled_bytes, ws_bytes;
+struct SnapLayout {
+  int vote_stride;
+  size_t stats_off, votes_off, pooled_off, bytes;
 };
 
-SnapPlan plan_snap(int64_t B, int64_t Hkv, int64_t rows, int64_t max_len) {
-  SnapPlan p;
-  const int64_t steps = std::max<int64_t>(1, sdh::ceil_div(max_len, kStepTokens));
-  const int64_t units = B * Hkv;
-  int64_t cs = sdh::ceil_div(steps * units, kSnapTargetWaves);
-  cs = std::max<int64_t>(cs, 16);
-  cs = std::min<int64_t>(cs, steps);
-  p.chunk_steps = (int)cs;
-  p.max_chunks = (int)sdh::ceil_div(steps, cs);
-  p.vote_stride = (int)std::max<int64_t>(1, max_len);
-  p.stats_bytes = sdh::align_up((size_t)units * p.max_chunks * rows * 2 * 4);
-  p.votes_bytes = sdh::align_up((size_t)units * p.vote_stride * 4);
-  p.pooled_bytes = p.votes_bytes;
-  p.ws_bytes = p.stats_bytes + p.votes_bytes + p.pooled_bytes;
-  return p;
+SnapLayout snap_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t max_len) {
+  SnapLayout l;
+  l.vote_stride = (int)std::max<int64_t>(1, max_len);
+  l.stats_off = sdh::sched_table_bytes(B, Hkv);
+  l.votes_off = l.stats_off + sdh::align_up((size_t)sdh::sched_max_slots(B, Hkv) * rows * 2 * 4);
+  l.pooled_off = l.votes_off + sdh::align_up((size_t)B * Hkv * l.vote_stride * 4);
+  l.bytes = l.pooled_off + sdh::align_up((size_t)B * Hkv * l.vote_stride * 4);
+  return l;
 }
 
 template <int D, int NB>
-void launch_snap_pair(const SnapParams &a, unsigned grid, hipStream_t st) {
-  snap_stats_kernel<D, NB><<<grid, 64, 0, st>>>(a);
-  snap_votes_kernel<D, NB><<<grid, 64, 0, st>>>(a);
+void launch_snap_pair(SnapParams &a, hipStream_t st) {
+  static int cache = 0;  // resident waves of this instantiation, queried once
+  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(snap_stats_kernel<D, NB>), 2 * kSimdsPerCU,
+                                   &cache);
+  snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+  snap_stats_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  snap_votes_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
 }
 
 template <int D>
-sd_status launch_snap(const SnapParams &a, int B, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)B * a.Hkv * a.max_chunks);
+sd_status launch_snap(SnapParams &a, int B, hipStream_t st) {
   switch ((a.rows + 15) / 16) {
-    case 1: launch_snap_pair<D, 1>(a, grid, st); break;
-    case 2: launch_snap_pair<D, 2>(a, grid, st); break;
-    case 3: launch_snap_pair<D, 3>(a, grid, st); break;
-    case 4: launch_snap_pair<D, 4>(a, grid, st); break;
-    case 5: launch_snap_pair<D, 5>(a, grid, st); break;
-    case 6: launch_snap_pair<D, 6>(a, grid, st); break;
-    case 7: launch_snap_pair<D, 7>(a, grid, st); break;
-    case 8: launch_snap_pair<D, 8>(a, grid, st); break;
+    case 1: launch_snap_pair<D, 1>(a, st); break;
+    case 2: launch_snap_pair<D, 2>(a, st); break;
+    case 3: launch_snap_pair<D, 3>(a, st); break;
+    case 4: launch_snap_pair<D, 4>(a, st); break;
+    case 5: launch_snap_pair<D, 5>(a, st); break;
+    case 6: launch_snap_pair<D, 6>(a, st); break;
+    case 7: launch_snap_pair<D, 7>(a, st); break;
+    case 8: launch_snap_pair<D, 8>(a, st); break;
     default: return SD_ERR_UNSUPPORTED;
   }
   snap_topk_kernel<<<(unsigned)(B * a.Hkv), kTopkThreads, 0, st>>>(a);
@@ -442,7 +514,7 @@ extern "C" size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window,
       num_q_heads % num_kv_heads != 0)
     return 0;
   const int rows = num_q_heads / num_kv_heads * window;
-  return plan_snap(batch, num_kv_heads, rows, max_kv_len).ws_bytes;
+  return snap_layout(batch, num_kv_heads, rows, max_kv_len).bytes;
 }
 
 extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
@@ -464,8 +536,9 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
   const int G = num_q_heads / kv->num_kv_heads;
   SD_REQUIRE((int64_t)G * window <= 128, SD_ERR_UNSUPPORTED);
   const int rows = G * window;
-  SnapPlan p = plan_snap(batch, kv->num_kv_heads, rows, max_kv_len);
-  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
+  const SnapLayout lay = snap_layout(batch, kv->num_kv_heads, rows, max_kv_len);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= lay.bytes, SD_ERR_WORKSPACE);
+  SD_REQUIRE((int64_t)batch * kv->num_kv_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
 
   SnapParams a{};
   a.k_pages = kv->k_pages;
@@ -473,9 +546,10 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
   a.kv_lens = kv->kv_lens;
   a.q_obs = q_obs;
   char *ws = reinterpret_cast<char *>(workspace);
-  a.stats = reinterpret_cast<float *>(ws);
-  a.votes = reinterpret_cast<float *>(ws + p.stats_bytes);
-  a.pooled = reinterpret_cast<float *>(ws + p.stats_bytes + p.votes_bytes);
+  sdh::sched_bind(a.sc, ws, batch, kv->num_kv_heads);
+  a.stats = reinterpret_cast<float *>(ws + lay.stats_off);
+  a.votes = reinterpret_cast<float *>(ws + lay.votes_off);
+  a.pooled = reinterpret_cast<float *>(ws + lay.pooled_off);
   a.idx = idx;
   a.sel_lens = sel_lens;
   a.W = window;
@@ -487,9 +561,7 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
   a.page_size = kv->page_size;
   a.max_pages = kv->max_pages;
   a.len_cap = max_kv_len;
-  a.vote_stride = p.vote_stride;
-  a.chunk_steps = p.chunk_steps;
-  a.max_chunks = p.max_chunks;
+  a.vote_stride = lay.vote_stride;
   a.pool_kernel = pool_kernel;
   a.budget = budget;
   a.scale_log2 = softmax_scale * kLog2e;
