@@ -12,11 +12,15 @@
 //      probabilities over the window rows of the group (in-lane over row
 //      tiles, then over the 16 lanes of each MFMA column group);
 //   3. snap_topk:   one 1024-thread block per (sequence, KV head): clipped
-//      max-pool of the votes, 4-pass 8-bit radix select of the
-//      (budget - W)-th largest pooled value (non-negative floats order as
-//      their bit patterns), an order-preserving block compaction that takes
-//      every value above the threshold and the lowest positions among the
-//      ties, then the window positions appended (already ascending).
+//      max-pool of the votes into registers, the (budget - W)-th largest
+//      pooled value found bit by bit from the top (non-negative floats order
+//      as their bit patterns; each bit is one ballot count over the block),
+//      then an order-preserving write of every value above that threshold
+//      and of the lowest positions among the ties, from one block scan of
+//      per-wave counts; the window positions are appended (ascending).
+//      Prefixes longer than 64 Ki keys and pool kernels wider than 129 use a
+//      variant that keeps the pooled values in the workspace and selects with
+//      a 4-pass 8-bit radix.
 #include "sd_device.h"
 #include "sd_host.h"
 #include "sd_sched.h"
@@ -29,6 +33,7 @@ namespace {
 
 constexpr int kStepTokens = 16;
 constexpr int kTopkThreads = 1024;
+constexpr int kMaxPoolHalf = 64;  // register top-K: pool kernels up to 129
 
 // ---------------------------------------------------------------- StreamingLLM
 __global__ __launch_bounds__(256) void streaming_select_kernel(const int32_t *kv_lens, int sink,
@@ -363,7 +368,159 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *l
   return res;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void snap_topk_kernel(SnapParams a) {
+// Sum over the wave (lane 0 holds the total): DPP within rows of 16, then
+// the row totals.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Block-wide exclusive scan of one uint64 per thread (WAVES waves).
+template <int WAVES>
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t *lds_waves) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds_waves[wave] = x;
+  __syncthreads();
+  uint64_t before = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w)
+    if (w < wave) before += lds_waves[w];
+  __syncthreads();
+  return before + x - v;
+}
+
+// Top-K of the pooled votes with the pooled values held in registers: thread
+// t of THREADS holds positions t + THREADS*i, i < VPT, so (i, wave, lane)
+// order is position order. The threshold key T is the largest key with at
+// least `keep` keys >= T, built greedily from the top bit down, one block
+// count per bit (counting several candidate bits per barrier measured slower:
+// the compares, not the barriers, dominate). The output slot of a kept position is (#keys > T before it) +
+// min(#keys == T before it, need), need = keep - #keys > T: every key above T
+// and the lowest-position ties.
+template <int THREADS, int VPT>
+__global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
+  constexpr int kWaves = THREADS / 64;
+  static_assert(VPT * kWaves <= THREADS, "one scan entry per thread");
+  __shared__ uint32_t cnt[2][kWaves];
+  __shared__ uint64_t pre[VPT * kWaves];
+  __shared__ uint64_t scan_waves[kWaves];
+  __shared__ float pool_lds[2][THREADS + 2 * kMaxPoolHalf];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
+  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
+  if (L <= a.budget) {
+    for (int t = tid; t < a.budget; t += THREADS) out[t] = t < L ? t : -1;
+    return;
+  }
+  const int npre = L - a.W;  // <= THREADS * VPT and pool_kernel / 2 <= kMaxPoolHalf (host)
+  const uint32_t keep = (uint32_t)(a.budget - a.W);
+  const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  const int half = a.pool_kernel / 2;
+
+  // Clipped max-pool. Raw votes of position tid + THREADS*i go to key[i] (0
+  // past the prefix: votes are >= 0, so zero padding equals clipping); tile i
+  // sits in LDS at offset kMaxPoolHalf with `half` halo values on each side
+  // (the left halo from the previous tile's buffer, the right one from
+  // key[i + 1]), and key[i] becomes the pooled value. 0 keys are never counted
+  // below (every candidate has a bit set).
+  uint32_t key[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int j = tid + THREADS * i;
+    key[i] = j < npre ? __float_as_uint(votes[j]) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    float *cur = pool_lds[i & 1];
+    const float *prev = pool_lds[(i + 1) & 1];
+    cur[kMaxPoolHalf + tid] = __uint_as_float(key[i]);
+    if (tid < half) {
+      cur[kMaxPoolHalf - half + tid] = i > 0 ? prev[kMaxPoolHalf + THREADS - half + tid] : 0.f;
+      cur[kMaxPoolHalf + THREADS + tid] = i + 1 < VPT ? __uint_as_float(key[i + 1 < VPT ? i + 1 : i]) : 0.f;
+    }
+    __syncthreads();
+    const float *w = cur + kMaxPoolHalf + tid;
+    float v = w[0];
+    if (half <= 3) {  // short windows: all reads issued together
+      float x[6];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        x[2 * t] = w[-(t + 1)];
+        x[2 * t + 1] = w[t + 1];
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        if (t < half) v = fmaxf(v, fmaxf(x[2 * t], x[2 * t + 1]));
+    } else {
+      for (int t = 1; t <= half; ++t) v = fmaxf(v, fmaxf(w[-t], w[t]));
+    }
+    key[i] = tid + THREADS * i < npre ? __float_as_uint(v) : 0u;
+  }
+
+  // Votes are sums of exponentials (>= +0), so bit 31 is clear.
+  uint32_t T = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) c += key[i] >= cand ? 1u : 0u;
+    c = wave_sum_u32(c);
+    if (lane == 0) cnt[bit & 1][wave] = c;
+    __syncthreads();  // a buffer is rewritten two bits later, after the next barrier
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += cnt[bit & 1][w];
+    if (total >= keep) T = cand;
+  }
+
+  // Per (i, wave): keys above T (low word) and equal to T (high word).
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const bool valid = tid + THREADS * i < npre;
+    const uint64_t gm = __ballot(key[i] > T);
+    const uint64_t em = __ballot(valid && key[i] == T);
+    if (lane == 0) pre[i * kWaves + wave] = (uint64_t)__popcll(gm) | ((uint64_t)__popcll(em) << 32);
+  }
+  __syncthreads();
+  const uint64_t mine = tid < VPT * kWaves ? pre[tid] : 0ull;
+  const uint64_t ex = block_exclusive_scan_u64<kWaves>(mine, scan_waves);
+  if (tid == THREADS - 1) scan_waves[0] = ex + mine;  // totals
+  if (tid < VPT * kWaves) pre[tid] = ex;
+  __syncthreads();
+  const uint32_t need = keep - (uint32_t)scan_waves[0];
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int j = tid + THREADS * i;
+    const bool valid = j < npre;
+    const bool gt = key[i] > T, eq = valid && key[i] == T;
+    const uint64_t gm = __ballot(gt);
+    const uint64_t em = __ballot(eq);
+    const uint64_t p = pre[i * kWaves + wave];
+    const uint32_t gt_before = (uint32_t)p + (uint32_t)__popcll(gm & below);
+    const uint32_t eq_before = (uint32_t)(p >> 32) + (uint32_t)__popcll(em & below);
+    if (gt)
+      out[gt_before + min(eq_before, need)] = j;
+    else if (eq && eq_before < need)
+      out[gt_before + eq_before] = j;
+  }
+  for (int w = tid; w < a.W; w += THREADS) out[keep + w] = npre + w;
+}
+
+// Long prefixes: pooled values in the workspace, 4-pass 8-bit radix select.
+__global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapParams a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t scan_tmp[40];
   __shared__ uint32_t sel_digit, sel_above;
@@ -468,6 +625,19 @@ SnapLayout snap_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t max_len) {
   return l;
 }
 
+// Register top-K with the fewest values per thread that cover the prefix.
+void launch_topk_reg(SnapParams &a, unsigned blocks, int64_t npre_cap, hipStream_t st) {
+  constexpr int TH = kTopkThreads;
+  if (npre_cap <= 8 * TH)
+    snap_topk_kernel<TH, 8><<<blocks, TH, 0, st>>>(a);
+  else if (npre_cap <= 16 * TH)
+    snap_topk_kernel<TH, 16><<<blocks, TH, 0, st>>>(a);
+  else if (npre_cap <= 32 * TH)
+    snap_topk_kernel<TH, 32><<<blocks, TH, 0, st>>>(a);
+  else
+    snap_topk_kernel<TH, 64><<<blocks, TH, 0, st>>>(a);
+}
+
 template <int D, int NB>
 void launch_snap_pair(SnapParams &a, hipStream_t st) {
   static int cache = 0;  // resident waves of this instantiation, queried once
@@ -491,7 +661,12 @@ sd_status launch_snap(SnapParams &a, int B, hipStream_t st) {
     case 8: launch_snap_pair<D, 8>(a, st); break;
     default: return SD_ERR_UNSUPPORTED;
   }
-  snap_topk_kernel<<<(unsigned)(B * a.Hkv), kTopkThreads, 0, st>>>(a);
+  const unsigned blocks = (unsigned)(B * a.Hkv);
+  const int64_t npre_cap = (int64_t)a.len_cap - a.W;
+  if (a.pool_kernel / 2 > kMaxPoolHalf || npre_cap > (int64_t)kTopkThreads * 64)
+    snap_topk_global_kernel<<<blocks, kTopkThreads, 0, st>>>(a);
+  else
+    launch_topk_reg(a, blocks, npre_cap, st);
   return sdh::launch_status();
 }
 

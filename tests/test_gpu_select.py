@@ -84,6 +84,13 @@ SNAP_CASES = [
     ("pool1-w1", 8, 2, 128, [900], 1, 1, 40, 0.0),
     ("d64-pool3", 8, 2, 64, [1234, 517], 4, 3, 100, 0.10),
     ("rows48-ragged-pages", 24, 2, 128, [1111, 4096, 333], 4, 5, 300, 0.05),
+    # longer prefixes: 16, 32 and 64 pooled values per top-K thread
+    ("prefix-12k", 8, 2, 128, [12000, 5000], 8, 7, 512, 0.10),
+    ("prefix-30k-rows128", 32, 1, 128, [30000], 4, 7, 1024, 0.10),
+    ("prefix-40k", 8, 2, 64, [40000, 33000], 8, 5, 2048, 0.10),
+    # radix variant: prefix beyond 64 Ki keys, and a pool kernel wider than 129
+    ("prefix-70k-radix", 8, 2, 64, [70000], 4, 3, 1000, 0.10),
+    ("pool131-radix", 8, 2, 128, [3000, 2500], 8, 131, 300, 0.0),
 ]
 
 
@@ -126,3 +133,23 @@ def test_snapkv_then_draft_end_to_end():
     out, lse = run_draft(kv_t, q, 1, 8, idx, sel)
     o_ref, l_ref = oracle.sparse_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, idx_ref, sel_ref, 1.0)
     compare_attn(out, lse, o_ref, l_ref, BF16)
+
+
+@pytest.mark.parametrize("lens,pool", [([2000, 1500], 7), ([3000], 131), ([70000], 3)],
+                         ids=["register", "radix-wide-pool", "radix-long"])
+def test_snapkv_all_ties_take_lowest_positions(lens, pool):
+    """All keys zero: every prefix position gets the same vote, bitwise, so the
+    kept set is the lowest budget - W positions plus the window."""
+    W, budget, Hq, Hkv = 8, 256, 8, 2
+    kv_t = paged_kv(57, lens, Hkv, 128 if pool != 3 else 64, BF16, "cuda")
+    d = kv_t.k_pages.shape[-1]
+    for b, L in enumerate(lens):
+        pages = kv_t.page_table[b, :-(-L // kv_t.page_size)].long()
+        kv_t.k_pages[pages] = 0
+    q_obs = queries(57, 4, (len(lens), W, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    idx, sel = run_snapkv(kv_t, q_obs, W, Hq, pool, budget)
+    keep = budget - W
+    for b, L in enumerate(lens):
+        want = np.concatenate([np.arange(keep), np.arange(L - W, L)])
+        assert (idx[b].cpu().numpy() == want).all()
+    assert (sel.cpu().numpy() == budget).all()
