@@ -6,11 +6,13 @@
 // votes). SnapKV runs in three kernels:
 //   1. snap_stats:  per (sequence, KV head, chunk of keys) the online max and
 //      sum of exp2 of every window row's scaled scores (causal over the last
-//      W keys), S^T = K Q^T on 16x16x32 bf16 MFMA, one wave per unit;
-//   2. snap_votes:  merge the chunk statistics into each row's (max, 1/sum),
-//      recompute the scores of the prefix keys, normalise, and sum the
-//      probabilities over the window rows of the group (in-lane over row
-//      tiles, then over the 16 lanes of each MFMA column group);
+//      W keys), S^T = K Q^T on 16x16x32 bf16 MFMA, persistent waves over
+//      (sequence, KV head, 16-key step) with K streamed through an LDS ring;
+//   2. snap_votes:  merge the chunk statistics into each row's log2
+//      normaliser, recompute the scores of the prefix keys as S = Q K^T (each
+//      lane holds four window rows of one key), normalise, and sum over the
+//      rows in-lane and across the four lane groups; votes of four steps are
+//      gathered in a register and stored 64 keys at a time;
 //   3. snap_topk:   one 1024-thread block per (sequence, KV head): clipped
 //      max-pool of the votes into registers, the (budget - W)-th largest
 //      pooled value found bit by bit from the top (non-negative floats order
@@ -76,8 +78,25 @@ struct SnapParams {
   float scale_log2;
 };
 
-constexpr int kMaxChunkSteps = 128;  // sub-chunk: LDS row-id table of 128 steps x 16 keys
-constexpr int kSnapBufs = 3;         // 16-key steps of K in flight
+constexpr int kRing = 4;       // 16-key K steps per wave in LDS: 3 loading while one is scored
+constexpr int kWinSteps = 64;  // steps per row-id window (lane i holds the first row of step i)
+constexpr float kHeadroom = 8.f;  // log2 slack of the lazily moved row max in the stats pass
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Asynchronous copies of 16 or 4 bytes per lane from global memory to LDS at
+// dst + lane * size (dst is wave-uniform). The builtin exists only for the
+// device target; a host pass that sees it drops the kernels that use it.
+__device__ __forceinline__ void lds_dma16(const void *src, __attribute__((address_space(3))) void *dst) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address_space(3))) void *dst) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+#endif
+}
 
 // Keys scored for sequence b: every cached key when the sequence is longer
 // than the budget (shorter ones keep everything and are not scored).
@@ -90,27 +109,130 @@ __global__ __launch_bounds__(kPlanThreads) void snap_plan_kernel(SnapParams a) {
   sched_plan(a.sc, [&](int b) { return snap_steps(a, b); });
 }
 
-// Row ids (page*Hkv + kvh)*P + slot of keys [s_begin*16, s_end*16) into LDS.
-__device__ __forceinline__ void snap_fill_rows(const SnapParams &a, int b, int kvh, int s_begin, int s_end,
-                                               int *rows) {
-  const int n_tok = (s_end - s_begin) * kStepTokens;
-  for (int t = lane_id(); t < n_tok; t += 64) {
-    const int pos = s_begin * kStepTokens + t;
-    int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
-    page = clampi(page, 0, a.num_pages - 1);
-    rows[t] = (page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
-  }
-}
-
-// K operand of one step: token r of the step, head-dim chunk 32*kk + 8*g.
+// K of one unit's consecutive 16-key steps streamed through a per-wave LDS
+// ring by asynchronous global->LDS loads, so loads in flight hold no
+// registers. Step s lands in slot s % kRing as 16 token rows; 16-byte chunk j
+// of token t is stored at chunk position j ^ (t mod chunks-per-row), so the
+// MFMA operand reads (16 tokens x one chunk) fall in distinct banks.
+//
+// Waits are explicit: every step issues the same number of loads (prefetches
+// past the segment re-load its last step into a slot no longer read), so
+// "at most (kRing-1)*kInsts newer operations outstanding" means the step has
+// landed; any other memory operation only makes that wait stricter. The ring
+// is read with inline ds_read blocks that end in their own lgkmcnt wait, which
+// keeps the compiler from adding its own vmcnt(0) before LDS reads (it cannot
+// tell which slot an asynchronous load writes).
+//
+// Row ids come in 64-step windows: lane i of rows_a / rows_b holds the first
+// row of step wb + i / wb + 64 + i, and the page-table entries of the window
+// after those are copied into LDS one window ahead, so sliding the window
+// never waits on a load issued in the same iteration.
 template <int D>
-__device__ __forceinline__ void snap_load_k(const SnapParams &a, const int *rows, u32x4 (&k)[D / 32]) {
-  const int lane = lane_id();
-  const int g = lane >> 4, r = lane & 15;
-  const char *kb = reinterpret_cast<const char *>(a.k_pages) + (size_t)rows[r] * D * 2;
+struct KStream {
+  static constexpr int kRowChunks = D * 2 / 16;  // 16-byte chunks per token row
+  static constexpr int kStepChunks = kStepTokens * kRowChunks;
+  static constexpr int kInsts = kStepChunks / 64;  // loads per lane and step
+  static constexpr int kLdsBytes = kRing * kStepChunks * 16 + kWinSteps * 4;
+  lds_u32x4 *ring;                                 // [kRing][kStepChunks]
+  __attribute__((address_space(3))) int32_t *entries;  // [kWinSteps] page-table entries
+  const char *kp;
+  const int32_t *pt;  // page-table row of the sequence
+  int Hkv, kvh, P, num_pages, last;
+  int lane_off[kInsts];  // byte offset of this lane's chunk inside a step
+  int wb, rows_a, rows_b;
+
+  __device__ KStream(const SnapParams &a, int b, int kvh_, int last_step, char *lds)
+      : ring((lds_u32x4 *)(__attribute__((address_space(3))) char *)lds),
+        entries((__attribute__((address_space(3))) int32_t *)(
+            (__attribute__((address_space(3))) char *)lds + kRing * kStepChunks * 16)),
+        kp(reinterpret_cast<const char *>(a.k_pages)), pt(a.page_table + (size_t)b * a.max_pages),
+        Hkv(a.Hkv), kvh(kvh_), P(a.page_size), num_pages(a.num_pages), last(last_step) {
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) k[kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
-}
+    for (int c = 0; c < kInsts; ++c) {
+      const int idx = c * 64 + lane_id();
+      const int t = idx / kRowChunks, p = idx % kRowChunks;
+      lane_off[c] = (t * kRowChunks + (p ^ (t & (kRowChunks - 1)))) * 16;
+    }
+  }
+  __device__ const int32_t *entry_ptr(int s) const { return pt + min(s, last) * kStepTokens / P; }
+  // First token row of step s (16 keys never straddle a page: P % 16 == 0).
+  __device__ int row_from(int entry, int s) const {
+    const int pos = min(s, last) * kStepTokens;
+    return (clampi(entry, 0, num_pages - 1) * Hkv + kvh) * P + pos % P;
+  }
+  // Copy the page-table entries of window steps w0 + lane into LDS.
+  __device__ void fetch_entries(int w0) {
+    lds_dma4(entry_ptr(w0 + lane_id()), entries);
+  }
+  __device__ int read_entry() const {
+    int e = 0;
+    const uint32_t addr = (uint32_t)(size_t)(entries + lane_id());
+#if __HIP_DEVICE_COMPILE__  // VGPR asm constraints exist only for the device target
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(e) : "v"(addr) : "memory");
+#endif
+    return e;
+  }
+  __device__ void issue(int s, int slot) {
+    const int d = s - wb;
+    const int row = d < kWinSteps ? __builtin_amdgcn_readlane(rows_a, d)
+                                  : __builtin_amdgcn_readlane(rows_b, d - kWinSteps);
+    const char *src = kp + (size_t)row * D * 2;
+#pragma unroll
+    for (int c = 0; c < kInsts; ++c)
+      lds_dma16(src + lane_off[c], ring + slot * kStepChunks + c * 64);
+  }
+  __device__ void begin(int s_begin) {
+    const int lane = lane_id();
+    wb = s_begin;
+    rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
+    rows_b = row_from(*entry_ptr(wb + kWinSteps + lane), wb + kWinSteps + lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // entries LDS of a previous segment is free
+    fetch_entries(wb + 2 * kWinSteps);
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) issue(min(s_begin + i, last), (s_begin + i) % kRing);
+  }
+  // Before scoring step s: slide the row window, start loading step
+  // s + kRing - 1 into the slot step s - 1 used, and wait for step s.
+  __device__ void advance(int s) {
+    if (s - wb == kWinSteps) {
+      const int lane = lane_id();
+      wb += kWinSteps;
+      rows_a = rows_b;
+      // entries of this window were requested 64 steps ago: at least kRing-1
+      // steps' loads were issued after them and waited for since
+      rows_b = row_from(read_entry(), wb + kWinSteps + lane);
+      fetch_entries(wb + 2 * kWinSteps);
+    }
+    issue(min(s + kRing - 1, last), (s + kRing - 1) % kRing);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts) : "memory");
+  }
+  // MFMA A operand of step s: token r, head-dim chunk 4*kk + g.
+  __device__ void operand(int s, u32x4 (&k)[D / 32]) const {
+    const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+    const lds_u32x4 *rowp = ring + (s % kRing) * kStepChunks + r * kRowChunks;
+    uint32_t ad[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) ad[kk] = (uint32_t)(size_t)(rowp + ((4 * kk + g) ^ (r & (kRowChunks - 1))));
+#if __HIP_DEVICE_COMPILE__  // VGPR asm constraints exist only for the device target
+    if constexpr (D == 128) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "memory");
+    } else {
+      static_assert(D == 64, "head_dim 64 or 128");
+      asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(k[0]), "=&v"(k[1])
+                   : "v"(ad[0]), "v"(ad[1])
+                   : "memory");
+    }
+#endif
+  }
+  // Loads still writing LDS must land before the wave's LDS is released.
+  __device__ static void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+};
 
 template <int D, int NB>
 __device__ __forceinline__ void snap_load_q(const SnapParams &a, int b, int kvh, u32x4 (&q)[NB][D / 32]) {
@@ -176,35 +298,46 @@ __device__ __forceinline__ float row16_sum_dpp(float v) {
 // scaled scores over the segment's keys, causal over the last W keys.
 template <int D, int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void snap_stats_kernel(SnapParams a) {
-  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
+  __shared__ __attribute__((aligned(16))) char lds[KStream<D>::kLdsBytes];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
   sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
-    const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+    s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+    s_end = __builtin_amdgcn_readfirstlane(s_end);
+    const int L = __builtin_amdgcn_readfirstlane(clampi(a.kv_lens[b], 0, a.len_cap));
     u32x4 q[NB][D / 32];
     snap_load_q<D, NB>(a, b, kvh, q);
-    int lim[NB];
     float m[NB], l[NB];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const int R = rb * 16 + r;
-      lim[rb] = R < a.rows ? L - a.W + R / a.G : L - 1;
       m[rb] = kNegInf;
       l[rb] = 0.f;
     }
     const int lim_min = L - a.W;  // keys up to here are seen by every window row
     const float c = a.scale_log2;
+    // Unmasked steps: the row max moves lazily. Exponents are taken against
+    // the current m; only when some lane's exponent exceeds kHeadroom (sums of
+    // up to 2^kHeadroom per key stay exact enough in fp32) does the wave rebase
+    // those lanes on their exact running max, in a rare uniform branch.
     auto plain_step = [&](const u32x4 (&k)[D / 32]) {
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const f32x4 sc = snap_scores<D, NB>(k, q, rb);
-        const float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * c;
-        if (pm > m[rb]) {
-          l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
-          m[rb] = pm;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], c, -m[rb]);
+        const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (__builtin_expect(__ballot(xm > kHeadroom) != 0, 0)) {
+          if (xm > kHeadroom) {  // also the first key of a lane (m = -inf gives +inf)
+            const float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * c;
+            l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
+            m[rb] = pm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], c, -pm);
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(fmaf(sc[e], c, -m[rb]));
+        for (int e = 0; e < 4; ++e) l[rb] += __builtin_amdgcn_exp2f(x[e]);
       }
     };
     auto masked_step = [&](const u32x4 (&k)[D / 32], int s) {
@@ -213,8 +346,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
       for (int rb = 0; rb < NB; ++rb) {
         const f32x4 sc = snap_scores<D, NB>(k, q, rb);
         float p[4];
+        const int R = rb * 16 + r;
+        const int lim = R < a.rows ? L - a.W + R / a.G : L - 1;  // last key row R sees
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = tok0 + 4 * g + e > lim[rb] ? kNegInf : sc[e] * c;
+        for (int e = 0; e < 4; ++e) p[e] = tok0 + 4 * g + e > lim ? kNegInf : sc[e] * c;
         const float pm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
         if (pm > m[rb]) {
           l[rb] = (m[rb] == kNegInf) ? 0.f : l[rb] * __builtin_amdgcn_exp2f(m[rb] - pm);
@@ -226,32 +361,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
         }
       }
     };
-    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
-      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
-      __syncthreads();
-      snap_fill_rows(a, b, kvh, sc_begin, sc_end, rows_lds);
-      __syncthreads();
-      const int last = sc_end - sc_begin - 1;
-      const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
-      const int n_plain = max(0, min(sc_end, first_masked) - sc_begin);
-      const int n_groups = n_plain / kSnapBufs;
-      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
-      u32x4 buf[kSnapBufs][D / 32];
-      if (n_groups > 0) {
-#pragma unroll
-        for (int k = 0; k < kSnapBufs - 1; ++k) snap_load_k<D>(a, rows_of(k), buf[k]);
-        for (int k0 = 0; k0 < n_groups * kSnapBufs; k0 += kSnapBufs) {
-#pragma unroll
-          for (int j = 0; j < kSnapBufs; ++j) {
-            snap_load_k<D>(a, rows_of(k0 + j + kSnapBufs - 1), buf[(j + kSnapBufs - 1) % kSnapBufs]);
-            plain_step(buf[j]);
-          }
-        }
-      }
-      for (int k = n_groups * kSnapBufs; k <= last; ++k) {
-        snap_load_k<D>(a, rows_of(k), buf[0]);
-        masked_step(buf[0], sc_begin + k);
-      }
+    KStream<D> ks(a, b, kvh, s_end - 1, lds);
+    ks.begin(s_begin);
+    const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
+    const int plain_end = max(s_begin, min(s_end, first_masked));
+    for (int s = s_begin; s < plain_end; ++s) {
+      ks.advance(s);
+      u32x4 k[D / 32];
+      ks.operand(s, k);
+      plain_step(k);
+    }
+    for (int s = plain_end; s < s_end; ++s) {
+      ks.advance(s);
+      u32x4 k[D / 32];
+      ks.operand(s, k);
+      masked_step(k, s);
     }
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
@@ -264,6 +388,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
       }
     }
   });
+  KStream<D>::drain();
 }
 
 // Pass 2: votes of the prefix keys [0, L - W): merge the unit's pass-1
@@ -271,17 +396,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
 // the normalised weights over the window rows of the group.
 template <int D, int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void snap_votes_kernel(SnapParams a) {
-  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
+  __shared__ __attribute__((aligned(16))) char lds[KStream<D>::kLdsBytes];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
+  // Votes of four consecutive steps gather in one register: lane 16*(s%4) + r
+  // keeps key r of step s.
   sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end_all, size_t) {
-    const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+    s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+    const int L = __builtin_amdgcn_readfirstlane(clampi(a.kv_lens[b], 0, a.len_cap));
     const int npre = L - a.W;
-    const int s_end = min(s_end_all, (npre + kStepTokens - 1) / kStepTokens);
+    const int s_end = __builtin_amdgcn_readfirstlane(min(s_end_all, (npre + kStepTokens - 1) / kStepTokens));
     if (s_begin >= s_end) return;
     const int u = b * a.Hkv + kvh;
     const int s0 = a.sc.slot_base[u], s1 = a.sc.slot_base[u + 1];
-    float off[NB];  // max + log2(sum): p = exp2(score*c - off); +inf for padding rows
+    // Scores are computed as S = Q K^T (window rows on M, keys on N): lane
+    // (g, r) holds rows 16*rb + 4g + e of key r, so a key's vote is an in-lane
+    // sum over (rb, e) plus a sum over the four lane groups. off[rb][e]: max +
+    // log2(sum) of that row (+inf for padding rows: p = 0).
+    float off[NB][4];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       const int R = rb * 16 + r;
@@ -289,52 +421,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
       if (R < a.rows)
         for (int s = s0; s < s1; ++s) merge_ml(mm, ll, a.stats[((size_t)s * a.rows + R) * 2],
                                                a.stats[((size_t)s * a.rows + R) * 2 + 1]);
-      off[rb] = (ll > 0.f) ? mm + __log2f(ll) : __builtin_inff();
+      const float o = (ll > 0.f) ? mm + __log2f(ll) : __builtin_inff();  // row R, held by lanes r
+#pragma unroll
+      for (int e = 0; e < 4; ++e) off[rb][e] = __shfl(o, 4 * g + e, 64);
     }
     u32x4 q[NB][D / 32];
     snap_load_q<D, NB>(a, b, kvh, q);
     const float c = a.scale_log2;
     float *vrow = a.votes + (size_t)u * a.vote_stride;
-    auto step = [&](const u32x4 (&k)[D / 32], int s) {
-      float col[4] = {0.f, 0.f, 0.f, 0.f};
+    const int t_lo = s_begin * kStepTokens, t_hi = min(s_end * kStepTokens, npre);
+    KStream<D> ks(a, b, kvh, s_end - 1, lds);
+    ks.begin(s_begin);
+    float gathered = 0.f;
+    for (int s = s_begin; s < s_end; ++s) {
+      ks.advance(s);
+      u32x4 k[D / 32];
+      ks.operand(s, k);
+      float acc = 0.f;
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
-        const f32x4 sc = snap_scores<D, NB>(k, q, rb);
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) col[e] += __builtin_amdgcn_exp2f(fmaf(sc[e], c, -off[rb]));
+        for (int kk = 0; kk < D / 32; ++kk) sc = mfma_16x16x32_bf16(q[rb][kk], k[kk], sc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += __builtin_amdgcn_exp2f(fmaf(sc[e], c, -off[rb][e]));
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) col[e] = row16_sum_dpp(col[e]);
-      const int tok = s * kStepTokens + 4 * g + r;  // lanes r < 4 of group g write key 4g + r
-      const float v = r == 0 ? col[0] : (r == 1 ? col[1] : (r == 2 ? col[2] : col[3]));
-      if (r < 4 && tok < npre) vrow[tok] = v;
-    };
-    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
-      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
-      __syncthreads();
-      snap_fill_rows(a, b, kvh, sc_begin, sc_end, rows_lds);
-      __syncthreads();
-      const int last = sc_end - sc_begin - 1;
-      const int n_groups = (last + 1) / kSnapBufs;
-      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
-      u32x4 buf[kSnapBufs][D / 32];
-      if (n_groups > 0) {
-#pragma unroll
-        for (int k = 0; k < kSnapBufs - 1; ++k) snap_load_k<D>(a, rows_of(k), buf[k]);
-        for (int k0 = 0; k0 < n_groups * kSnapBufs; k0 += kSnapBufs) {
-#pragma unroll
-          for (int j = 0; j < kSnapBufs; ++j) {
-            snap_load_k<D>(a, rows_of(k0 + j + kSnapBufs - 1), buf[(j + kSnapBufs - 1) % kSnapBufs]);
-            step(buf[j], sc_begin + k0 + j);
-          }
-        }
-      }
-      for (int k = n_groups * kSnapBufs; k <= last; ++k) {
-        snap_load_k<D>(a, rows_of(k), buf[0]);
-        step(buf[0], sc_begin + k);
+      // sum over the four lane groups: every lane (g, r) ends with key r's vote
+      auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+      const float acc2 = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+      auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc2), __float_as_uint(acc2), false, false);
+      const float w = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+      if ((lane >> 4) == (s & 3)) gathered = w;
+      if ((s & 3) == 3 || s == s_end - 1) {
+        const int tok = (s & ~3) * kStepTokens + lane;  // lanes cover the four steps' 64 keys
+        if (tok >= t_lo && tok < t_hi) vrow[tok] = gathered;
       }
     }
   });
+  KStream<D>::drain();
 }
 
 // Block-wide exclusive scan of one uint32 per thread (1024 threads); returns the
