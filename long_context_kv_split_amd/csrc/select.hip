@@ -193,7 +193,10 @@ struct KStream {
   }
   // Before scoring step s: slide the row window, start loading step
   // s + kRing - 1 into the slot step s - 1 used, and wait for step s.
-  __device__ void advance(int s) {
+  // `stores` (0 or 1) is the number of store instructions the wave issued
+  // after step s's loads (a store shares the load counter; counting it avoids
+  // waiting for its acknowledgement).
+  __device__ void advance(int s, int stores = 0) {
     if (s - wb == kWinSteps) {
       const int lane = lane_id();
       wb += kWinSteps;
@@ -204,7 +207,10 @@ struct KStream {
       fetch_entries(wb + 2 * kWinSteps);
     }
     issue(min(s + kRing - 1, last), (s + kRing - 1) % kRing);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts) : "memory");
+    if (stores)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts) : "memory");
   }
   // MFMA A operand of step s: token r, head-dim chunk 4*kk + g.
   __device__ void operand(int s, u32x4 (&k)[D / 32]) const {
@@ -433,8 +439,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     KStream<D> ks(a, b, kvh, s_end - 1, lds);
     ks.begin(s_begin);
     float gathered = 0.f;
+    // Iteration of the last vote store: the next kRing - 1 waits count it.
+    // The store always has an active lane (the first key of the step just
+    // scored is in range), so it is always issued.
+    int stored_at = -(1 << 30);
     for (int s = s_begin; s < s_end; ++s) {
-      ks.advance(s);
+      ks.advance(s, s - stored_at < kRing ? 1 : 0);
       u32x4 k[D / 32];
       ks.operand(s, k);
       float acc = 0.f;
@@ -455,6 +465,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
       if ((s & 3) == 3 || s == s_end - 1) {
         const int tok = (s & ~3) * kStepTokens + lane;  // lanes cover the four steps' 64 keys
         if (tok >= t_lo && tok < t_hi) vrow[tok] = gathered;
+        stored_at = s;
       }
     }
   });

@@ -88,6 +88,10 @@ SNAP_CASES = [
     ("prefix-12k", 8, 2, 128, [12000, 5000], 8, 7, 512, 0.10),
     ("prefix-30k-rows128", 32, 1, 128, [30000], 4, 7, 1024, 0.10),
     ("prefix-40k", 8, 2, 64, [40000, 33000], 8, 5, 2048, 0.10),
+    # 5..8 row tiles: two waves per block share the K stream
+    ("rows80-two-waves", 8, 2, 128, [2500, 1900], 20, 7, 256, 0.10),
+    ("rows96-two-waves", 16, 2, 128, [2100, 3300], 12, 5, 300, 0.05),
+    ("d64-rows112-two-waves", 16, 2, 64, [3000, 1000], 14, 5, 300, 0.10),
     # radix variant: prefix beyond 64 Ki keys, and a pool kernel wider than 129
     ("prefix-70k-radix", 8, 2, 64, [70000], 4, 3, 1000, 0.10),
     ("pool131-radix", 8, 2, 128, [3000, 2500], 8, 131, 300, 0.0),
