@@ -90,7 +90,8 @@ typedef struct {
  *   rounded to nearest even). lse: [batch, n_q, num_q_heads] float32 natural-
  *   log log-sum-exp of the scaled scores, or NULL. A row that sees no key gets
  *   out = 0 and lse = -inf.
- * Limits: (num_q_heads / num_kv_heads) * n_q <= 64.
+ * Limits: (num_q_heads / num_kv_heads) * n_q <= 64; batch * ceil(max_kv_len / 16)
+ *   < 2^31 (else SD_ERR_UNSUPPORTED).
  */
 sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
                          int32_t num_q_heads, int32_t max_kv_len, float softmax_scale,
@@ -113,7 +114,8 @@ size_t sd_verify_attn_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_h
  *   sel_lens[b] entries of idx[b, idx_heads > 1 ? g : 0, :].
  * Every query row attends to every selected position (q: [batch, n_q,
  *   num_q_heads, head_dim], normally n_q = 1). out/lse as for verify.
- * Limits: (num_q_heads / num_kv_heads) * n_q <= 64.
+ * Limits: (num_q_heads / num_kv_heads) * n_q <= 64; batch * ceil(max_sel / 16)
+ *   < 2^31 (else SD_ERR_UNSUPPORTED).
  */
 sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
                                int32_t num_q_heads, const int32_t *idx, const int32_t *sel_lens,
@@ -151,7 +153,8 @@ sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, int32_t sin
  * q_obs: [batch, window, num_q_heads, head_dim] of kv->dtype.
  * idx: int32 [batch, num_kv_heads, budget]; sel_lens: int32 [batch] = min(L, budget).
  * Limits: budget > window >= 1; (num_q_heads / num_kv_heads) * window <= 128;
- *   pool_kernel odd and >= 1; max_kv_len bounds kv_lens.
+ *   pool_kernel odd and >= 1; max_kv_len bounds kv_lens; batch *
+ *   ceil(max_kv_len / 16) < 2^31 (else SD_ERR_UNSUPPORTED).
  */
 sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
                            int32_t window, int32_t num_q_heads, int32_t pool_kernel,

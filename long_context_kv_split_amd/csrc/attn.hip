@@ -522,6 +522,8 @@ extern "C" sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_
   if (s != SD_OK) return s;
   SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
              SD_ERR_INVALID_ARG);
+  // the schedule keeps per-sequence step prefix sums in int32
+  SD_REQUIRE((int64_t)batch * sdh::ceil_div(max_kv_len, 16) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
   const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
@@ -551,6 +553,7 @@ extern "C" sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, 
   SD_REQUIRE(idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
   SD_REQUIRE(idx_heads == 1 || idx_heads == kv->num_kv_heads, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_sel > 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE((int64_t)batch * sdh::ceil_div(max_sel, 16) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
   const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};

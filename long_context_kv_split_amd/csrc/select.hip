@@ -849,6 +849,8 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
   const SnapLayout lay = snap_layout(batch, kv->num_kv_heads, rows, max_kv_len);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= lay.bytes, SD_ERR_WORKSPACE);
   SD_REQUIRE((int64_t)batch * kv->num_kv_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
+  // the schedule keeps per-sequence step prefix sums in int32
+  SD_REQUIRE((int64_t)batch * sdh::ceil_div(max_kv_len, 16) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
 
   SnapParams a{};
   a.k_pages = kv->k_pages;

@@ -98,6 +98,8 @@ WS = ctypes.c_void_p(0x6000)
     ({}, dict(ws=None), sd.SD_ERR_WORKSPACE),
     ({}, dict(ws_bytes=1), sd.SD_ERR_WORKSPACE),
     ({}, dict(scale=float("nan")), sd.SD_ERR_INVALID_ARG),
+    # batch * ceil(max_len / 16) steps would overflow the schedule's int32 prefix sums
+    ({"max_pages": 4096}, dict(batch=1 << 20, max_len=1 << 16), sd.SD_ERR_UNSUPPORTED),
 ])
 def test_verify_rejects_invalid_arguments(L, over, args, want):
     kv = _kv(**over)
