@@ -11,8 +11,8 @@
 //   2. snap_votes:  merge the chunk statistics into each row's log2
 //      normaliser, recompute the scores of the prefix keys as S = Q K^T (each
 //      lane holds four window rows of one key), normalise, and sum over the
-//      rows in-lane and across the four lane groups; votes of four steps are
-//      gathered in a register and stored 64 keys at a time;
+//      rows in-lane and across the four lane groups; votes are staged in LDS
+//      and stored 512 keys at a time;
 //   3. snap_topk:   one 1024-thread block per (sequence, KV head): clipped
 //      max-pool of the votes into registers, the (budget - W)-th largest
 //      pooled value found bit by bit from the top (non-negative floats order
@@ -80,6 +80,7 @@ struct SnapParams {
 
 constexpr int kRing = 4;       // 16-key K steps per wave in LDS: 3 loading while one is scored
 constexpr int kWinSteps = 64;  // steps per row-id window (lane i holds the first row of step i)
+constexpr int kStageSteps = 32;  // votes staged in LDS and stored every 32 steps
 constexpr float kHeadroom = 8.f;  // log2 slack of the lazily moved row max in the stats pass
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -96,6 +97,23 @@ __device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address
 #if __HIP_DEVICE_COMPILE__
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 #endif
+}
+
+// LDS word access the compiler does not track (so it adds no wait for the
+// asynchronous ring loads); the read returns with its data.
+__device__ __forceinline__ void lds_write_f32(const char *lds, int byte_off, float v) {
+  const uint32_t addr = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+#endif
+}
+__device__ __forceinline__ float lds_read_f32(const char *lds, int byte_off) {
+  float v = 0.f;
+  const uint32_t addr = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+#endif
+  return v;
 }
 
 // Keys scored for sequence b: every cached key when the sequence is longer
@@ -193,10 +211,7 @@ struct KStream {
   }
   // Before scoring step s: slide the row window, start loading step
   // s + kRing - 1 into the slot step s - 1 used, and wait for step s.
-  // `stores` (0 or 1) is the number of store instructions the wave issued
-  // after step s's loads (a store shares the load counter; counting it avoids
-  // waiting for its acknowledgement).
-  __device__ void advance(int s, int stores = 0) {
+  __device__ void advance(int s) {
     if (s - wb == kWinSteps) {
       const int lane = lane_id();
       wb += kWinSteps;
@@ -207,10 +222,7 @@ struct KStream {
       fetch_entries(wb + 2 * kWinSteps);
     }
     issue(min(s + kRing - 1, last), (s + kRing - 1) % kRing);
-    if (stores)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts + 1) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRing - 1) * kInsts) : "memory");
   }
   // MFMA A operand of step s: token r, head-dim chunk 4*kk + g.
   __device__ void operand(int s, u32x4 (&k)[D / 32]) const {
@@ -402,11 +414,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
 // the normalised weights over the window rows of the group.
 template <int D, int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void snap_votes_kernel(SnapParams a) {
-  __shared__ __attribute__((aligned(16))) char lds[KStream<D>::kLdsBytes];
+  // K stream, then the votes of up to kStageSteps steps (16 floats per step).
+  // Stores share the in-order load counter with the K stream, so a store
+  // stalls the stream until it is acknowledged: votes leave in batches of
+  // 512 keys (8 stores) every kStageSteps steps.
+  constexpr int kStageOff = KStream<D>::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kStageOff + kStageSteps * kStepTokens * 4];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  // Votes of four consecutive steps gather in one register: lane 16*(s%4) + r
-  // keeps key r of step s.
   sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end_all, size_t) {
     s_begin = __builtin_amdgcn_readfirstlane(s_begin);
     const int L = __builtin_amdgcn_readfirstlane(clampi(a.kv_lens[b], 0, a.len_cap));
@@ -435,16 +450,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     snap_load_q<D, NB>(a, b, kvh, q);
     const float c = a.scale_log2;
     float *vrow = a.votes + (size_t)u * a.vote_stride;
-    const int t_lo = s_begin * kStepTokens, t_hi = min(s_end * kStepTokens, npre);
+    const int t_hi = min(s_end * kStepTokens, npre);
     KStream<D> ks(a, b, kvh, s_end - 1, lds);
     ks.begin(s_begin);
-    float gathered = 0.f;
-    // Iteration of the last vote store: the next kRing - 1 waits count it.
-    // The store always has an active lane (the first key of the step just
-    // scored is in range), so it is always issued.
-    int stored_at = -(1 << 30);
+    // Staged steps [w0, s] of the current batch to global memory.
+    auto flush = [&](int w0, int s) {
+      const int n = (s - w0 + 1) * kStepTokens;
+#pragma unroll
+      for (int i = 0; i < kStageSteps * kStepTokens / 64; ++i) {
+        const int j = i * 64 + lane;
+        const int tok = w0 * kStepTokens + j;
+        const float v = lds_read_f32(lds, kStageOff + j * 4);
+        if (j < n && tok < t_hi) vrow[tok] = v;
+      }
+    };
     for (int s = s_begin; s < s_end; ++s) {
-      ks.advance(s, s - stored_at < kRing ? 1 : 0);
+      ks.advance(s);
       u32x4 k[D / 32];
       ks.operand(s, k);
       float acc = 0.f;
@@ -461,12 +482,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
       const float acc2 = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
       auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc2), __float_as_uint(acc2), false, false);
       const float w = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
-      if ((lane >> 4) == (s & 3)) gathered = w;
-      if ((s & 3) == 3 || s == s_end - 1) {
-        const int tok = (s & ~3) * kStepTokens + lane;  // lanes cover the four steps' 64 keys
-        if (tok >= t_lo && tok < t_hi) vrow[tok] = gathered;
-        stored_at = s;
-      }
+      const int k_in = (s - s_begin) % kStageSteps;
+      if (g == 0) lds_write_f32(lds, kStageOff + (k_in * kStepTokens + r) * 4, w);
+      if (k_in == kStageSteps - 1 || s == s_end - 1) flush(s - k_in, s);
     }
   });
   KStream<D>::drain();
