@@ -6,6 +6,7 @@ value within 1e-5 relative of the threshold value (the budget-W-th largest),
 where float32 (GPU) and float64 (oracle) scoring may legitimately order two
 distinct values differently. Such cases are counted and reported.
 """
+import dataclasses
 import zlib
 
 import numpy as np
@@ -41,10 +42,10 @@ def test_streaming_select_parity(sink, recent):
     assert (idx.cpu().numpy() == idx_ref).all()
 
 
-def run_snapkv(kv_t, q_obs, window, Hq, pool, budget):
+def run_snapkv(kv_t, q_obs, window, Hq, pool, budget, max_kv_len=None):
     kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
     B = kv.batch
-    mk = max(1, kv_t.max_kv_len)
+    mk = max(1, kv_t.max_kv_len) if max_kv_len is None else max_kv_len
     idx = torch.full((B, kv.num_kv_heads, budget), 7, dtype=torch.int32, device="cuda")
     sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
     ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, window, Hq, kv.num_kv_heads, mk), "cuda")
@@ -157,3 +158,34 @@ def test_snapkv_all_ties_take_lowest_positions(lens, pool):
         want = np.concatenate([np.arange(keep), np.arange(L - W, L)])
         assert (idx[b].cpu().numpy() == want).all()
     assert (sel.cpu().numpy() == budget).all()
+
+
+@pytest.mark.parametrize("page_size", [32, 48])
+def test_snapkv_page_sizes(page_size):
+    """16-key steps inside larger pages (the K stream's row arithmetic), shuffled."""
+    lens = [2000, 3333]
+    kv_t = paged_kv(71, lens, 2, 128, BF16, "cuda", shuffle=True, spike_frac=0.1, page_size=page_size)
+    q_obs = queries(71, 4, (2, 16, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    idx, sel = run_snapkv(kv_t, q_obs, 16, 8, 7, 256)
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    16, 7, 256, 1.0, return_pooled=True)
+    near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, 16, 256)
+    assert near <= 1
+
+
+def test_snapkv_max_len_above_lengths():
+    """max_kv_len well above every length: plan, workspace and top-K variant are
+    sized from it, the results from the real lengths."""
+    lens = [1500, 900]
+    kv_t = paged_kv(73, lens, 2, 128, BF16, "cuda", shuffle=True, spike_frac=0.1)
+    q_obs = queries(73, 4, (2, 8, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    P = kv_t.page_size
+    # let the page table cover max_kv_len: pad it with the spare page
+    pad = torch.full((2, 2600 // P), kv_t.spare_page, dtype=torch.int32, device="cuda")
+    kv_t = dataclasses.replace(kv_t, page_table=torch.cat([kv_t.page_table, pad], dim=1).contiguous())
+    mk = kv_t.page_table.shape[1] * P
+    idx, sel = run_snapkv(kv_t, q_obs, 8, 8, 7, 128, max_kv_len=mk)
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    8, 7, 128, 1.0, return_pooled=True)
+    near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, 8, 128)
+    assert near <= 1
