@@ -24,6 +24,12 @@ Functions and what pins them (tests/test_oracle_*.py):
   selection.snapkv_select  brute-force subset search on tiny inputs, special cases
   accept.spec_accept       hand-worked fixtures, Monte Carlo distribution
                            preservation, closed-form acceptance probabilities
+                           (with gamma = 0 it is the draft-token sampler)
+  round.kv_append          caches built from dense concatenations; verify after
+                           append equals SDPA with a causal mask
+  round.kv_advance         hand values, the round identity L + 1 + n
+  round.sparse_attn_tail   SDPA over explicitly gathered rows; tail-only equals
+                           dense decode
 No function here is "parity unpinned".
 """
 from oracle.attention import attend, sparse_attn, token_rows, verify_attn  # noqa: F401
@@ -35,4 +41,5 @@ from oracle.selection import (  # noqa: F401
     topk_lowest_index,
 )
 from oracle.accept import softmax, spec_accept  # noqa: F401
+from oracle.round import draft_positions, kv_advance, kv_append, sparse_attn_tail  # noqa: F401
 from oracle.common import f64  # noqa: F401
