@@ -161,3 +161,22 @@ def test_temperature_scales_logits():
     b = oracle.spec_accept(zt * 2.0, zd * 2.0, x, ua, us, temperature=1.0)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_gamma_zero_is_inverse_cdf_sampling_from_softmax():
+    """With no drafts the round emits one token drawn from p_0 = softmax(z / T):
+    the draft-token sampler. Hand-worked inverse CDF and Monte Carlo."""
+    p = np.array([0.2, 0.5, 0.3])
+    zt = np.log(p)[None, None, :].repeat(6, axis=0)
+    us = np.array([0.0, 0.1, 0.25, 0.69, 0.71, 0.99])[:, None]  # off the CDF boundaries 0.2, 0.7
+    none = np.zeros((6, 0))
+    n, out, _ = oracle.spec_accept(zt, none.reshape(6, 0, 3), none.astype(int), none, us)
+    assert (n == 0).all()
+    assert list(out[:, 0]) == [0, 0, 1, 1, 2, 2]
+    rng = np.random.default_rng(72)
+    q = rng.dirichlet(np.ones(7))
+    trials = 40000
+    zt = np.log(q)[None, None, :].repeat(trials, axis=0)
+    n, out, _ = oracle.spec_accept(zt, np.zeros((trials, 0, 7)), np.zeros((trials, 0), int),
+                                   np.zeros((trials, 0)), rng.random((trials, 1)))
+    assert _chi2_ok(out[:, 0], q) > 1e-3
