@@ -127,6 +127,27 @@ size_t sd_draft_attn_sparse_workspace_size(int32_t batch, int32_t n_q, int32_t n
                                            int32_t max_sel);
 
 /*
+ * Draft attention over the selection plus the tokens appended since it was
+ * made (MagicDec notes, §3.3 and §4.1: the static compressed cache is chosen
+ * once at prefill; each draft step then also reads the tokens generated after
+ * that, the drafts of the current round included).
+ *
+ * As sd_draft_attn_sparse, and sequence b, KV head g then also reads
+ * positions tail_begin[b] .. kv->kv_lens[b] - 1 in order (an empty range when
+ * kv_lens[b] <= tail_begin[b]). tail_begin: int32 [batch], device. max_tail
+ *   bounds kv_lens[b] - tail_begin[b] (longer tails are cut to it).
+ * Workspace: sd_draft_attn_sparse_workspace_size.
+ * Limits: as sd_draft_attn_sparse, with batch * ceil((max_sel + max_tail) / 16)
+ *   < 2^31; 0 <= max_tail <= max_pages * page_size.
+ */
+sd_status sd_draft_attn_sparse_tail(const sd_kv_cache *kv, const void *q, int32_t batch,
+                                    int32_t n_q, int32_t num_q_heads, const int32_t *idx,
+                                    const int32_t *sel_lens, int32_t idx_heads, int32_t max_sel,
+                                    const int32_t *tail_begin, int32_t max_tail,
+                                    float softmax_scale, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * StreamingLLM draft set (named as a static KV selection in the MagicDec
  * notes, §4.4 and §5.2): the first `sink` positions and the last `recent`
  * positions of each sequence, ascending, without duplicates:
@@ -192,6 +213,40 @@ sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab);
+
+/*
+ * Draft-token sampling is sd_spec_accept with gamma = 0: draft_logits,
+ * draft_tokens and u_accept may be NULL, n_accepted is 0 and out_tokens[b, 0]
+ * is drawn from softmax(target_logits[b, 0] / temperature) by inverse CDF with
+ * u_sample[b, 0].
+ */
+
+/*
+ * Append n_new tokens' K/V at the end of every sequence (MagicDec notes,
+ * §3.1-§3.3: each draft step and the verification pass add the K/V of the
+ * tokens they process to the cache).
+ *
+ * k_new, v_new: [batch, n_new, num_kv_heads, head_dim] of kv->dtype, device.
+ * Token j of sequence b goes to position p = kv->kv_lens[b] + j: page
+ *   kv->page_table[b, p / page_size], slot p % page_size, of the pools kv
+ *   points at. THIS CALL WRITES kv->k_pages and kv->v_pages (the only entry
+ *   point that does); it does not change kv_lens (see sd_kv_advance).
+ * The caller provides the pages; positions at or past max_pages * page_size
+ *   are not written, and page ids are clamped into [0, num_pages).
+ */
+sd_status sd_kv_append(const sd_kv_cache *kv, const void *k_new, const void *v_new,
+                       int32_t batch, int32_t n_new, void *stream);
+
+/*
+ * kv_lens[b] <- max(0, kv_lens[b] + add + (n_accepted ? n_accepted[b] : 0)),
+ * on the device. After appending a round's gamma + 1 tokens and accepting n
+ * drafts: add = -gamma keeps the round's first token and the accepted drafts
+ * (MagicDec notes, §3.1: rejected drafts are discarded).
+ * kv_lens: int32 [batch], device, updated in place; n_accepted: int32 [batch]
+ *   or NULL.
+ */
+sd_status sd_kv_advance(int32_t *kv_lens, const int32_t *n_accepted, int32_t batch, int32_t add,
+                        void *stream);
 
 /* Static string for a status code (never NULL). */
 const char *sd_status_string(sd_status status);

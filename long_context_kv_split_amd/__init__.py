@@ -3,8 +3,9 @@
 The computation lives in libsdkv.so, a HIP library with the C ABI of
 include/sd.h: verify attention over a paged bf16 KV cache (split-KV MFMA
 kernel plus combine), sparse draft attention over gathered positions,
-StreamingLLM and SnapKV draft-KV selection, and modified-rejection speculative
-acceptance. This package is its ctypes binding (argument marshalling only) and
+StreamingLLM and SnapKV draft-KV selection, modified-rejection speculative
+acceptance, and the round's cache bookkeeping (KV append, length advance, draft
+over the selection plus the appended tail). This package is its ctypes binding (argument marshalling only) and
 its build script; importing it never computes anything on the CPU.
 """
 from long_context_kv_split_amd.binding import (  # noqa: F401
@@ -20,7 +21,10 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     SdError,
     lib,
     sd_draft_attn_sparse,
+    sd_draft_attn_sparse_tail,
     sd_draft_attn_sparse_workspace_size,
+    sd_kv_advance,
+    sd_kv_append,
     sd_kv_cache,
     sd_snapkv_select,
     sd_snapkv_select_workspace_size,

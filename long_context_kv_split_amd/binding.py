@@ -55,6 +55,9 @@ _SIGNATURES = {
     "sd_verify_attn_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "sd_draft_attn_sparse": (_I, [_KV, _P, _I, _I, _I, _P, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_draft_attn_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "sd_draft_attn_sparse_tail": (_I, [_KV, _P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _F, _P, _P, _P, _S, _P]),
+    "sd_kv_append": (_I, [_KV, _P, _P, _I, _I, _P]),
+    "sd_kv_advance": (_I, [_P, _P, _I, _I, _P]),
     "sd_streaming_select": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "sd_snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_snapkv_select_workspace_size": (_S, [_I, _I, _I, _I, _I]),
@@ -207,6 +210,38 @@ def sd_draft_attn_sparse(kv, q, n_q, num_q_heads, idx, sel_lens, idx_heads, max_
     _check(lib().sd_draft_attn_sparse(kv.ref, qp, B, n_q, num_q_heads, ip, sp, idx_heads, max_sel,
                                       softmax_scale, op, lp, wp, wb, _stream(stream)),
            "sd_draft_attn_sparse")
+
+
+def sd_draft_attn_sparse_tail(kv, q, n_q, num_q_heads, idx, sel_lens, idx_heads, max_sel, tail_begin,
+                              max_tail, softmax_scale, out, lse=None, workspace=None, stream=None):
+    B, d = kv.batch, kv.head_dim
+    n = B * n_q * num_q_heads * d
+    qp = _dev(q, "q", kv.dtype, n)
+    op = _dev(out, "out", kv.dtype, n)
+    lp = _dev(lse, "lse", torch.float32, B * n_q * num_q_heads, allow_none=True)
+    ip = _dev(idx, "idx", torch.int32, B * idx_heads * max_sel)
+    sp = _dev(sel_lens, "sel_lens", torch.int32, B)
+    tp = _dev(tail_begin, "tail_begin", torch.int32, B)
+    need = sd_draft_attn_sparse_workspace_size(B, n_q, num_q_heads, kv.num_kv_heads, d, max_sel)
+    wp, wb = _ws(workspace, need)
+    _check(lib().sd_draft_attn_sparse_tail(kv.ref, qp, B, n_q, num_q_heads, ip, sp, idx_heads, max_sel, tp,
+                                           max_tail, softmax_scale, op, lp, wp, wb, _stream(stream)),
+           "sd_draft_attn_sparse_tail")
+
+
+def sd_kv_append(kv, k_new, v_new, n_new, stream=None):
+    B, d = kv.batch, kv.head_dim
+    n = B * n_new * kv.num_kv_heads * d
+    kp = _dev(k_new, "k_new", kv.dtype, n)
+    vp = _dev(v_new, "v_new", kv.dtype, n)
+    _check(lib().sd_kv_append(kv.ref, kp, vp, B, n_new, _stream(stream)), "sd_kv_append")
+
+
+def sd_kv_advance(kv_lens, n_accepted, add, stream=None):
+    B = kv_lens.numel()
+    lp = _dev(kv_lens, "kv_lens", torch.int32, B)
+    np_ = _dev(n_accepted, "n_accepted", torch.int32, B, allow_none=True)
+    _check(lib().sd_kv_advance(lp, np_, B, add, _stream(stream)), "sd_kv_advance")
 
 
 def sd_streaming_select(kv_lens, sink, recent, idx, sel_lens, stream=None):

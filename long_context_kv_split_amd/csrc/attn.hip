@@ -53,8 +53,20 @@ struct AttnParams {
   int32_t num_pages, page_size, max_pages;
   int32_t idx_heads, max_sel;
   int32_t len_cap;  // upper clamp of lens
+  // draft only: positions [tail_begin[b], kv_lens[b]) read after the selection
+  const int32_t *tail_begin;  // [B] or null (no tail)
+  const int32_t *kv_lens;     // the cache's lengths (end of the tail)
+  int32_t tail_cap;           // upper clamp of a tail's length
   float scale_log2;
 };
+
+// Tokens read for sequence b: the clamped length, plus the draft's tail.
+__device__ __forceinline__ int tail_len(const AttnParams &a, int b) {
+  return a.tail_begin ? clampi(a.kv_lens[b] - a.tail_begin[b], 0, a.tail_cap) : 0;
+}
+__device__ __forceinline__ int attn_len(const AttnParams &a, int b) {
+  return clampi(a.lens[b], 0, a.len_cap) + tail_len(a, b);
+}
 
 template <typename T>
 struct EltInfo;
@@ -98,11 +110,14 @@ __device__ __forceinline__ void load_dwords(uint32_t (&dst)[N], const char *p) {
 // Row id (page*Hkv + kvh)*P + slot of cached token `t` of the chunk's token
 // list: position t (verify) or idx_row[t] (draft), through the page table.
 template <bool SPARSE>
-__device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, int t, int len,
+__device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, int t, int len, int sel,
                                          const int32_t *idx_row) {
   int pos;
   if constexpr (SPARSE) {
-    pos = clampi(idx_row[clampi(t, 0, len - 1)], 0, a.max_pages * a.page_size - 1);
+    // token t of the draft: entry t of the selection, then the tail in order
+    const int tt = clampi(t, 0, len - 1);
+    pos = tt < sel ? idx_row[tt] : a.tail_begin[b] + (tt - sel);
+    pos = clampi(pos, 0, a.max_pages * a.page_size - 1);
   } else {
     pos = t;
   }
@@ -255,7 +270,7 @@ struct AttnTuning {
 
 
 __device__ __forceinline__ int unit_steps(const AttnParams &a, int b) {
-  return (clampi(a.lens[b], 0, a.len_cap) + kStepTokens - 1) / kStepTokens;
+  return (attn_len(a, b) + kStepTokens - 1) / kStepTokens;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams a) {
@@ -274,7 +289,8 @@ void attn_split_kernel(AttnParams a) {
   const int g = lane >> 4, r = lane & 15;
 
   sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
-    const int len = clampi(a.lens[b], 0, a.len_cap);
+    const int len = attn_len(a, b);
+    const int sel = clampi(a.lens[b], 0, a.len_cap);  // draft: entries of idx read before the tail
     const int32_t *idx_row = nullptr;
     if constexpr (SPARSE)
       idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
@@ -318,7 +334,7 @@ void attn_split_kernel(AttnParams a) {
       const int n_tok = (sc_end - sc_begin) * kStepTokens;
       __syncthreads();  // the previous sub-chunk's table reads are done
       for (int tt = lane; tt < n_tok; tt += 64)
-        rows_lds[tt] = token_row<SPARSE>(a, b, kvh, sc_begin * kStepTokens + tt, len, idx_row);
+        rows_lds[tt] = token_row<SPARSE>(a, b, kvh, sc_begin * kStepTokens + tt, len, sel, idx_row);
       __syncthreads();
       // Main loop: groups of NBUF steps that need no mask, with a ring of NBUF
       // step buffers unrolled so every buffer has a fixed role and the loop
@@ -542,18 +558,20 @@ extern "C" size_t sd_draft_attn_sparse_workspace_size(int32_t batch, int32_t n_q
   return sd_verify_attn_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_sel);
 }
 
-extern "C" sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, int32_t batch,
-                                          int32_t n_q, int32_t num_q_heads, const int32_t *idx,
-                                          const int32_t *sel_lens, int32_t idx_heads,
-                                          int32_t max_sel, float softmax_scale, void *out,
-                                          float *lse, void *workspace, size_t workspace_bytes,
-                                          void *stream) {
+namespace {
+
+sd_status draft_impl(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q, int32_t num_q_heads,
+                     const int32_t *idx, const int32_t *sel_lens, int32_t idx_heads, int32_t max_sel,
+                     const int32_t *tail_begin, int32_t max_tail, float softmax_scale, void *out, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream) {
   sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, softmax_scale, out);
   if (s != SD_OK) return s;
   SD_REQUIRE(idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
   SD_REQUIRE(idx_heads == 1 || idx_heads == kv->num_kv_heads, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(max_sel > 0, SD_ERR_INVALID_ARG);
-  SD_REQUIRE((int64_t)batch * sdh::ceil_div(max_sel, 16) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
+  SD_REQUIRE(max_sel > 0 && max_tail >= 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE((int64_t)max_tail <= (int64_t)kv->max_pages * kv->page_size, SD_ERR_INVALID_ARG);
+  SD_REQUIRE((int64_t)batch * sdh::ceil_div((int64_t)max_sel + max_tail, 16) < ((int64_t)1 << 31),
+             SD_ERR_UNSUPPORTED);
   const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
@@ -563,5 +581,32 @@ extern "C" sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, 
   a.idx_heads = idx_heads;
   a.max_sel = max_sel;
   a.len_cap = max_sel;
+  a.tail_begin = tail_begin;
+  a.kv_lens = kv->kv_lens;
+  a.tail_cap = max_tail;
   return run_attn<true>(a, kv->head_dim, kv->dtype, out, lse, sdh::as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" sd_status sd_draft_attn_sparse(const sd_kv_cache *kv, const void *q, int32_t batch,
+                                          int32_t n_q, int32_t num_q_heads, const int32_t *idx,
+                                          const int32_t *sel_lens, int32_t idx_heads,
+                                          int32_t max_sel, float softmax_scale, void *out,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream) {
+  return draft_impl(kv, q, batch, n_q, num_q_heads, idx, sel_lens, idx_heads, max_sel, nullptr, 0,
+                    softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" sd_status sd_draft_attn_sparse_tail(const sd_kv_cache *kv, const void *q, int32_t batch,
+                                               int32_t n_q, int32_t num_q_heads, const int32_t *idx,
+                                               const int32_t *sel_lens, int32_t idx_heads,
+                                               int32_t max_sel, const int32_t *tail_begin,
+                                               int32_t max_tail, float softmax_scale, void *out,
+                                               float *lse, void *workspace, size_t workspace_bytes,
+                                               void *stream) {
+  SD_REQUIRE(tail_begin != nullptr, SD_ERR_INVALID_ARG);
+  return draft_impl(kv, q, batch, n_q, num_q_heads, idx, sel_lens, idx_heads, max_sel, tail_begin, max_tail,
+                    softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }

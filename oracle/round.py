@@ -13,7 +13,7 @@ bookkeeping open; the plainest reading, used here:
     lives at pool[page_table[b, t // P], kv_head, t % P] (kv_append).
   * After acceptance the cache keeps the round's first token and the n accepted
     drafts, dropping the gamma - n rejected ones: kv_len <- kv_len - gamma + n
-    (kv_advance with add = -gamma).
+    (kv_advance with add = -gamma); a length never goes below zero.
   * While drafting, the draft attends to the positions chosen at prefill plus
     every position appended since: the tail [tail_begin, kv_len)
     (sparse_attn_tail).
@@ -47,11 +47,12 @@ def kv_append(k_pages, v_pages, page_table, kv_lens, k_new, v_new):
 
 
 def kv_advance(kv_lens, add, n_accepted=None):
-    """kv_len + add (+ n_accepted[b]); after a round, add = -gamma."""
+    """max(0, kv_len + add (+ n_accepted[b])); after a round, add = -gamma.
+    A length never goes below zero."""
     lens = i64(kv_lens) + int(add)
     if n_accepted is not None:
         lens = lens + i64(n_accepted)
-    return lens
+    return np.maximum(lens, 0)
 
 
 def draft_positions(idx, sel_lens, tail_begin, kv_lens, b, g):

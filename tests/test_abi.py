@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 100
+    assert sd.version() == 200
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
@@ -191,3 +191,31 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(tail=None), sd.SD_ERR_INVALID_ARG),
+    (dict(max_tail=-1), sd.SD_ERR_INVALID_ARG),
+    (dict(max_tail=65), sd.SD_ERR_INVALID_ARG),   # > max_pages * page_size
+    (dict(ws_bytes=0), sd.SD_ERR_WORKSPACE),
+])
+def test_draft_tail_rejects_invalid_arguments(L, args, want):
+    kv = _kv()
+    a = dict(tail=FAKE, max_tail=16, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_draft_attn_sparse_tail(ctypes.byref(kv), FAKE, 2, 1, 8, FAKE, FAKE, 1, 64, a["tail"],
+                                     a["max_tail"], 1.0, FAKE, None, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+def test_append_and_advance_reject_invalid_arguments(L):
+    kv = _kv()
+    assert L.sd_kv_append(ctypes.byref(kv), None, FAKE, 2, 1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 0, 1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, -1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_append(ctypes.byref(_kv(v_pages=None)), FAKE, FAKE, 2, 1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, 0, None) == sd.SD_OK  # nothing to write
+    assert L.sd_kv_advance(None, None, 2, 1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_advance(FAKE, None, 0, 1, None) == sd.SD_ERR_INVALID_ARG

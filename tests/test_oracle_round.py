@@ -89,6 +89,7 @@ def test_verify_after_append_is_causal_attention_over_the_extended_sequence():
 def test_advance_hand_values():
     assert list(kv_advance([10, 5, 0], -4, [2, 0, 4])) == [8, 1, 0]
     assert list(kv_advance([7], 3)) == [10]
+    assert list(kv_advance([2, 3], -5, [1, 0])) == [0, 0]  # clamped at zero
     # a round: L tokens, append gamma + 1, accept n -> the first token plus n drafts kept
     L, gamma = 100, 4
     for n in range(gamma + 1):
