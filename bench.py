@@ -12,8 +12,11 @@ One step = one pass of every kernel of the hot path, in call order:
 `value` = draft+verify KV token reads per step / step time (selection counted
 as overhead). Per-call HIP event times, verify GB/s against the 8 TB/s HBM
 peak, and the CPU oracle's rate on a bounded sample are reported beside it.
+After that, `round` times one whole self-speculative round at the same shape
+(draft steps with KV append and sampling, verify, accept, roll back), eager and
+replayed from a HIP graph, and dense decode as the attention-only target step.
 
-python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
 """
 import argparse
@@ -44,6 +47,7 @@ def parse():
     ap.add_argument("--cpu-sample-units", type=int, default=0,
                     help="(sequence, kv head) units the oracle runs (0 = auto, ~15 s)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-round", action="store_true", help="skip the round measurement")
     return ap.parse_args()
 
 
@@ -224,6 +228,105 @@ def cpu_baseline(wl, n_units):
                       f"{wl.L} tokens + {wl.gamma} sparse drafts over {wl.w.budget} SnapKV tokens each"}
 
 
+def measure_round(wl, reps=10):
+    """One self-speculative round at the bench shape, timed eager and replayed
+    from a HIP graph. SnapKV selects once at L0 = L - (gamma + 1); the round is
+    gamma x [append the token's K/V, advance, draft over selection + tail,
+    sample the next draft token], then append, advance, verify (n_q = gamma + 1
+    over L), accept, roll back. The appended K/V are the rows the cache already
+    holds at L0 .. L - 1, so the cache is the same after every round. Also
+    times dense decode (n_q = 1 over L) as the attention-only target step T_T."""
+    import torch
+
+    sd, w = wl.sd, wl.w
+    B, g, Hq, Hkv, V = wl.B, wl.gamma, wl.Hq, wl.Hkv, wl.V
+    dev = wl.q.device
+    i32 = torch.int32
+    L0 = wl.L - (g + 1)
+    lens0 = torch.full((B,), L0, dtype=i32, device=dev)
+    kv_lens = lens0.clone()
+    kv = sd.KVCache(wl.kv_t.k_pages, wl.kv_t.v_pages, wl.kv_t.page_table, kv_lens)
+    sd.sd_snapkv_select(kv, wl.q_obs, w.window, Hq, w.pool_kernel, w.budget, L0, 1.0, wl.idx, wl.sel,
+                        wl.ws_snap)
+    tail_begin = lens0.clone()
+    pt = wl.kv_t.page_table.long()
+    rows = torch.arange(B, device=dev)
+    k_new, v_new = [], []
+    for i in range(g + 1):
+        pos = L0 + i
+        pages = pt[rows, pos // 16]
+        k_new.append(wl.kv_t.k_pages[pages, :, pos % 16, :].unsqueeze(1).contiguous())
+        v_new.append(wl.kv_t.v_pages[pages, :, pos % 16, :].unsqueeze(1).contiguous())
+    zd_i = [wl.zd[:, i:i + 1].contiguous() for i in range(g)]
+    u_i = [wl.ua[:, i:i + 1].contiguous() for i in range(g)]
+    drafted_t = torch.empty((g, B), dtype=i32, device=dev)  # row i: draft token i of every sequence
+    drafted = torch.empty((B, g), dtype=i32, device=dev)
+    n0 = torch.empty((B,), dtype=i32, device=dev)
+    ws_s = sd.workspace(sd.sd_spec_accept_workspace_size(B, 0, V), dev)
+
+    def one_round():
+        for i in range(g):
+            sd.sd_kv_append(kv, k_new[i], v_new[i], 1)
+            sd.sd_kv_advance(kv_lens, None, 1)
+            sd.sd_draft_attn_sparse_tail(kv, wl.q_draft[i], 1, Hq, wl.idx, wl.sel, Hkv, w.budget, tail_begin,
+                                         g + 1, 1.0, wl.o_draft[i], None, wl.ws_draft)
+            sd.sd_spec_accept(zd_i[i], None, None, None, u_i[i], 0, V, 1.0, n0, drafted_t[i], ws_s)
+        sd.sd_kv_append(kv, k_new[g], v_new[g], 1)
+        sd.sd_kv_advance(kv_lens, None, 1)
+        sd.sd_verify_attn(kv, wl.q, g + 1, Hq, wl.L, 1.0, wl.o, wl.lse, wl.ws_ver)
+        drafted.copy_(drafted_t.t())
+        sd.sd_spec_accept(wl.zt, wl.zd, drafted, wl.ua, wl.us, g, V, 1.0, wl.n_acc, wl.toks, wl.ws_acc)
+        sd.sd_kv_advance(kv_lens, wl.n_acc, -g)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            kv_lens.copy_(lens0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sum(ts) / len(ts)
+
+    one_round()
+    torch.cuda.synchronize()
+    eager_ms = timed(one_round)
+    graph = torch.cuda.CUDAGraph()
+    kv_lens.copy_(lens0)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            one_round()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay)
+    mean_acc = float(wl.n_acc.float().mean().item())
+
+    # attention-only step times over the full cache (lengths L)
+    q1 = wl.q[:, :1].contiguous()
+    o1 = torch.empty_like(q1)
+
+    def decode():
+        sd.sd_verify_attn(wl.kv, q1, 1, Hq, wl.L, 1.0, o1, None, wl.ws_ver)
+
+    def verify():
+        sd.sd_verify_attn(wl.kv, wl.q, g + 1, Hq, wl.L, 1.0, wl.o, wl.lse, wl.ws_ver)
+
+    def draft():
+        sd.sd_draft_attn_sparse(wl.kv, wl.q_draft[0], 1, Hq, wl.idx, wl.sel, Hkv, w.budget, 1.0, wl.o_draft[0],
+                                None, wl.ws_draft)
+
+    decode()
+    t_dec, t_ver, t_dr = timed(decode), timed(verify), timed(draft)
+    return {"L0": L0, "eager_ms": eager_ms, "graph_ms": graph_ms, "mean_accepted": mean_acc,
+            "decode_ms": t_dec, "verify_ms": t_ver, "draft_ms": t_dr,
+            "verify_over_decode": t_ver / t_dec, "draft_over_decode": t_dr / t_dec,
+            "budget_over_context": w.budget / wl.L}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -285,6 +388,12 @@ def main():
         cpu = cpu_baseline(wl, n_units)
         log(f"cpu baseline {cpu['value']:.3e} KV tokens/s in {cpu['seconds']} s")
 
+    rnd = None
+    if not args.no_round:
+        rnd = measure_round(wl)
+        log(f"round: eager {rnd['eager_ms']:.3f} ms, graph {rnd['graph_ms']:.3f} ms, "
+            f"verify/decode {rnd['verify_over_decode']:.3f}, draft/decode {rnd['draft_over_decode']:.3f}")
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -314,6 +423,7 @@ def main():
         "per_call_ms": avg,
         "mean_accepted": float(wl.n_acc.float().mean().item()),
         "cpu_baseline": cpu,
+        "round": rnd,
     }
     print(json.dumps(rec), flush=True)
 
