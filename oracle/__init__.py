@@ -21,7 +21,8 @@ Functions and what pins them (tests/test_oracle_*.py):
   selection.snapkv_votes   brute-force double loop, column sums of a library softmax
   selection.maxpool1d      brute force, hand fixture
   selection.topk_lowest_index  brute-force subset enumeration
-  selection.snapkv_select  brute-force subset search on tiny inputs, special cases
+  selection.snapkv_select  brute-force subset search on tiny inputs (one budget,
+                           and per-sequence budgets in a ragged batch), special cases
   accept.spec_accept       hand-worked fixtures, Monte Carlo distribution
                            preservation, closed-form acceptance probabilities
                            (with gamma = 0 it is the draft-token sampler)

@@ -91,9 +91,13 @@ def snapkv_select(q_obs, k_pages, page_table, kv_lens, window, pool_kernel, budg
                   units=None, return_pooled=False):
     """SnapKV selection per (sequence, KV head).
 
-    q_obs: [B, W, Hq, d] queries of the last W prompt tokens.
-    Returns idx int32 [B, Hkv, budget] (unused tail = -1), sel_lens int32 [B],
-    and with return_pooled=True a dict {(b, g): pooled votes} as well.
+    q_obs: [B, W, Hq, d] queries of the last W prompt tokens. budget: one KV
+    budget for every sequence, or one per sequence (the MagicDec notes, §4.3:
+    the best draft budget depends on the context length; with per-sequence
+    budgets each sequence is selected on its own budget).
+    Returns idx int32 [B, Hkv, max budget] (unused tail = -1), sel_lens int32
+    [B] = min(L, budget_b), and with return_pooled=True a dict
+    {(b, g): pooled votes} as well.
     """
     q = f64(q_obs)
     K = f64(k_pages)
@@ -103,22 +107,25 @@ def snapkv_select(q_obs, k_pages, page_table, kv_lens, window, pool_kernel, budg
     assert W == window
     Hkv = K.shape[1]
     G = Hq // Hkv
-    idx = np.full((B, Hkv, budget), -1, dtype=np.int32)
-    sel = np.array([min(int(L), budget) for L in lens], dtype=np.int32)
+    budgets = np.broadcast_to(np.asarray(budget, dtype=np.int64), (B,))
+    width = int(budgets.max())
+    idx = np.full((B, Hkv, width), -1, dtype=np.int32)
+    sel = np.array([min(int(L), int(K_b)) for L, K_b in zip(lens, budgets)], dtype=np.int32)
     pooled_out = {}
     todo = [(b, g) for b in range(B) for g in range(Hkv)] if units is None else list(units)
     for b, g in todo:
         L = int(lens[b])
-        if L <= budget:
+        K_b = int(budgets[b])
+        if L <= K_b:
             idx[b, g, :L] = np.arange(L)
             continue
         keys = token_rows(K, pt, b, np.arange(L), g)
         rows = q[b][:, g * G:(g + 1) * G, :]
         votes = snapkv_votes(rows, keys, scale, W)
         pooled = maxpool1d(votes, pool_kernel)
-        kept = topk_lowest_index(pooled, budget - W)
+        kept = topk_lowest_index(pooled, K_b - W)
         chosen = np.concatenate([kept, np.arange(L - W, L)])
-        idx[b, g, :] = np.sort(chosen)
+        idx[b, g, :K_b] = np.sort(chosen)
         pooled_out[(b, g)] = pooled
     if return_pooled:
         return idx, sel, pooled_out

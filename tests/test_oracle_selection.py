@@ -219,3 +219,35 @@ def test_snapkv_per_head_sets_differ_and_include_window():
         assert s == sorted(set(s)) and len(s) == budget
         assert s[-W:] == list(range(L - W, L))
     assert idx[0, 0].tolist() != idx[0, 1].tolist()
+
+
+def test_snapkv_per_sequence_budgets_brute_force():
+    """Per-sequence budgets (ragged batch): each sequence's set is the brute-force
+    optimum for its own budget, rows are padded with -1 to the largest budget,
+    and a sequence with L <= budget keeps everything."""
+    rng = np.random.default_rng(9)
+    W, G, d, pk, P = 2, 2, 4, 3, 16
+    lens, budgets = [12, 11, 7], [6, 5, 9]
+    dense = [rng.standard_normal((L, 1, d)) for L in lens]
+    q = rng.standard_normal((3, W, G, d))
+    # one pool holding the three sequences on consecutive pages
+    pools, tables, base = [], [], 0
+    for x in dense:
+        pool, pt = _pool_from_dense(x, P)
+        pools.append(pool)
+        tables.append(pt[0] + base)
+        base += pool.shape[0]
+    pool = np.concatenate(pools)
+    width = max(len(t) for t in tables)
+    pt = np.stack([np.pad(t, (0, width - len(t))) for t in tables])
+    idx, sel = oracle.snapkv_select(q, pool, pt, np.array(lens), W, pk, np.array(budgets), 1.0)
+    assert idx.shape == (3, 1, max(budgets))
+    assert sel.tolist() == [min(L, K) for L, K in zip(lens, budgets)]
+    for b in range(2):
+        L, K = lens[b], budgets[b]
+        votes = _votes_brute(q[b], dense[b][:, 0], 1.0, W)
+        pooled = np.array([max(votes[max(0, j - 1):j + 2]) for j in range(L - W)])
+        best = min((-sum(pooled[list(sub)]), sub) for sub in itertools.combinations(range(L - W), K - W))
+        want = sorted(list(best[1]) + list(range(L - W, L)))
+        assert idx[b, 0].tolist() == want + [-1] * (max(budgets) - K)
+    assert idx[2, 0].tolist() == list(range(7)) + [-1, -1]
