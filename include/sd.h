@@ -187,6 +187,22 @@ size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window, int32_t nu
                                        int32_t num_kv_heads, int32_t max_kv_len);
 
 /*
+ * SnapKV with one budget per sequence (MagicDec notes, §4.3: the best draft
+ * budget depends on batch size and context length, so a ragged batch may give
+ * each sequence its own): as sd_snapkv_select, with sequence b selected on
+ * budgets[b] (int32 [batch], device; values are clamped into
+ * [window + 1, max_budget]). idx: int32 [batch, num_kv_heads, max_budget], rows
+ * padded with -1 past min(L, budgets[b]); sel_lens[b] = min(L, budgets[b]).
+ * Workspace: sd_snapkv_select_workspace_size. Limits: as sd_snapkv_select with
+ * budget = max_budget.
+ */
+sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                                   int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                                   const int32_t *budgets, int32_t max_budget, int32_t max_kv_len,
+                                   float softmax_scale, int32_t *idx, int32_t *sel_lens,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Modified rejection sampling for one verification round ("Wann beschleunigt
  * spekulatives Decoding das LLM-Serving?", section on a verification round):
  * per sequence, with p_i = softmax(target_logits[b, i] / temperature) and

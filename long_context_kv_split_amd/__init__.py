@@ -27,6 +27,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_kv_append,
     sd_kv_cache,
     sd_snapkv_select,
+    sd_snapkv_select_budgets,
     sd_snapkv_select_workspace_size,
     sd_spec_accept,
     sd_spec_accept_workspace_size,

@@ -61,6 +61,7 @@ _SIGNATURES = {
     "sd_streaming_select": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "sd_snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_snapkv_select_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "sd_snapkv_select_budgets": (_I, [_KV, _P, _I, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_spec_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_spec_accept_workspace_size": (_S, [_I, _I, _I]),
     "sd_status_string": (ctypes.c_char_p, [_I]),
@@ -263,6 +264,20 @@ def sd_snapkv_select(kv, q_obs, window, num_q_heads, pool_kernel, budget, max_kv
     wp, wb = _ws(workspace, need)
     _check(lib().sd_snapkv_select(kv.ref, qp, B, window, num_q_heads, pool_kernel, budget, max_kv_len,
                                   softmax_scale, ip, sp, wp, wb, _stream(stream)), "sd_snapkv_select")
+
+
+def sd_snapkv_select_budgets(kv, q_obs, window, num_q_heads, pool_kernel, budgets, max_budget, max_kv_len,
+                             softmax_scale, idx, sel_lens, workspace=None, stream=None):
+    B, d = kv.batch, kv.head_dim
+    qp = _dev(q_obs, "q_obs", kv.dtype, B * window * num_q_heads * d)
+    bp = _dev(budgets, "budgets", torch.int32, B)
+    ip = _dev(idx, "idx", torch.int32, B * kv.num_kv_heads * max_budget)
+    sp = _dev(sel_lens, "sel_lens", torch.int32, B)
+    need = sd_snapkv_select_workspace_size(B, window, num_q_heads, kv.num_kv_heads, max_kv_len)
+    wp, wb = _ws(workspace, need)
+    _check(lib().sd_snapkv_select_budgets(kv.ref, qp, B, window, num_q_heads, pool_kernel, bp, max_budget,
+                                          max_kv_len, softmax_scale, ip, sp, wp, wb, _stream(stream)),
+           "sd_snapkv_select_budgets")
 
 
 def sd_spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, gamma, vocab,

@@ -74,7 +74,8 @@ struct SnapParams {
   int32_t W, Hq, Hkv, G, rows;
   int32_t num_pages, page_size, max_pages;
   int32_t len_cap, vote_stride;
-  int32_t pool_kernel, budget;
+  int32_t pool_kernel, budget;  // budget: the largest budget and the width of an idx row
+  const int32_t *budgets;       // [B] per-sequence budgets, or null (every sequence uses `budget`)
   float scale_log2;
 };
 
@@ -116,11 +117,17 @@ __device__ __forceinline__ float lds_read_f32(const char *lds, int byte_off) {
   return v;
 }
 
+// Budget of sequence b (device-side per-sequence values are clamped into
+// [W + 1, budget]).
+__device__ __forceinline__ int seq_budget(const SnapParams &a, int b) {
+  return a.budgets ? clampi(a.budgets[b], a.W + 1, a.budget) : a.budget;
+}
+
 // Keys scored for sequence b: every cached key when the sequence is longer
-// than the budget (shorter ones keep everything and are not scored).
+// than its budget (shorter ones keep everything and are not scored).
 __device__ __forceinline__ int snap_steps(const SnapParams &a, int b) {
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  return L > a.budget ? (L + kStepTokens - 1) / kStepTokens : 0;
+  return L > seq_budget(a, b) ? (L + kStepTokens - 1) / kStepTokens : 0;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void snap_plan_kernel(SnapParams a) {
@@ -572,13 +579,14 @@ __global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
   int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
-  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
-  if (L <= a.budget) {
+  const int budget = seq_budget(a, b);
+  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, budget);
+  if (L <= budget) {
     for (int t = tid; t < a.budget; t += THREADS) out[t] = t < L ? t : -1;
     return;
   }
   const int npre = L - a.W;  // <= THREADS * VPT and pool_kernel / 2 <= kMaxPoolHalf (host)
-  const uint32_t keep = (uint32_t)(a.budget - a.W);
+  const uint32_t keep = (uint32_t)(budget - a.W);
   const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
   const int half = a.pool_kernel / 2;
 
@@ -670,6 +678,7 @@ __global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
       out[gt_before + eq_before] = j;
   }
   for (int w = tid; w < a.W; w += THREADS) out[keep + w] = npre + w;
+  for (int t = budget + tid; t < a.budget; t += THREADS) out[t] = -1;  // row past this budget
 }
 
 // Long prefixes: pooled values in the workspace, 4-pass 8-bit radix select.
@@ -681,13 +690,14 @@ __global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapPara
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
   int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
-  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
-  if (L <= a.budget) {
+  const int budget = seq_budget(a, b);
+  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, budget);
+  if (L <= budget) {
     for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
     return;
   }
   const int npre = L - a.W;
-  const int keep = a.budget - a.W;
+  const int keep = budget - a.W;
   const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
   float *pooled = a.pooled + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
   const int half = a.pool_kernel / 2;
@@ -761,6 +771,7 @@ __global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapPara
     out_carry += take_total;
   }
   for (int w = tid; w < a.W; w += kTopkThreads) out[keep + w] = npre + w;
+  for (int t = budget + tid; t < a.budget; t += kTopkThreads) out[t] = -1;  // row past this budget
 }
 
 struct SnapLayout {
@@ -845,11 +856,12 @@ extern "C" size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window,
   return snap_layout(batch, num_kv_heads, rows, max_kv_len).bytes;
 }
 
-extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
-                                      int32_t window, int32_t num_q_heads, int32_t pool_kernel,
-                                      int32_t budget, int32_t max_kv_len, float softmax_scale,
-                                      int32_t *idx, int32_t *sel_lens, void *workspace,
-                                      size_t workspace_bytes, void *stream) {
+namespace {
+
+sd_status snapkv_impl(const sd_kv_cache *kv, const void *q_obs, int32_t batch, int32_t window,
+                      int32_t num_q_heads, int32_t pool_kernel, const int32_t *budgets, int32_t budget,
+                      int32_t max_kv_len, float softmax_scale, int32_t *idx, int32_t *sel_lens,
+                      void *workspace, size_t workspace_bytes, void *stream) {
   sd_status s = sdh::check_kv(kv, false);
   if (s != SD_OK) return s;
   SD_REQUIRE(q_obs != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
@@ -894,8 +906,31 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
   a.vote_stride = lay.vote_stride;
   a.pool_kernel = pool_kernel;
   a.budget = budget;
+  a.budgets = budgets;
   a.scale_log2 = softmax_scale * kLog2e;
   hipStream_t st = sdh::as_stream(stream);
   if (kv->head_dim == 128) return launch_snap<128>(a, batch, st);
   return launch_snap<64>(a, batch, st);
+}
+
+}  // namespace
+
+extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                                      int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                                      int32_t budget, int32_t max_kv_len, float softmax_scale,
+                                      int32_t *idx, int32_t *sel_lens, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  return snapkv_impl(kv, q_obs, batch, window, num_q_heads, pool_kernel, nullptr, budget, max_kv_len,
+                     softmax_scale, idx, sel_lens, workspace, workspace_bytes, stream);
+}
+
+extern "C" sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                                              int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                                              const int32_t *budgets, int32_t max_budget,
+                                              int32_t max_kv_len, float softmax_scale, int32_t *idx,
+                                              int32_t *sel_lens, void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+  SD_REQUIRE(budgets != nullptr, SD_ERR_INVALID_ARG);
+  return snapkv_impl(kv, q_obs, batch, window, num_q_heads, pool_kernel, budgets, max_budget, max_kv_len,
+                     softmax_scale, idx, sel_lens, workspace, workspace_bytes, stream);
 }

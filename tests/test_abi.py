@@ -219,3 +219,14 @@ def test_append_and_advance_reject_invalid_arguments(L):
     assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, 0, None) == sd.SD_OK  # nothing to write
     assert L.sd_kv_advance(None, None, 2, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_advance(FAKE, None, 0, 1, None) == sd.SD_ERR_INVALID_ARG
+
+
+@no_gpu
+def test_snapkv_budgets_rejects_missing_budgets(L):
+    kv = _kv()
+    st = L.sd_snapkv_select_budgets(ctypes.byref(kv), FAKE, 2, 8, 8, 7, None, 64, 64, 1.0, FAKE, FAKE, WS,
+                                    1 << 30, None)
+    assert st == sd.SD_ERR_INVALID_ARG
+    st = L.sd_snapkv_select_budgets(ctypes.byref(kv), FAKE, 2, 8, 8, 7, FAKE, 8, 64, 1.0, FAKE, FAKE, WS,
+                                    1 << 30, None)
+    assert st == sd.SD_ERR_INVALID_ARG  # max_budget <= window

@@ -189,3 +189,45 @@ def test_snapkv_max_len_above_lengths():
                                                     8, 7, 128, 1.0, return_pooled=True)
     near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, 8, 128)
     assert near <= 1
+
+
+@pytest.mark.parametrize("name,lens,budgets,Hq,Hkv,W", [
+    ("ragged-mixed", [3000, 700, 5000, 1200, 90], [256, 800, 1024, 300, 64], 8, 2, 16),
+    ("rows128-mixed", [4100, 2600], [512, 2000], 32, 1, 4),
+])
+def test_snapkv_per_sequence_budgets(name, lens, budgets, Hq, Hkv, W):
+    """A ragged batch with one budget per sequence (some sequences shorter than
+    their budget keep everything); then the sparse draft over the per-sequence
+    sets."""
+    from tests.gpu_helpers import compare_attn, run_draft
+
+    kv_t = paged_kv(91, lens, Hkv, 128, BF16, "cuda", shuffle=True, spike_frac=0.1)
+    q_obs = queries(91, 4, (len(lens), W, Hq, 128), BF16, "cuda", scale=128 ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    B, Kmax = len(lens), max(budgets)
+    bud = torch.tensor(budgets, dtype=torch.int32, device="cuda")
+    idx = torch.full((B, Hkv, Kmax), 7, dtype=torch.int32, device="cuda")
+    sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+    mk = max(lens)
+    ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, mk), "cuda")
+    sd.sd_snapkv_select_budgets(kv, q_obs, W, Hq, 7, bud, Kmax, mk, 1.0, idx, sel, ws)
+    torch.cuda.synchronize()
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens, W, 7,
+                                                    np.array(budgets), 1.0, return_pooled=True)
+    idx_np, sel_np = idx.cpu().numpy(), sel.cpu().numpy()
+    assert (sel_np == sel_ref).all()
+    near = 0
+    for b in range(B):
+        K_b = budgets[b]
+        assert (idx_np[b, :, min(lens[b], K_b):] == -1).all()
+        near += check_selection(idx_np[b:b + 1, :, :K_b], idx_ref[b:b + 1, :, :K_b], sel_np[b:b + 1],
+                                sel_ref[b:b + 1], {(0, g): pooled[(b, g)] for g in range(Hkv) if (b, g) in pooled},
+                                W, K_b)
+    say(f"  {name}: near-tie units {near}")
+    assert near <= 1
+    q = queries(91, 1, (B, 1, Hq, 128), BF16, "cuda", scale=128 ** -0.5)
+    out, lse = run_draft(kv_t, q, 1, Hq, idx, sel)
+    if near == 0:
+        o_ref, l_ref = oracle.sparse_attn(q.cpu(), kv_t.k_pages.cpu(), kv_t.v_pages.cpu(), kv_t.page_table.cpu(),
+                                          idx_ref, sel_ref, 1.0)
+        compare_attn(out, lse, o_ref, l_ref, BF16)
