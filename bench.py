@@ -14,7 +14,9 @@ as overhead). Per-call HIP event times, verify GB/s against the 8 TB/s HBM
 peak, and the CPU oracle's rate on a bounded sample are reported beside it.
 After that, `round` times one whole self-speculative round at the same shape
 (draft steps with KV append and sampling, verify, accept, roll back), eager and
-replayed from a HIP graph, and dense decode as the attention-only target step.
+replayed from a HIP graph, and dense decode as the attention-only target step;
+`per_sequence_budgets` times SnapKV with one budget per sequence and a draft
+step on the ragged B=256 batch.
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
@@ -47,7 +49,8 @@ def parse():
     ap.add_argument("--cpu-sample-units", type=int, default=0,
                     help="(sequence, kv head) units the oracle runs (0 = auto, ~15 s)")
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--no-round", action="store_true", help="skip the round measurement")
+    ap.add_argument("--no-round", action="store_true",
+                    help="skip the round and per-sequence-budget measurements")
     return ap.parse_args()
 
 
@@ -327,6 +330,59 @@ def measure_round(wl, reps=10):
             "budget_over_context": w.budget / wl.L}
 
 
+def measure_hetero(reps=5):
+    """SnapKV with per-sequence budgets on the ragged batch (B=256, contexts
+    4096..32768 on shuffled 16-token pages): budget_b = L_b / 16 rounded down
+    to 16 (256..2048, the headline's budget/context ratio), observation window
+    32, pool 7; then one draft step over the per-sequence sets."""
+    import torch
+
+    import long_context_kv_split_amd as sd
+    from synth import WORKLOADS, paged_kv, queries, workload_lens
+
+    w = WORKLOADS["ragged-b256-l4k-32k"]
+    B, Hq, Hkv, d, W = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, 32
+    lens = workload_lens(w)
+    kv_t = paged_kv(w.seed, lens, Hkv, d, torch.bfloat16, "cuda", shuffle=True, spike_frac=0.1)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    budgets = [max(256, min(2048, L // 16 // 16 * 16)) for L in lens]
+    Kmax, L = max(budgets), max(lens)
+    bud = torch.tensor(budgets, dtype=torch.int32, device="cuda")
+    q_obs = queries(w.seed, 4, (B, W, Hq, d), torch.bfloat16, "cuda", scale=d ** -0.5)
+    q = queries(w.seed, 1, (B, 1, Hq, d), torch.bfloat16, "cuda", scale=d ** -0.5)
+    idx = torch.empty((B, Hkv, Kmax), dtype=torch.int32, device="cuda")
+    sel = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws_s = sd.workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L))
+    ws_d = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, Kmax))
+
+    def select():
+        sd.sd_snapkv_select_budgets(kv, q_obs, W, Hq, 7, bud, Kmax, L, 1.0, idx, sel, ws_s)
+
+    def draft():
+        sd.sd_draft_attn_sparse(kv, q, 1, Hq, idx, sel, Hkv, Kmax, 1.0, out, None, ws_d)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_sel = timed(select)
+    t_dr = timed(draft)
+    k_bytes = sum(lens) * Hkv * d * 2          # K of every token, read by each scoring pass
+    d_bytes = sum(budgets) * KV_BYTES_PER_TOKEN
+    return {"workload": w.name, "budgets": "L_b/16 rounded down to 16, clamped to [256, 2048]",
+            "sum_context": sum(lens), "sum_budget": sum(budgets), "select_ms": t_sel,
+            "select_K_GBps": 2 * k_bytes / (t_sel * 1e-3) / 1e9, "draft_ms": t_dr,
+            "draft_GBps": d_bytes / (t_dr * 1e-3) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -394,6 +450,11 @@ def main():
         log(f"round: eager {rnd['eager_ms']:.3f} ms, graph {rnd['graph_ms']:.3f} ms, "
             f"verify/decode {rnd['verify_over_decode']:.3f}, draft/decode {rnd['draft_over_decode']:.3f}")
 
+    het = None
+    if not args.no_round:
+        het = measure_hetero()
+        log(f"per-sequence budgets: select {het['select_ms']:.3f} ms, draft {het['draft_ms']:.3f} ms")
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -424,6 +485,7 @@ def main():
         "mean_accepted": float(wl.n_acc.float().mean().item()),
         "cpu_baseline": cpu,
         "round": rnd,
+        "per_sequence_budgets": het,
     }
     print(json.dumps(rec), flush=True)
 
