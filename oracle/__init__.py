@@ -31,6 +31,11 @@ Functions and what pins them (tests/test_oracle_*.py):
   round.kv_advance         hand values, the round identity L + 1 + n
   round.sparse_attn_tail   SDPA over explicitly gathered rows; tail-only equals
                            dense decode
+  dynamic.topk_select      brute-force subset search on tiny inputs with integer
+                           scores (ties), hand-listed per-head sets
+  dynamic.topk_attn        budget >= L equals dense decode; the dropped-mass bound
+                           against library SDPA over the whole cache; library SDPA
+                           over each head's gathered rows
 No function here is "parity unpinned".
 """
 from oracle.attention import attend, sparse_attn, token_rows, verify_attn  # noqa: F401
@@ -43,4 +48,5 @@ from oracle.selection import (  # noqa: F401
 )
 from oracle.accept import softmax, spec_accept  # noqa: F401
 from oracle.round import draft_positions, kv_advance, kv_append, sparse_attn_tail  # noqa: F401
+from oracle.dynamic import topk_attn, topk_scores, topk_select  # noqa: F401
 from oracle.common import f64  # noqa: F401

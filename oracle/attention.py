@@ -103,9 +103,10 @@ def sparse_attn(q, k_pages, v_pages, page_table, idx, sel_lens, scale, units=Non
     """Draft attention over a selected subset of cached positions.
 
     idx: [B, idx_heads, max_sel] positions; idx_heads is 1 (one set shared by
-    all KV heads, e.g. StreamingLLM) or Hkv (one set per KV head, SnapKV).
-    Sequence b uses idx[b, g or 0, :sel_lens[b]]; every query row sees every
-    selected position. q: [B, n_q, Hq, d].
+    all KV heads, e.g. StreamingLLM), Hkv (one set per KV head, SnapKV) or Hq
+    (one set per query head, top-K attention; the same as Hkv when Hq = Hkv).
+    Sequence b uses idx[b, g or 0, :sel_lens[b]] (idx[b, h, ...] per query
+    head); every query row sees every selected position. q: [B, n_q, Hq, d].
     """
     q = f64(q)
     K = f64(k_pages)
@@ -119,14 +120,18 @@ def sparse_attn(q, k_pages, v_pages, page_table, idx, sel_lens, scale, units=Non
     idx_heads = idx.shape[1]
     o = np.zeros((B, n_q, Hq, d))
     lse = np.full((B, n_q, Hq), -np.inf)
+    per_query_head = idx_heads == Hq and G > 1
     for b, g in _units(B, Hkv, units):
-        gi = g if idx_heads > 1 else 0
-        pos = idx[b, gi, :int(sl[b])]
-        keys = token_rows(K, pt, b, pos, g)
-        vals = token_rows(V, pt, b, pos, g)
         heads = list(range(g * G, (g + 1) * G))
-        rows = q[b][:, heads, :].reshape(n_q * G, d)
-        ob, lb = attend(rows, keys, vals, scale)
-        o[b][:, heads, :] = ob.reshape(n_q, G, d)
-        lse[b][:, heads] = lb.reshape(n_q, G)
+        # one set for the group, or one per query head of it
+        groups = [[h] for h in heads] if per_query_head else [heads]
+        for hs in groups:
+            gi = hs[0] if per_query_head else (g if idx_heads > 1 else 0)
+            pos = idx[b, gi, :int(sl[b])]
+            keys = token_rows(K, pt, b, pos, g)
+            vals = token_rows(V, pt, b, pos, g)
+            rows = q[b][:, hs, :].reshape(n_q * len(hs), d)
+            ob, lb = attend(rows, keys, vals, scale)
+            o[b][:, hs, :] = ob.reshape(n_q, len(hs), d)
+            lse[b][:, hs] = lb.reshape(n_q, len(hs))
     return o, lse
