@@ -16,7 +16,8 @@ After that, `round` times one whole self-speculative round at the same shape
 (draft steps with KV append and sampling, verify, accept, roll back), eager and
 replayed from a HIP graph, and dense decode as the attention-only target step;
 `per_sequence_budgets` times SnapKV with one budget per sequence and a draft
-step on the ragged B=256 batch.
+step on the ragged B=256 batch; `dynamic_topk` times a top-K attention draft
+step (selection over the whole cache, then the per-head draft).
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
@@ -330,6 +331,50 @@ def measure_round(wl, reps=10):
             "budget_over_context": w.budget / wl.L}
 
 
+def measure_topk(wl, reps=10):
+    """Dynamic top-K attention draft step at the bench shape (MagicDec notes
+    §4.4): per query head, the budget positions with the largest q.k over the
+    whole cache (sd_topk_select), then the draft over those positions with one
+    index set per query head. The selection is paid again at every step."""
+    import torch
+
+    sd, w = wl.sd, wl.w
+    B, Hq, Hkv, d, K = wl.B, wl.Hq, wl.Hkv, wl.d, w.budget
+    dev = wl.q.device
+    idx = torch.empty((B, Hq, K), dtype=torch.int32, device=dev)
+    sel = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = sd.workspace(sd.sd_topk_select_workspace_size(B, Hq, Hkv, wl.L), dev)
+    q = wl.q_draft[0]
+    out = wl.o_draft[0]
+
+    def select():
+        sd.sd_topk_select(wl.kv, q, Hq, K, wl.L, idx, sel, ws)
+
+    def attn():
+        sd.sd_draft_attn_sparse(wl.kv, q, 1, Hq, idx, sel, Hq, K, 1.0, out, None, wl.ws_draft)
+
+    def step():
+        select()
+        attn()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_sel, t_att, t_step = timed(select), timed(attn), timed(step)
+    k_bytes = B * wl.L * Hkv * d * 2                 # every cached K row, read once
+    a_bytes = B * Hq * K * 2 * d * 2                 # K and V of each head's own set
+    return {"budget": K, "select_ms": t_sel, "attn_ms": t_att, "step_ms": t_step,
+            "select_K_GBps": k_bytes / (t_sel * 1e-3) / 1e9, "attn_GBps": a_bytes / (t_att * 1e-3) / 1e9}
+
+
 def measure_hetero(reps=5):
     """SnapKV with per-sequence budgets on the ragged batch (B=256, contexts
     4096..32768 on shuffled 16-token pages): budget_b = L_b / 16 rounded down
@@ -450,6 +495,15 @@ def main():
         log(f"round: eager {rnd['eager_ms']:.3f} ms, graph {rnd['graph_ms']:.3f} ms, "
             f"verify/decode {rnd['verify_over_decode']:.3f}, draft/decode {rnd['draft_over_decode']:.3f}")
 
+    topk = None
+    if not args.no_round:
+        topk = measure_topk(wl)
+        topk["step_over_static_draft"] = topk["step_ms"] / avg["draft_ms"]
+        if rnd is not None:
+            topk["step_over_decode"] = topk["step_ms"] / rnd["decode_ms"]
+        log(f"top-K draft step: select {topk['select_ms']:.3f} ms + attention {topk['attn_ms']:.3f} ms "
+            f"= {topk['step_ms']:.3f} ms ({topk['step_over_static_draft']:.1f}x the SnapKV draft step)")
+
     het = None
     if not args.no_round:
         het = measure_hetero()
@@ -486,6 +540,7 @@ def main():
         "cpu_baseline": cpu,
         "round": rnd,
         "per_sequence_budgets": het,
+        "dynamic_topk": topk,
     }
     print(json.dumps(rec), flush=True)
 

@@ -109,9 +109,11 @@ size_t sd_verify_attn_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_h
  * context).
  *
  * idx: int32 [batch, idx_heads, max_sel] cached positions; idx_heads is 1 (one
- *   set for all KV heads, as StreamingLLM selects) or num_kv_heads (one set per
- *   KV head, as SnapKV selects). Sequence b, KV head g uses the first
- *   sel_lens[b] entries of idx[b, idx_heads > 1 ? g : 0, :].
+ *   set for all KV heads, as StreamingLLM selects), num_kv_heads (one set per
+ *   KV head, as SnapKV selects) or num_q_heads (one set per query head, as
+ *   sd_topk_select selects). Sequence b, KV head g uses the first sel_lens[b]
+ *   entries of idx[b, idx_heads > 1 ? g : 0, :]; with one set per query head
+ *   (and num_q_heads > num_kv_heads), query head h uses idx[b, h, :].
  * Every query row attends to every selected position (q: [batch, n_q,
  *   num_q_heads, head_dim], normally n_q = 1). out/lse as for verify.
  * Limits: (num_q_heads / num_kv_heads) * n_q <= 64; batch * ceil(max_sel / 16)
@@ -201,6 +203,35 @@ sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void *q_obs, int
                                    const int32_t *budgets, int32_t max_budget, int32_t max_kv_len,
                                    float softmax_scale, int32_t *idx, int32_t *sel_lens,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Top-K attention selection for one draft step (MagicDec notes, §4.4: dynamic
+ * selection searches the cache again for every query; exact top-K attention
+ * keeps acceptance high at a small budget but pays its search at every draft
+ * step, and §4.1 counts that search in the draft cost).
+ *
+ * q: [batch, 1, num_q_heads, head_dim] bf16, the draft query. For sequence b
+ *   and query head h, s_j = <q_h, k_j> over the kv_lens[b] cached keys of KV
+ *   head h / (num_q_heads / num_kv_heads); the `budget` positions with the
+ *   largest s_j are kept, ties to the lower position, ascending (a positive
+ *   softmax scale does not change the order, so none is taken). A sequence
+ *   not longer than the budget keeps every position.
+ * idx: int32 [batch, num_q_heads, budget]: the kept positions, then -1.
+ * sel_lens: int32 [batch] = min(kv_len, budget). Feed both to
+ *   sd_draft_attn_sparse with idx_heads = num_q_heads.
+ * Scores are fp32 sums of exact bf16 products; where two scores lie within
+ *   fp32 rounding of each other at the cut, either may be kept.
+ * Limits: bf16 caches; num_q_heads / num_kv_heads <= 16; batch *
+ *   ceil(max_kv_len / 16) < 2^31 (else SD_ERR_UNSUPPORTED). max_kv_len bounds
+ *   kv_lens as for verify. Workspace: sd_topk_select_workspace_size (it holds
+ *   batch * num_q_heads * max_kv_len 32-bit score keys).
+ */
+sd_status sd_topk_select(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t num_q_heads,
+                         int32_t budget, int32_t max_kv_len, int32_t *idx, int32_t *sel_lens,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+size_t sd_topk_select_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t max_kv_len);
 
 /*
  * Modified rejection sampling for one verification round ("Wann beschleunigt

@@ -3,10 +3,12 @@
 The computation lives in libsdkv.so, a HIP library with the C ABI of
 include/sd.h: verify attention over a paged bf16 KV cache (split-KV MFMA
 kernel plus combine), sparse draft attention over gathered positions,
-StreamingLLM and SnapKV draft-KV selection, modified-rejection speculative
-acceptance, and the round's cache bookkeeping (KV append, length advance, draft
-over the selection plus the appended tail). This package is its ctypes binding (argument marshalling only) and
-its build script; importing it never computes anything on the CPU.
+StreamingLLM and SnapKV draft-KV selection (one budget, or one per sequence),
+per-step top-K attention selection, modified-rejection speculative acceptance,
+and the round's cache bookkeeping (KV append, length advance, draft over the
+selection plus the appended tail). This package is its ctypes binding
+(argument marshalling only) and its build script; importing it never computes
+anything on the CPU.
 """
 from long_context_kv_split_amd.binding import (  # noqa: F401
     KVCache,
@@ -32,6 +34,8 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_spec_accept,
     sd_spec_accept_workspace_size,
     sd_streaming_select,
+    sd_topk_select,
+    sd_topk_select_workspace_size,
     sd_verify_attn,
     sd_verify_attn_workspace_size,
     status_string,

@@ -62,6 +62,8 @@ _SIGNATURES = {
     "sd_snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_snapkv_select_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "sd_snapkv_select_budgets": (_I, [_KV, _P, _I, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "sd_topk_select": (_I, [_KV, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P]),
+    "sd_topk_select_workspace_size": (_S, [_I, _I, _I, _I]),
     "sd_spec_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_spec_accept_workspace_size": (_S, [_I, _I, _I]),
     "sd_status_string": (ctypes.c_char_p, [_I]),
@@ -165,6 +167,10 @@ def sd_verify_attn_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_di
 def sd_draft_attn_sparse_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_sel):
     return int(lib().sd_draft_attn_sparse_workspace_size(batch, n_q, num_q_heads, num_kv_heads,
                                                          head_dim, max_sel))
+
+
+def sd_topk_select_workspace_size(batch, num_q_heads, num_kv_heads, max_kv_len):
+    return int(lib().sd_topk_select_workspace_size(batch, num_q_heads, num_kv_heads, max_kv_len))
 
 
 def sd_snapkv_select_workspace_size(batch, window, num_q_heads, num_kv_heads, max_kv_len):
@@ -278,6 +284,17 @@ def sd_snapkv_select_budgets(kv, q_obs, window, num_q_heads, pool_kernel, budget
     _check(lib().sd_snapkv_select_budgets(kv.ref, qp, B, window, num_q_heads, pool_kernel, bp, max_budget,
                                           max_kv_len, softmax_scale, ip, sp, wp, wb, _stream(stream)),
            "sd_snapkv_select_budgets")
+
+
+def sd_topk_select(kv, q, num_q_heads, budget, max_kv_len, idx, sel_lens, workspace=None, stream=None):
+    B, d = kv.batch, kv.head_dim
+    qp = _dev(q, "q", kv.dtype, B * num_q_heads * d)
+    ip = _dev(idx, "idx", torch.int32, B * num_q_heads * budget)
+    sp = _dev(sel_lens, "sel_lens", torch.int32, B)
+    need = sd_topk_select_workspace_size(B, num_q_heads, kv.num_kv_heads, max_kv_len)
+    wp, wb = _ws(workspace, need)
+    _check(lib().sd_topk_select(kv.ref, qp, B, num_q_heads, budget, max_kv_len, ip, sp, wp, wb, _stream(stream)),
+           "sd_topk_select")
 
 
 def sd_spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, gamma, vocab,

@@ -26,6 +26,10 @@
 // d-tile dt from element dt of those four rows (v_perm), which assigns
 // head-dim index DPL*m + dt to MFMA row m. float32 caches use the same
 // structure with 16x16x4 f32 MFMA.
+//
+// A draft with one index set per query head (top-K attention, §4.4 of the
+// notes) cannot share K/V loads across the group, so its units are (sequence,
+// query head) with one query row each (G = 1), reading pool head h / G.
 #include "sd_device.h"
 #include "sd_host.h"
 #include "sd_sched.h"
@@ -49,7 +53,11 @@ struct AttnParams {
   Sched sc;             // persistent schedule tables (written by the plan kernel)
   float *part_o;        // [slots, rows, D]
   float *part_ml;       // [slots, rows, 2]
+  // Units are (sequence, head) pairs: the KV heads (Hkv = pool heads, G query
+  // heads each), or, for a draft with one index set per query head, the query
+  // heads (Hkv = Hq, G = 1) reading pool head h / unit_div.
   int32_t B, n_q, Hq, Hkv, G, rows;
+  int32_t pool_heads, unit_div;
   int32_t num_pages, page_size, max_pages;
   int32_t idx_heads, max_sel;
   int32_t len_cap;  // upper clamp of lens
@@ -107,10 +115,10 @@ __device__ __forceinline__ void load_dwords(uint32_t (&dst)[N], const char *p) {
   }
 }
 
-// Row id (page*Hkv + kvh)*P + slot of cached token `t` of the chunk's token
-// list: position t (verify) or idx_row[t] (draft), through the page table.
+// Row id (page*pool_heads + pkvh)*P + slot of cached token `t` of the chunk's
+// token list: position t (verify) or idx_row[t] (draft), through the page table.
 template <bool SPARSE>
-__device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, int t, int len, int sel,
+__device__ __forceinline__ int token_row(const AttnParams &a, int b, int pkvh, int t, int len, int sel,
                                          const int32_t *idx_row) {
   int pos;
   if constexpr (SPARSE) {
@@ -123,7 +131,7 @@ __device__ __forceinline__ int token_row(const AttnParams &a, int b, int kvh, in
   }
   int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
   page = clampi(page, 0, a.num_pages - 1);
-  return (page * a.Hkv + kvh) * a.page_size + pos % a.page_size;
+  return (page * a.pool_heads + pkvh) * a.page_size + pos % a.page_size;
 }
 
 // Issue the K and V loads of one 16-token step whose row ids sit in LDS at
@@ -291,6 +299,7 @@ void attn_split_kernel(AttnParams a) {
   sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     const int len = attn_len(a, b);
     const int sel = clampi(a.lens[b], 0, a.len_cap);  // draft: entries of idx read before the tail
+    const int pkvh = kvh / a.unit_div;                // pool head of the unit
     const int32_t *idx_row = nullptr;
     if constexpr (SPARSE)
       idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
@@ -334,7 +343,7 @@ void attn_split_kernel(AttnParams a) {
       const int n_tok = (sc_end - sc_begin) * kStepTokens;
       __syncthreads();  // the previous sub-chunk's table reads are done
       for (int tt = lane; tt < n_tok; tt += 64)
-        rows_lds[tt] = token_row<SPARSE>(a, b, kvh, sc_begin * kStepTokens + tt, len, sel, idx_row);
+        rows_lds[tt] = token_row<SPARSE>(a, b, pkvh, sc_begin * kStepTokens + tt, len, sel, idx_row);
       __syncthreads();
       // Main loop: groups of NBUF steps that need no mask, with a ring of NBUF
       // step buffers unrolled so every buffer has a fixed role and the loop
@@ -497,22 +506,27 @@ sd_status common_checks(const sd_kv_cache *kv, const void *q, int32_t batch, int
   return SD_OK;
 }
 
+// per_query_head: one unit per (sequence, query head) instead of per KV head.
 void fill_common(AttnParams &a, const sd_kv_cache *kv, const void *q, int32_t batch, int32_t n_q,
-                 int32_t num_q_heads, float softmax_scale, void *workspace, const WsLayout &l) {
+                 int32_t num_q_heads, float softmax_scale, void *workspace, const WsLayout &l,
+                 bool per_query_head) {
   char *ws = reinterpret_cast<char *>(workspace);
+  const int G = num_q_heads / kv->num_kv_heads;
   a.k_pages = kv->k_pages;
   a.v_pages = kv->v_pages;
   a.page_table = kv->page_table;
   a.q = q;
-  sdh::sched_bind(a.sc, ws, batch, kv->num_kv_heads);
-  a.part_ml = reinterpret_cast<float *>(ws + l.ml_off);
-  a.part_o = reinterpret_cast<float *>(ws + l.o_off);
   a.B = batch;
   a.n_q = n_q;
   a.Hq = num_q_heads;
-  a.Hkv = kv->num_kv_heads;
-  a.G = num_q_heads / kv->num_kv_heads;
+  a.Hkv = per_query_head ? num_q_heads : kv->num_kv_heads;
+  a.G = per_query_head ? 1 : G;
   a.rows = a.G * n_q;
+  a.pool_heads = kv->num_kv_heads;
+  a.unit_div = per_query_head ? G : 1;
+  sdh::sched_bind(a.sc, ws, batch, a.Hkv);
+  a.part_ml = reinterpret_cast<float *>(ws + l.ml_off);
+  a.part_o = reinterpret_cast<float *>(ws + l.o_off);
   a.num_pages = kv->num_pages;
   a.page_size = kv->page_size;
   a.max_pages = kv->max_pages;
@@ -543,7 +557,7 @@ extern "C" sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_
   const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
-  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l);
+  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l, false);
   a.lens = kv->kv_lens;
   a.idx = nullptr;
   a.idx_heads = 1;
@@ -555,7 +569,10 @@ extern "C" sd_status sd_verify_attn(const sd_kv_cache *kv, const void *q, int32_
 extern "C" size_t sd_draft_attn_sparse_workspace_size(int32_t batch, int32_t n_q,
                                                       int32_t num_q_heads, int32_t num_kv_heads,
                                                       int32_t head_dim, int32_t max_sel) {
-  return sd_verify_attn_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_sel);
+  // enough for units per KV head and, with idx_heads = num_q_heads, per query head
+  const size_t per_kv = sd_verify_attn_workspace_size(batch, n_q, num_q_heads, num_kv_heads, head_dim, max_sel);
+  if (per_kv == 0) return 0;
+  return std::max(per_kv, ws_layout(batch, num_q_heads, n_q, head_dim).bytes);
 }
 
 namespace {
@@ -567,15 +584,20 @@ sd_status draft_impl(const sd_kv_cache *kv, const void *q, int32_t batch, int32_
   sd_status s = common_checks(kv, q, batch, n_q, num_q_heads, softmax_scale, out);
   if (s != SD_OK) return s;
   SD_REQUIRE(idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(idx_heads == 1 || idx_heads == kv->num_kv_heads, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(idx_heads == 1 || idx_heads == kv->num_kv_heads || idx_heads == num_q_heads, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_sel > 0 && max_tail >= 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)max_tail <= (int64_t)kv->max_pages * kv->page_size, SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)batch * sdh::ceil_div((int64_t)max_sel + max_tail, 16) < ((int64_t)1 << 31),
              SD_ERR_UNSUPPORTED);
-  const WsLayout l = ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
+  // one index set per query head (top-K attention): units per query head
+  const bool per_query_head = idx_heads == num_q_heads && num_q_heads != kv->num_kv_heads;
+  SD_REQUIRE((int64_t)batch * num_q_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
+  const WsLayout l = per_query_head
+                         ? ws_layout(batch, num_q_heads, n_q, kv->head_dim)
+                         : ws_layout(batch, kv->num_kv_heads, num_q_heads / kv->num_kv_heads * n_q, kv->head_dim);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= l.bytes, SD_ERR_WORKSPACE);
   AttnParams a{};
-  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l);
+  fill_common(a, kv, q, batch, n_q, num_q_heads, softmax_scale, workspace, l, per_query_head);
   a.lens = sel_lens;
   a.idx = idx;
   a.idx_heads = idx_heads;

@@ -23,6 +23,13 @@
 //      Prefixes longer than 64 Ki keys and pool kernels wider than 129 use a
 //      variant that keeps the pooled values in the workspace and selects with
 //      a 4-pass 8-bit radix.
+//
+// Top-K attention (the dynamic draft of §4.4: per query head, the budget
+// positions with the largest q.k, searched again at every draft step) reuses
+// the pieces: topk_scores streams K like the SnapKV passes and writes every
+// score as an order-preserving 32-bit key (S^T = K Q^T, one 16-byte store per
+// head and step), and topk_rows selects per (sequence, query head) with the
+// same bit-by-bit threshold search, from bit 31.
 #include "sd_device.h"
 #include "sd_host.h"
 #include "sd_sched.h"
@@ -77,6 +84,8 @@ struct SnapParams {
   int32_t pool_kernel, budget;  // budget: the largest budget and the width of an idx row
   const int32_t *budgets;       // [B] per-sequence budgets, or null (every sequence uses `budget`)
   float scale_log2;
+  uint32_t *keys;      // top-K attention: [B*Hq, key_stride] order keys of q.k
+  int32_t key_stride;  // a multiple of 16
 };
 
 constexpr int kRing = 4;       // 16-key K steps per wave in LDS: 3 loading while one is scored
@@ -567,15 +576,81 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
 // the compares, not the barriers, dominate). The output slot of a kept position is (#keys > T before it) +
 // min(#keys == T before it, need), need = keep - #keys > T: every key above T
 // and the lowest-position ties.
+// Shared memory of the register top-K.
+template <int THREADS, int VPT>
+struct TopkLds {
+  static constexpr int kWaves = THREADS / 64;
+  static_assert(VPT * kWaves <= THREADS, "one scan entry per thread");
+  uint32_t cnt[2][kWaves];
+  uint64_t pre[VPT * kWaves];
+  uint64_t scan_waves[kWaves];
+};
+
+// Writes out[0, keep) = the positions j < n with the `keep` largest keys, ties
+// to the lower position, ascending; 0 < keep <= n. key[i] is the key of
+// position threadIdx.x + THREADS * i and 0 past n (a zero is never counted
+// above a candidate, which has a bit set); bits above TOP_BIT are clear. The keep-th largest key T is found bit by bit from the
+// top (each bit one ballot count over the block); then every key above T and
+// the lowest-positioned keys equal to T are written in position order from one
+// block scan of per-wave counts.
+template <int THREADS, int VPT, int TOP_BIT>
+__device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int n, uint32_t keep, int32_t *out,
+                                                TopkLds<THREADS, VPT> &sm) {
+  constexpr int kWaves = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t T = 0;
+  for (int bit = TOP_BIT; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) c += key[i] >= cand ? 1u : 0u;
+    c = wave_sum_u32(c);
+    if (lane == 0) sm.cnt[bit & 1][wave] = c;
+    __syncthreads();  // a buffer is rewritten two bits later, after the next barrier
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += sm.cnt[bit & 1][w];
+    if (total >= keep) T = cand;
+  }
+
+  // Per (i, wave): keys above T (low word) and equal to T (high word).
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const bool valid = tid + THREADS * i < n;
+    const uint64_t gm = __ballot(key[i] > T);  // a zero past n is never above T
+    const uint64_t em = __ballot(valid && key[i] == T);
+    if (lane == 0) sm.pre[i * kWaves + wave] = (uint64_t)__popcll(gm) | ((uint64_t)__popcll(em) << 32);
+  }
+  __syncthreads();
+  const uint64_t mine = tid < VPT * kWaves ? sm.pre[tid] : 0ull;
+  const uint64_t ex = block_exclusive_scan_u64<kWaves>(mine, sm.scan_waves);
+  if (tid == THREADS - 1) sm.scan_waves[0] = ex + mine;  // totals
+  if (tid < VPT * kWaves) sm.pre[tid] = ex;
+  __syncthreads();
+  const uint32_t need = keep - (uint32_t)sm.scan_waves[0];
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int j = tid + THREADS * i;
+    const bool valid = j < n;
+    const bool gt = key[i] > T, eq = valid && key[i] == T;
+    const uint64_t gm = __ballot(gt);
+    const uint64_t em = __ballot(eq);
+    const uint64_t p = sm.pre[i * kWaves + wave];
+    const uint32_t gt_before = (uint32_t)p + (uint32_t)__popcll(gm & below);
+    const uint32_t eq_before = (uint32_t)(p >> 32) + (uint32_t)__popcll(em & below);
+    if (gt)
+      out[gt_before + min(eq_before, need)] = j;
+    else if (eq && eq_before < need)
+      out[gt_before + eq_before] = j;
+  }
+}
+
 template <int THREADS, int VPT>
 __global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
-  constexpr int kWaves = THREADS / 64;
-  static_assert(VPT * kWaves <= THREADS, "one scan entry per thread");
-  __shared__ uint32_t cnt[2][kWaves];
-  __shared__ uint64_t pre[VPT * kWaves];
-  __shared__ uint64_t scan_waves[kWaves];
+  __shared__ TopkLds<THREADS, VPT> sm;
   __shared__ float pool_lds[2][THREADS + 2 * kMaxPoolHalf];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
   int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
@@ -594,8 +669,7 @@ __global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
   // past the prefix: votes are >= 0, so zero padding equals clipping); tile i
   // sits in LDS at offset kMaxPoolHalf with `half` halo values on each side
   // (the left halo from the previous tile's buffer, the right one from
-  // key[i + 1]), and key[i] becomes the pooled value. 0 keys are never counted
-  // below (every candidate has a bit set).
+  // key[i + 1]), and key[i] becomes the pooled value.
   uint32_t key[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -631,95 +705,32 @@ __global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
   }
 
   // Votes are sums of exponentials (>= +0), so bit 31 is clear.
-  uint32_t T = 0;
-  for (int bit = 30; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) c += key[i] >= cand ? 1u : 0u;
-    c = wave_sum_u32(c);
-    if (lane == 0) cnt[bit & 1][wave] = c;
-    __syncthreads();  // a buffer is rewritten two bits later, after the next barrier
-    uint32_t total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) total += cnt[bit & 1][w];
-    if (total >= keep) T = cand;
-  }
-
-  // Per (i, wave): keys above T (low word) and equal to T (high word).
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const bool valid = tid + THREADS * i < npre;
-    const uint64_t gm = __ballot(key[i] > T);
-    const uint64_t em = __ballot(valid && key[i] == T);
-    if (lane == 0) pre[i * kWaves + wave] = (uint64_t)__popcll(gm) | ((uint64_t)__popcll(em) << 32);
-  }
-  __syncthreads();
-  const uint64_t mine = tid < VPT * kWaves ? pre[tid] : 0ull;
-  const uint64_t ex = block_exclusive_scan_u64<kWaves>(mine, scan_waves);
-  if (tid == THREADS - 1) scan_waves[0] = ex + mine;  // totals
-  if (tid < VPT * kWaves) pre[tid] = ex;
-  __syncthreads();
-  const uint32_t need = keep - (uint32_t)scan_waves[0];
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int j = tid + THREADS * i;
-    const bool valid = j < npre;
-    const bool gt = key[i] > T, eq = valid && key[i] == T;
-    const uint64_t gm = __ballot(gt);
-    const uint64_t em = __ballot(eq);
-    const uint64_t p = pre[i * kWaves + wave];
-    const uint32_t gt_before = (uint32_t)p + (uint32_t)__popcll(gm & below);
-    const uint32_t eq_before = (uint32_t)(p >> 32) + (uint32_t)__popcll(em & below);
-    if (gt)
-      out[gt_before + min(eq_before, need)] = j;
-    else if (eq && eq_before < need)
-      out[gt_before + eq_before] = j;
-  }
+  select_top_keys<THREADS, VPT, 30>(key, npre, keep, out, sm);
   for (int w = tid; w < a.W; w += THREADS) out[keep + w] = npre + w;
   for (int t = budget + tid; t < a.budget; t += THREADS) out[t] = -1;  // row past this budget
 }
 
 // Long prefixes: pooled values in the workspace, 4-pass 8-bit radix select.
-__global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapParams a) {
+// Writes out[0, keep) = the positions j < n with the `keep` largest keys,
+// ties to the lower position, ascending; 0 < keep <= n; key(j) reads the key
+// of position j from global memory. A 4-pass 8-bit radix select over an LDS
+// histogram finds the keep-th largest key; an order-preserving compaction
+// (two block scans per 1024 positions) writes every key above it and the
+// lowest-positioned ties. One block of kTopkThreads threads.
+template <class KeyFn>
+__device__ __forceinline__ void select_top_keys_global(KeyFn key, int n, int keep, int32_t *out) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t scan_tmp[40];
   __shared__ uint32_t sel_digit, sel_above;
   const int tid = threadIdx.x;
-  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
-  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
-  const int budget = seq_budget(a, b);
-  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, budget);
-  if (L <= budget) {
-    for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
-    return;
-  }
-  const int npre = L - a.W;
-  const int keep = budget - a.W;
-  const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
-  float *pooled = a.pooled + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
-  const int half = a.pool_kernel / 2;
-
-  for (int j = tid; j < npre; j += kTopkThreads) {
-    const int lo = max(0, j - half), hi = min(npre - 1, j + half);
-    float v = votes[lo];
-    for (int t = lo + 1; t <= hi; ++t) v = fmaxf(v, votes[t]);
-    pooled[j] = v;
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  // Radix select of the keep-th largest key (bit pattern of a non-negative float).
   uint32_t prefix = 0, mask = 0;
   uint32_t k_rem = (uint32_t)keep;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < npre; j += kTopkThreads) {
-      const uint32_t key = __float_as_uint(pooled[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int j = tid; j < n; j += kTopkThreads) {
+      const uint32_t k = key(j);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -750,17 +761,16 @@ __global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapPara
     k_rem -= sel_above;
     __syncthreads();
   }
-  const uint32_t thr = prefix;  // key of the keep-th largest value
+  const uint32_t thr = prefix;  // the keep-th largest key
   const uint32_t need_eq = k_rem;  // how many keys equal to thr are taken
 
-  // Order-preserving compaction: every key > thr, and the first need_eq keys == thr.
   uint32_t eq_carry = 0, out_carry = 0;
-  for (int base = 0; base < npre; base += kTopkThreads) {
+  for (int base = 0; base < n; base += kTopkThreads) {
     const int j = base + tid;
-    const uint32_t key = j < npre ? __float_as_uint(pooled[j]) : 0u;
-    const bool valid = j < npre;
-    const bool gt = valid && key > thr;
-    const bool eq = valid && key == thr;
+    const bool valid = j < n;
+    const uint32_t k = valid ? key(j) : 0u;
+    const bool gt = valid && k > thr;
+    const bool eq = valid && k == thr;
     uint32_t eq_total;
     const uint32_t eq_rank = block_exclusive_scan(eq ? 1u : 0u, scan_tmp, &eq_total) + eq_carry;
     const bool take = gt || (eq && eq_rank < need_eq);
@@ -770,8 +780,116 @@ __global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapPara
     eq_carry += eq_total;
     out_carry += take_total;
   }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void snap_topk_global_kernel(SnapParams a) {
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  int32_t *out = a.idx + ((size_t)b * a.Hkv + kvh) * a.budget;
+  const int budget = seq_budget(a, b);
+  if (kvh == 0 && tid == 0) a.sel_lens[b] = min(L, budget);
+  if (L <= budget) {
+    for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
+    return;
+  }
+  const int npre = L - a.W;
+  const int keep = budget - a.W;
+  const float *votes = a.votes + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  float *pooled = a.pooled + ((size_t)b * a.Hkv + kvh) * a.vote_stride;
+  const int half = a.pool_kernel / 2;
+
+  for (int j = tid; j < npre; j += kTopkThreads) {
+    const int lo = max(0, j - half), hi = min(npre - 1, j + half);
+    float v = votes[lo];
+    for (int t = lo + 1; t <= hi; ++t) v = fmaxf(v, votes[t]);
+    pooled[j] = v;
+  }
+  __threadfence_block();
+  __syncthreads();
+  // pooled votes are >= +0: their bit patterns order like the values
+  select_top_keys_global([&](int j) { return __float_as_uint(pooled[j]); }, npre, keep, out);
   for (int w = tid; w < a.W; w += kTopkThreads) out[keep + w] = npre + w;
   for (int t = budget + tid; t < a.budget; t += kTopkThreads) out[t] = -1;  // row past this budget
+}
+
+// ---------------------------------------------------------------- top-K attention
+// Order key of a score: a larger float gets a larger unsigned key; -0 and +0
+// share the key of +0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = u == 0x80000000u ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Scores <q_h, k_j> of the G query heads of each KV head over the unit's keys
+// (sequences longer than the budget only), as order keys at
+// keys[(b*Hq + h)*key_stride + j]. Lane (g, r) holds keys 4g..4g+3 of the step
+// for head r. A store joins the in-order memory counter after the K loads of
+// three steps ahead, so the stream's wait also covers one load of the next
+// step: slightly stricter, never looser.
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void topk_scores_kernel(SnapParams a) {
+  __shared__ __attribute__((aligned(16))) char lds[KStream<D>::kLdsBytes];
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t) {
+    s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+    s_end = __builtin_amdgcn_readfirstlane(s_end);
+    u32x4 q[1][D / 32];
+    snap_load_q<D, 1>(a, b, kvh, q);  // rows = G (one query row per head)
+    uint32_t *krow = a.keys + ((size_t)b * a.Hq + (size_t)kvh * a.G + min(r, a.G - 1)) * a.key_stride + 4 * g;
+    KStream<D> ks(a, b, kvh, s_end - 1, lds);
+    ks.begin(s_begin);
+    for (int s = s_begin; s < s_end; ++s) {
+      ks.advance(s);
+      u32x4 k[D / 32];
+      ks.operand(s, k);
+      const f32x4 sc = snap_scores<D, 1>(k, q, 0);
+      if (r < a.G)
+        *reinterpret_cast<u32x4 *>(krow + (size_t)s * kStepTokens) =
+            u32x4{order_key(sc[0]), order_key(sc[1]), order_key(sc[2]), order_key(sc[3])};
+    }
+  });
+  KStream<D>::drain();
+}
+
+// One block per (sequence, query head): the budget largest keys of the row,
+// or every position when the sequence is not longer than the budget.
+template <int THREADS, int VPT>
+__global__ __launch_bounds__(THREADS) void topk_rows_kernel(SnapParams a) {
+  __shared__ TopkLds<THREADS, VPT> sm;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  int32_t *out = a.idx + ((size_t)b * a.Hq + h) * a.budget;
+  if (h == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
+  if (L <= a.budget) {
+    for (int t = tid; t < a.budget; t += THREADS) out[t] = t < L ? t : -1;
+    return;
+  }
+  const uint32_t *krow = a.keys + ((size_t)b * a.Hq + h) * a.key_stride;  // L <= THREADS * VPT (host)
+  uint32_t key[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int j = tid + THREADS * i;
+    key[i] = j < L ? krow[j] : 0u;
+  }
+  select_top_keys<THREADS, VPT, 31>(key, L, (uint32_t)a.budget, out, sm);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_global_kernel(SnapParams a) {
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  int32_t *out = a.idx + ((size_t)b * a.Hq + h) * a.budget;
+  if (h == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
+  if (L <= a.budget) {
+    for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
+    return;
+  }
+  const uint32_t *krow = a.keys + ((size_t)b * a.Hq + h) * a.key_stride;
+  select_top_keys_global([&](int j) { return krow[j]; }, L, a.budget, out);
 }
 
 struct SnapLayout {
@@ -933,4 +1051,101 @@ extern "C" sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void 
   SD_REQUIRE(budgets != nullptr, SD_ERR_INVALID_ARG);
   return snapkv_impl(kv, q_obs, batch, window, num_q_heads, pool_kernel, budgets, max_budget, max_kv_len,
                      softmax_scale, idx, sel_lens, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+struct TopkLayout {
+  size_t keys_off, bytes;
+  int key_stride;
+};
+
+TopkLayout topk_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len) {
+  TopkLayout l;
+  l.key_stride = (int)(sdh::ceil_div(std::max<int64_t>(1, max_len), 16) * 16);
+  l.keys_off = sdh::sched_table_bytes(B, Hkv);
+  l.bytes = l.keys_off + sdh::align_up((size_t)B * Hq * l.key_stride * 4);
+  return l;
+}
+
+template <int D>
+void launch_topk_attn_select(SnapParams &a, int B, hipStream_t st) {
+  static int cache = 0;  // resident waves of the scoring kernel, queried once
+  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(topk_scores_kernel<D>), 2 * kSimdsPerCU, &cache);
+  snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+  topk_scores_kernel<D><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  const unsigned blocks = (unsigned)(B * a.Hq);
+  constexpr int TH = kTopkThreads;
+  const int64_t n = a.len_cap;
+  if (n <= 8 * TH)
+    topk_rows_kernel<TH, 8><<<blocks, TH, 0, st>>>(a);
+  else if (n <= 16 * TH)
+    topk_rows_kernel<TH, 16><<<blocks, TH, 0, st>>>(a);
+  else if (n <= 32 * TH)
+    topk_rows_kernel<TH, 32><<<blocks, TH, 0, st>>>(a);
+  else if (n <= 64 * TH)
+    topk_rows_kernel<TH, 64><<<blocks, TH, 0, st>>>(a);
+  else
+    topk_rows_global_kernel<<<blocks, TH, 0, st>>>(a);
+}
+
+}  // namespace
+
+extern "C" size_t sd_topk_select_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t max_kv_len) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_kv_len < 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  return topk_layout(batch, num_q_heads, num_kv_heads, max_kv_len).bytes;
+}
+
+extern "C" sd_status sd_topk_select(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t num_q_heads,
+                                    int32_t budget, int32_t max_kv_len, int32_t *idx, int32_t *sel_lens,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  sd_status s = sdh::check_kv(kv, false);
+  if (s != SD_OK) return s;
+  SD_REQUIRE(q != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(batch > 0 && num_q_heads > 0 && budget > 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
+             SD_ERR_INVALID_ARG);
+  SD_REQUIRE(kv->dtype == SD_BF16, SD_ERR_UNSUPPORTED);
+  const int G = num_q_heads / kv->num_kv_heads;
+  SD_REQUIRE(G <= 16, SD_ERR_UNSUPPORTED);
+  SD_REQUIRE((int64_t)batch * kv->num_kv_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
+  SD_REQUIRE((int64_t)batch * num_q_heads < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
+  // the schedule keeps per-sequence step prefix sums in int32
+  SD_REQUIRE((int64_t)batch * sdh::ceil_div(max_kv_len, 16) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
+  const TopkLayout lay = topk_layout(batch, num_q_heads, kv->num_kv_heads, max_kv_len);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= lay.bytes, SD_ERR_WORKSPACE);
+
+  SnapParams a{};
+  a.k_pages = kv->k_pages;
+  a.page_table = kv->page_table;
+  a.kv_lens = kv->kv_lens;
+  a.q_obs = q;  // [B, 1, Hq, D]: one query row per head
+  char *ws = reinterpret_cast<char *>(workspace);
+  sdh::sched_bind(a.sc, ws, batch, kv->num_kv_heads);
+  a.keys = reinterpret_cast<uint32_t *>(ws + lay.keys_off);
+  a.key_stride = lay.key_stride;
+  a.idx = idx;
+  a.sel_lens = sel_lens;
+  a.W = 1;
+  a.Hq = num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = G;
+  a.rows = G;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages;
+  a.len_cap = max_kv_len;
+  a.budget = budget;  // scored only when L > budget (snap_steps)
+  a.budgets = nullptr;
+  a.pool_kernel = 1;
+  a.scale_log2 = 1.f;
+  hipStream_t st = sdh::as_stream(stream);
+  if (kv->head_dim == 128)
+    launch_topk_attn_select<128>(a, batch, st);
+  else
+    launch_topk_attn_select<64>(a, batch, st);
+  return sdh::launch_status();
 }

@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 200
+    assert sd.version() == 210
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
@@ -114,6 +114,7 @@ def test_verify_rejects_invalid_arguments(L, over, args, want):
 @pytest.mark.parametrize("args,want", [
     (dict(idx=None), sd.SD_ERR_INVALID_ARG),
     (dict(idx_heads=3), sd.SD_ERR_INVALID_ARG),
+    (dict(idx_heads=4), sd.SD_ERR_INVALID_ARG),       # neither 1, Hkv = 2 nor Hq = 8
     (dict(max_sel=0), sd.SD_ERR_INVALID_ARG),
     (dict(ws_bytes=0), sd.SD_ERR_WORKSPACE),
 ])
@@ -157,6 +158,37 @@ def test_snapkv_rejects_invalid_arguments(L, over, args, want):
     st = L.sd_snapkv_select(ctypes.byref(kv), FAKE, 2, a["window"], 8, a["pool"], a["budget"],
                             a["max_len"], 1.0, FAKE, FAKE, WS, a["ws_bytes"], None)
     assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("over,args,want", [
+    ({}, dict(q=None), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(idx=None), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(budget=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(hq=9), sd.SD_ERR_INVALID_ARG),          # Hq % Hkv != 0
+    ({}, dict(hq=34), sd.SD_ERR_UNSUPPORTED),         # G = 17 > 16
+    ({"dtype": binding.SD_F32}, {}, sd.SD_ERR_UNSUPPORTED),
+    ({}, dict(max_len=65), sd.SD_ERR_INVALID_ARG),    # > max_pages * page_size
+    ({}, dict(ws_bytes=64), sd.SD_ERR_WORKSPACE),
+    ({"max_pages": 4096}, dict(batch=1 << 20, max_len=1 << 16), sd.SD_ERR_UNSUPPORTED),
+])
+def test_topk_select_rejects_invalid_arguments(L, over, args, want):
+    kv = _kv(**over)
+    a = dict(q=FAKE, idx=FAKE, batch=2, hq=8, budget=16, max_len=64, ws_bytes=1 << 30)
+    a.update(args)
+    st = L.sd_topk_select(ctypes.byref(kv), a["q"], a["batch"], a["hq"], a["budget"], a["max_len"], a["idx"],
+                          FAKE, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+def test_topk_workspace_sizes():
+    t = sd.sd_topk_select_workspace_size(128, 32, 8, 32768)
+    assert t >= 128 * 32 * 32768 * 4 and t % 256 == 0   # one 32-bit key per (row, position)
+    assert sd.sd_topk_select_workspace_size(2, 9, 2, 100) == 0
+    assert sd.sd_topk_select_workspace_size(0, 8, 2, 100) == 0
+    # the draft workspace also covers one unit per query head
+    assert sd.sd_draft_attn_sparse_workspace_size(128, 1, 32, 8, 128, 2048) >= \
+        sd.sd_verify_attn_workspace_size(128, 1, 32, 32, 128, 2048)
 
 
 @no_gpu
