@@ -36,6 +36,8 @@ Functions and what pins them (tests/test_oracle_*.py):
   dynamic.topk_attn        budget >= L equals dense decode; the dropped-mass bound
                            against library SDPA over the whole cache; library SDPA
                            over each head's gathered rows
+  model.omega / speedup / best_gamma  Monte Carlo of the round process, the
+                           explicit sum over acceptance lengths, limits, hand values
 No function here is "parity unpinned".
 """
 from oracle.attention import attend, sparse_attn, token_rows, verify_attn  # noqa: F401
@@ -49,4 +51,5 @@ from oracle.selection import (  # noqa: F401
 from oracle.accept import softmax, spec_accept  # noqa: F401
 from oracle.round import draft_positions, kv_advance, kv_append, sparse_attn_tail  # noqa: F401
 from oracle.dynamic import topk_attn, topk_scores, topk_select  # noqa: F401
+from oracle.model import best_gamma, omega, round_time, speedup  # noqa: F401
 from oracle.common import f64  # noqa: F401
