@@ -17,7 +17,9 @@ After that, `round` times one whole self-speculative round at the same shape
 replayed from a HIP graph, and dense decode as the attention-only target step;
 `per_sequence_budgets` times SnapKV with one budget per sequence and a draft
 step on the ragged B=256 batch; `dynamic_topk` times a top-K attention draft
-step (selection over the whole cache, then the per-head draft).
+step (selection over the whole cache, then the per-head draft);
+`speedup_model` evaluates the analytic speedup model (best speculation length
+and attention-side speedup per draft kind and budget) on measured times.
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
@@ -375,6 +377,72 @@ def measure_topk(wl, reps=10):
             "select_K_GBps": k_bytes / (t_sel * 1e-3) / 1e9, "attn_GBps": a_bytes / (t_att * 1e-3) / 1e9}
 
 
+def measure_model(wl, rnd, topk, mean_accepted, reps=5, max_gamma=8, budgets=(256, 512, 1024, 2048, 4096)):
+    """The analytic speedup model (sd_best_gamma) evaluated on measured
+    attention times at the bench shape: T_T = dense decode (n_q = 1 over L),
+    T_V(g) = verify with n_q = g + 1, g = 1..max_gamma; SnapKV drafts at
+    several budgets K (T_D(K) one draft step, the selection made once at
+    prefill and not charged to rounds) and the top-K attention draft (its
+    search charged at every draft step). Attention only: the linear layers
+    are not part of the path, so these are attention-side speedups."""
+    import torch
+
+    sd, w = wl.sd, wl.w
+    B, Hq, Hkv, d, L = wl.B, wl.Hq, wl.Hkv, wl.d, wl.L
+    dev = wl.q.device
+    from synth import queries
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    q_all = queries(w.seed, 21, (B, max_gamma + 1, Hq, d), torch.bfloat16, dev, scale=d ** -0.5)
+    ws_v = sd.workspace(sd.sd_verify_attn_workspace_size(B, max_gamma + 1, Hq, Hkv, d, L), dev)
+    t_verify = []
+    for g in range(1, max_gamma + 1):
+        qg = q_all[:, :g + 1].contiguous()
+        og = torch.empty_like(qg)
+        t_verify.append(timed(lambda: sd.sd_verify_attn(wl.kv, qg, g + 1, Hq, L, 1.0, og, None, ws_v)))
+    t_target = rnd["decode_ms"]
+
+    # alpha of the synthetic logits, from the mean accepted count at gamma:
+    # E[n] = alpha + ... + alpha^gamma, increasing in alpha (bisection)
+    lo, hi = 0.0, 1.0
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if sd.sd_expected_tokens(wl.gamma, mid) - 1.0 < mean_accepted:
+            lo = mid
+        else:
+            hi = mid
+    alphas = {"synthetic": 0.5 * (lo + hi), "0.90": 0.9}
+
+    def best(t_draft, fixed, step):
+        return {k: dict(zip(("best_gamma", "speedup"), sd.sd_best_gamma(t_target, t_draft, t_verify, a, fixed, step)))
+                for k, a in alphas.items()}
+
+    rows = []
+    q1, o1 = wl.q_draft[0], wl.o_draft[0]
+    for K in budgets:
+        idx = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev)
+        sel = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws_d = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, K), dev)
+        t_sel = timed(lambda: sd.sd_snapkv_select(wl.kv, wl.q_obs, w.window, Hq, w.pool_kernel, K, L, 1.0, idx,
+                                                 sel, wl.ws_snap))
+        t_d = timed(lambda: sd.sd_draft_attn_sparse(wl.kv, q1, 1, Hq, idx, sel, Hkv, K, 1.0, o1, None, ws_d))
+        rows.append({"draft": "snapkv", "K": K, "T_D_ms": t_d, "T_select_once_ms": t_sel, **best(t_d, 0.0, 0.0)})
+    if topk is not None:
+        rows.append({"draft": "topk", "K": topk["budget"], "T_D_ms": topk["attn_ms"],
+                     "T_select_step_ms": topk["select_ms"], **best(topk["attn_ms"], 0.0, topk["select_ms"])})
+    return {"attention_only": True, "T_T_ms": t_target, "T_V_ms": t_verify, "alpha": alphas, "rows": rows}
+
+
 def measure_hetero(reps=5):
     """SnapKV with per-sequence budgets on the ragged batch (B=256, contexts
     4096..32768 on shuffled 16-token pages): budget_b = L_b / 16 rounded down
@@ -504,6 +572,14 @@ def main():
         log(f"top-K draft step: select {topk['select_ms']:.3f} ms + attention {topk['attn_ms']:.3f} ms "
             f"= {topk['step_ms']:.3f} ms ({topk['step_over_static_draft']:.1f}x the SnapKV draft step)")
 
+    model = None
+    if not args.no_round:
+        model = measure_model(wl, rnd, topk, float(wl.n_acc.float().mean().item()))
+        for r in model["rows"]:
+            log(f"model {r['draft']} K={r['K']}: T_D {r['T_D_ms']:.3f} ms, best gamma / speedup "
+                + ", ".join(f"alpha {k}: {v['best_gamma']} / {v['speedup']:.2f}" for k, v in r.items()
+                            if isinstance(v, dict)))
+
     het = None
     if not args.no_round:
         het = measure_hetero()
@@ -541,6 +617,7 @@ def main():
         "round": rnd,
         "per_sequence_budgets": het,
         "dynamic_topk": topk,
+        "speedup_model": model,
     }
     print(json.dumps(rec), flush=True)
 

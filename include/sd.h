@@ -295,6 +295,35 @@ sd_status sd_kv_append(const sd_kv_cache *kv, const void *k_new, const void *v_n
 sd_status sd_kv_advance(int32_t *kv_lens, const int32_t *n_accepted, int32_t batch, int32_t add,
                         void *stream);
 
+/*
+ * Analytic speedup model, host only (no GPU call; safe on any thread). The
+ * MagicDec summary (jarxiv.com) gives the speedup of speculative decoding as
+ * T_T * Omega(gamma, alpha) / (gamma * T_D + T_V(gamma)), where with a
+ * compressed draft cache gamma * T_D becomes T_select(K) + gamma * T_D(K)
+ * (MagicDec notes, §3.1 and §4.1). Times are in any one unit.
+ *
+ * sd_expected_tokens: Omega = sum_{i=0..gamma} alpha^i, the expected tokens
+ *   of one round for a constant per-token acceptance rate alpha in [0, 1];
+ *   NaN for gamma < 0 or alpha outside [0, 1].
+ * sd_speedup: t_target * Omega / (t_select_fixed + gamma * t_select_step +
+ *   gamma * t_draft + t_verify). t_select_fixed is the selection cost charged
+ *   to one round by a static selection (made once), t_select_step that of a
+ *   dynamic selection searched at every draft step. NaN for a negative or
+ *   non-finite time, t_target <= 0, or a round time of 0.
+ * sd_best_gamma: the gamma in 1..max_gamma with the lowest expected time per
+ *   token (round time / Omega; ties to the smaller gamma), t_verify[g - 1]
+ *   being T_V(g); writes it and its speedup. SD_ERR_INVALID_ARG for null
+ *   pointers, max_gamma < 1, or any argument sd_speedup rejects.
+ */
+double sd_expected_tokens(int32_t gamma, double alpha);
+
+double sd_speedup(double t_target, double t_draft, double t_verify, int32_t gamma, double alpha,
+                  double t_select_fixed, double t_select_step);
+
+sd_status sd_best_gamma(double t_target, double t_draft, const double *t_verify, int32_t max_gamma,
+                        double alpha, double t_select_fixed, double t_select_step, int32_t *gamma_out,
+                        double *speedup_out);
+
 /* Static string for a status code (never NULL). */
 const char *sd_status_string(sd_status status);
 

@@ -5,8 +5,9 @@ include/sd.h: verify attention over a paged bf16 KV cache (split-KV MFMA
 kernel plus combine), sparse draft attention over gathered positions,
 StreamingLLM and SnapKV draft-KV selection (one budget, or one per sequence),
 per-step top-K attention selection, modified-rejection speculative acceptance,
-and the round's cache bookkeeping (KV append, length advance, draft over the
-selection plus the appended tail). This package is its ctypes binding
+the round's cache bookkeeping (KV append, length advance, draft over the
+selection plus the appended tail), and the analytic speedup model (host
+arithmetic on measured step times). This package is its ctypes binding
 (argument marshalling only) and its build script; importing it never computes
 anything on the CPU.
 """
@@ -22,9 +23,11 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     SD_OK,
     SdError,
     lib,
+    sd_best_gamma,
     sd_draft_attn_sparse,
     sd_draft_attn_sparse_tail,
     sd_draft_attn_sparse_workspace_size,
+    sd_expected_tokens,
     sd_kv_advance,
     sd_kv_append,
     sd_kv_cache,
@@ -33,6 +36,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_snapkv_select_workspace_size,
     sd_spec_accept,
     sd_spec_accept_workspace_size,
+    sd_speedup,
     sd_streaming_select,
     sd_topk_select,
     sd_topk_select_workspace_size,

@@ -66,6 +66,10 @@ _SIGNATURES = {
     "sd_topk_select_workspace_size": (_S, [_I, _I, _I, _I]),
     "sd_spec_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_spec_accept_workspace_size": (_S, [_I, _I, _I]),
+    "sd_expected_tokens": (ctypes.c_double, [_I, ctypes.c_double]),
+    "sd_speedup": (ctypes.c_double, [ctypes.c_double] * 3 + [_I] + [ctypes.c_double] * 3),
+    "sd_best_gamma": (_I, [ctypes.c_double, ctypes.c_double, _P, _I, ctypes.c_double, ctypes.c_double,
+                           ctypes.c_double, _P, _P]),
     "sd_status_string": (ctypes.c_char_p, [_I]),
     "sd_version": (_I, []),
 }
@@ -93,6 +97,27 @@ def status_string(status):
 
 def version():
     return int(lib().sd_version())
+
+
+def sd_expected_tokens(gamma, alpha):
+    return float(lib().sd_expected_tokens(int(gamma), float(alpha)))
+
+
+def sd_speedup(t_target, t_draft, t_verify, gamma, alpha, t_select_fixed=0.0, t_select_step=0.0):
+    return float(lib().sd_speedup(float(t_target), float(t_draft), float(t_verify), int(gamma), float(alpha),
+                                  float(t_select_fixed), float(t_select_step)))
+
+
+def sd_best_gamma(t_target, t_draft, t_verify_by_gamma, alpha, t_select_fixed=0.0, t_select_step=0.0):
+    """(gamma, speedup); t_verify_by_gamma[g - 1] = T_V(g), host floats."""
+    n = len(t_verify_by_gamma)
+    tv = (ctypes.c_double * max(n, 1))(*[float(t) for t in t_verify_by_gamma])
+    g = ctypes.c_int32(0)
+    sp = ctypes.c_double(0.0)
+    _check(lib().sd_best_gamma(float(t_target), float(t_draft), ctypes.cast(tv, _P), n, float(alpha),
+                               float(t_select_fixed), float(t_select_step), ctypes.byref(g), ctypes.byref(sp)),
+           "sd_best_gamma")
+    return int(g.value), float(sp.value)
 
 
 def _stream(stream):

@@ -33,7 +33,7 @@ def L():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:sd_status|size_t|const char \*|int32_t)\s*\*?\s*(sd_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:sd_status|size_t|const char \*|int32_t|double)\s*\*?\s*(sd_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 210
+    assert sd.version() == 220
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
