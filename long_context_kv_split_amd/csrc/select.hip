@@ -28,8 +28,8 @@
 // positions with the largest q.k, searched again at every draft step) reuses
 // the pieces: topk_scores streams K like the SnapKV passes and writes every
 // score as an order-preserving 32-bit key (S^T = K Q^T, one 16-byte store per
-// head and step), and topk_rows selects per (sequence, query head) with the
-// same bit-by-bit threshold search, from bit 31.
+// head and step, staged in LDS), and topk_rows selects per (sequence, query
+// head) with the same bit-by-bit threshold search, from bit 31.
 #include "sd_device.h"
 #include "sd_host.h"
 #include "sd_sched.h"
@@ -84,8 +84,14 @@ struct SnapParams {
   int32_t pool_kernel, budget;  // budget: the largest budget and the width of an idx row
   const int32_t *budgets;       // [B] per-sequence budgets, or null (every sequence uses `budget`)
   float scale_log2;
-  uint32_t *keys;      // top-K attention: [B*Hq, key_stride] order keys of q.k
+  // top-K attention
+  uint32_t *keys;      // [B*Hq, key_stride] candidate order keys of q.k (per scoring segment)
+  int32_t *cand_pos;   // [B*Hq, key_stride] their positions
+  uint32_t *tau;       // [B*Hq] candidate threshold per row
+  int32_t *counts;     // [slots, G] candidates per scoring segment and head
+  int32_t *deferred;   // [1 + B*Hq]: count, then the rows left to the full selection kernel
   int32_t key_stride;  // a multiple of 16
+  int32_t head_dim;
 };
 
 constexpr int kRing = 4;       // 16-key K steps per wave in LDS: 3 loading while one is scored
@@ -593,9 +599,14 @@ struct TopkLds {
 // top (each bit one ballot count over the block); then every key above T and
 // the lowest-positioned keys equal to T are written in position order from one
 // block scan of per-wave counts.
-template <int THREADS, int VPT, int TOP_BIT>
+struct PosIdentity {
+  __device__ int operator()(int, int j) const { return j; }
+};
+
+// pos(i, j): the value written for the key in register i of position j.
+template <int THREADS, int VPT, int TOP_BIT, class PosFn = PosIdentity>
 __device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int n, uint32_t keep, int32_t *out,
-                                                TopkLds<THREADS, VPT> &sm) {
+                                                TopkLds<THREADS, VPT> &sm, PosFn pos = PosFn()) {
   constexpr int kWaves = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t T = 0;
@@ -640,9 +651,9 @@ __device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int 
     const uint32_t gt_before = (uint32_t)p + (uint32_t)__popcll(gm & below);
     const uint32_t eq_before = (uint32_t)(p >> 32) + (uint32_t)__popcll(em & below);
     if (gt)
-      out[gt_before + min(eq_before, need)] = j;
+      out[gt_before + min(eq_before, need)] = pos(i, j);
     else if (eq && eq_before < need)
-      out[gt_before + eq_before] = j;
+      out[gt_before + eq_before] = pos(i, j);
   }
 }
 
@@ -822,23 +833,171 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kTauWords = 4096;      // sampled keys per unit (all heads)
+constexpr int kTauThreads = 1024;
+constexpr int kSmallThreads = 256;   // selection of rows with few candidates
+constexpr int kSmallVpt = 24;
+constexpr int kSmallSegs = 512;
+constexpr int kStageEntries = 256;   // staged candidates per wave in the scoring pass
+constexpr int kRowsThreads = 1024;
+constexpr int kCandVpt = 8;          // candidates per thread in the selection (8192 per row)
+constexpr int kCandVptBig = 32;      // the same for large budgets (32768 per row)
+constexpr int kMaxSegs = 4096;       // scoring segments per unit the selection gathers from LDS
+
+// Sampled position i < n_s of a sequence of length L: every position when
+// n_s = L; otherwise n_s / 16 runs of 16 consecutive positions (one step, one
+// page block) at evenly spread steps, all below L.
+__device__ __forceinline__ int sample_pos(int i, int L, int n_s) {
+  if (n_s >= L) return i;
+  const int runs = n_s / kStepTokens, full_steps = L / kStepTokens;  // full_steps >= runs since L > n_s
+  return (int)((int64_t)(i / kStepTokens) * full_steps / runs) * kStepTokens + i % kStepTokens;
+}
+
+// Threshold per (sequence, query head): the t-th largest score key of n_s
+// sampled positions (sample_pos), with t chosen so that at least `budget`
+// keys of the whole row lie at or above it unless the sample is far from
+// representative: t = n_s * budget / L (the expected number of samples among
+// the budget largest keys) plus five standard deviations of that count plus
+// 8, a binomial tail of about 1e-8 per row for independent scores. Keys at or
+// above the threshold are the row's candidates; a row with fewer than
+// `budget` candidates is recomputed in full by the selection kernel, so the
+// threshold only affects speed, never the result. One block of
+// 16 waves per (sequence, KV head): each wave scores at most kBatch steps of
+// 16 samples, with all their loads in flight at once.
+template <int D>
+__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(SnapParams a) {
+  __shared__ uint32_t sk[kTauWords];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.deferred[0] = 0;  // the selection kernels run after this one
+  const int L = clampi(a.kv_lens[b], 0, a.len_cap);
+  if (L <= a.budget) return;
+  const int cap = min(1024, kTauWords / a.G / kStepTokens * kStepTokens);  // samples per head, >= 256
+  const int n_s = min(L, cap);
+  u32x4 q[1][D / 32];
+  snap_load_q<D, 1>(a, b, kvh, q);
+  const char *kp = reinterpret_cast<const char *>(a.k_pages);
+  const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+  constexpr int kBatch = 4;  // steps of 16 samples whose loads are issued together
+  constexpr int kWaves = kTauThreads / 64;
+  const int n_steps = (n_s + kStepTokens - 1) / kStepTokens;
+  // wave w scores steps w, w + kWaves, ...
+  for (int s0 = wave; s0 < n_steps; s0 += kBatch * kWaves) {
+    u32x4 k[kBatch][D / 32];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = min((s0 + j * kWaves) * kStepTokens + r, n_s - 1);
+      const int pos = sample_pos(i, L, n_s);
+      const int page = clampi(pt[pos / a.page_size], 0, a.num_pages - 1);
+      const char *kb = kp + ((size_t)(page * a.Hkv + kvh) * a.page_size + pos % a.page_size) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) k[j][kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int st = s0 + j * kWaves;
+      if (st >= n_steps) break;
+      const f32x4 sc = snap_scores<D, 1>(k[j], q, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = st * kStepTokens + 4 * g + e;
+        if (r < a.G && i < n_s) sk[r * cap + i] = order_key(sc[e]);
+      }
+    }
+  }
+  __syncthreads();
+  const float expect = (float)a.budget * (float)n_s / (float)L;
+  const int t = n_s == L ? a.budget : min(n_s, (int)ceilf(expect + 5.f * sqrtf(expect) + 8.f));
+  for (int h = wave; h < a.G; h += kWaves) {
+    uint32_t v[16];  // cap / 64 <= 16 keys per lane
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = lane + 64 * i;
+      v[i] = idx < n_s ? sk[h * cap + idx] : 0u;
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c += v[i] >= cand ? 1u : 0u;
+      if (wave_sum_u32(c) >= (uint32_t)t) T = cand;
+    }
+    if (lane == 0) a.tau[(size_t)b * a.Hq + (size_t)kvh * a.G + h] = T;
+  }
+}
+
+// LDS accesses the compiler does not track (no wait added for the
+// asynchronous ring loads); reads return with their data.
+__device__ __forceinline__ void lds_write_b64(const char *lds, int byte_off, uint32_t x, uint32_t y) {
+  const uint32_t addr = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
+  u32x2 v = {x, y};
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+#endif
+}
+__device__ __forceinline__ void lds_read_4xb64(const char *lds, int byte_off, int stride, u32x2 (&v)[4]) {
+  const uint32_t a0 = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
+  const uint32_t a1 = a0 + stride, a2 = a0 + 2 * stride, a3 = a0 + 3 * stride;
+#if __HIP_DEVICE_COMPILE__
+  asm volatile(
+      "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+#endif
+}
+
 // Scores <q_h, k_j> of the G query heads of each KV head over the unit's keys
-// (sequences longer than the budget only), as order keys at
-// keys[(b*Hq + h)*key_stride + j]. Lane (g, r) holds keys 4g..4g+3 of the step
-// for head r. A store joins the in-order memory counter after the K loads of
-// three steps ahead, so the stream's wait also covers one load of the next
-// step: slightly stricter, never looser.
+// (sequences longer than the budget only). Keys at or above the row's
+// threshold are candidates: each segment writes its candidates, in position
+// order, as (key, position) at the start of its own key range of the row
+// (keys[row][s_begin*16 + c], cand_pos likewise) and their number to
+// counts[slot*G + h]. Lane (g, r) holds keys 4g..4g+3 of a step for head r;
+// a candidate's place among the step's candidates of its head comes from four
+// ballots. Stores share the in-order memory counter with the K stream, so
+// candidates are staged in LDS (kStageEntries / G per head) and leave in
+// batches.
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void topk_scores_kernel(SnapParams a) {
-  __shared__ __attribute__((aligned(16))) char lds[KStream<D>::kLdsBytes];
+  constexpr int kStageOff = KStream<D>::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kStageOff + kStageEntries * 8];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t) {
+  const int cap_h = kStageEntries / a.G;  // staged entries per head (G <= 16: >= 16, one step's worth)
+  const uint64_t head_lanes = 0x0001000100010001ull << r;          // lanes (0..3, r)
+  const uint64_t lower_lanes = head_lanes & ((1ull << (16 * g)) - 1ull);  // lanes (g' < g, r)
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     s_begin = __builtin_amdgcn_readfirstlane(s_begin);
     s_end = __builtin_amdgcn_readfirstlane(s_end);
     u32x4 q[1][D / 32];
     snap_load_q<D, 1>(a, b, kvh, q);  // rows = G (one query row per head)
-    uint32_t *krow = a.keys + ((size_t)b * a.Hq + (size_t)kvh * a.G + min(r, a.G - 1)) * a.key_stride + 4 * g;
+    const size_t row0 = (size_t)b * a.Hq + (size_t)kvh * a.G;
+    const uint32_t tau = r < a.G ? a.tau[row0 + r] : 0u;
+    const int L = clampi(a.kv_lens[b], 0, a.len_cap);  // positions past L are never candidates
+    int staged = 0, written = 0;  // of head r (the same in every lane of that head)
+    // Write the staged entries of every head after the ones already written:
+    // lane l moves stage slots l, l+64, l+128, l+192.
+    auto flush = [&]() {
+      u32x2 v[4];
+      lds_read_4xb64(lds, kStageOff + 8 * lane, 64 * 8, v);
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int slot_i = lane + 64 * k4;
+        const int h = slot_i / cap_h, i = slot_i % cap_h;
+        const int hs = min(h, a.G - 1);
+        const int n_h = __shfl(staged, hs, 64), w_h = __shfl(written, hs, 64);
+        if (h < a.G && i < n_h) {
+          const size_t at = (row0 + h) * a.key_stride + (size_t)s_begin * kStepTokens + w_h + i;
+          a.keys[at] = v[k4].x;
+          a.cand_pos[at] = (int32_t)v[k4].y;
+        }
+      }
+      written += staged;
+      staged = 0;
+    };
     KStream<D> ks(a, b, kvh, s_end - 1, lds);
     ks.begin(s_begin);
     for (int s = s_begin; s < s_end; ++s) {
@@ -846,50 +1005,272 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void to
       u32x4 k[D / 32];
       ks.operand(s, k);
       const f32x4 sc = snap_scores<D, 1>(k, q, 0);
-      if (r < a.G)
-        *reinterpret_cast<u32x4 *>(krow + (size_t)s * kStepTokens) =
-            u32x4{order_key(sc[0]), order_key(sc[1]), order_key(sc[2]), order_key(sc[3])};
+      uint32_t key[4];
+      bool pass[4];
+      uint64_t m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = order_key(sc[e]);
+        pass[e] = r < a.G && key[e] >= tau && s * kStepTokens + 4 * g + e < L;
+        m[e] = __ballot(pass[e]);
+      }
+      if ((m[0] | m[1] | m[2] | m[3]) == 0ull) continue;  // no candidate in this step (the common case)
+      if (__ballot(staged + kStepTokens > cap_h) != 0ull) flush();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        before += __popcll(m[e] & lower_lanes);
+        total += __popcll(m[e] & head_lanes);
+      }
+      int at = staged + before;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (pass[e]) {
+          lds_write_b64(lds, kStageOff + (r * cap_h + at) * 8, key[e], (uint32_t)(s * kStepTokens + 4 * g + e));
+          ++at;
+        }
+      }
+      staged += total;
     }
+    flush();
+    if (g == 0 && r < a.G) a.counts[slot * a.G + r] = written;
   });
   KStream<D>::drain();
 }
 
-// One block per (sequence, query head): the budget largest keys of the row,
-// or every position when the sequence is not longer than the budget.
-template <int THREADS, int VPT>
-__global__ __launch_bounds__(THREADS) void topk_rows_kernel(SnapParams a) {
-  __shared__ TopkLds<THREADS, VPT> sm;
+// Segments of the unit (sequence b, KV head kvh) in the scoring schedule:
+// waves w_lo..w_hi each own a run of its steps.
+struct UnitSegs {
+  int64_t T, W, A, w_lo, w_hi;
+  __device__ UnitSegs(const SnapParams &a, int b, int kvh, int n) {
+    T = (int64_t)a.Hkv * a.sc.seq_prefix[a.sc.B];
+    W = sched_working_waves(a.sc, T);
+    A = (int64_t)a.Hkv * a.sc.seq_prefix[b] + (int64_t)kvh * n;
+    sched_unit_waves(A, n, T, W, w_lo, w_hi);
+  }
+  __device__ int count() const { return (int)(w_hi - w_lo + 1); }
+  // first key (within the unit) of segment i
+  __device__ int key0(int i) const {
+    const int64_t w = w_lo + i;
+    return (int)(max(A, (w * T + W - 1) / W) - A) * kStepTokens;
+  }
+};
+
+// Per (sequence, query head) with at most kSmallThreads * kSmallVpt
+// candidates (the common case): gather the row's candidates from its unit's
+// scoring segments and select the budget largest, ties to the lower position,
+// ascending, in one block of four waves. Other rows are marked for
+// topk_rows_full_kernel.
+__global__ __launch_bounds__(kSmallThreads) void topk_rows_small_kernel(SnapParams a) {
+  __shared__ TopkLds<kSmallThreads, kSmallVpt> sm;
+  __shared__ int32_t seg_off[kSmallSegs + 1];
+  __shared__ int32_t seg_key0[kSmallSegs];
+  __shared__ uint64_t scan_w[kSmallThreads / 64];
+  __shared__ uint64_t total_sh;
   const int tid = threadIdx.x;
   const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const size_t row = (size_t)b * a.Hq + h;
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  int32_t *out = a.idx + ((size_t)b * a.Hq + h) * a.budget;
-  if (h == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
+  int32_t *out = a.idx + row * a.budget;
   if (L <= a.budget) {
-    for (int t = tid; t < a.budget; t += THREADS) out[t] = t < L ? t : -1;
+    if (h == 0 && tid == 0) a.sel_lens[b] = L;
+    for (int t = tid; t < a.budget; t += kSmallThreads) out[t] = t < L ? t : -1;
     return;
   }
-  const uint32_t *krow = a.keys + ((size_t)b * a.Hq + h) * a.key_stride;  // L <= THREADS * VPT (host)
-  uint32_t key[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int j = tid + THREADS * i;
-    key[i] = j < L ? krow[j] : 0u;
+  const int kvh = h / a.G, hl = h % a.G;
+  const int u = b * a.Hkv + kvh;
+  const UnitSegs us(a, b, kvh, (L + kStepTokens - 1) / kStepTokens);
+  const int nseg = us.count();
+  int E = -1;
+  if (nseg <= kSmallSegs) {
+    uint64_t carry = 0;
+    for (int base = 0; base < nseg; base += kSmallThreads) {
+      const int sgi = base + tid;
+      uint64_t cnt = 0;
+      if (sgi < nseg) {
+        seg_key0[sgi] = us.key0(sgi);
+        cnt = (uint64_t)a.counts[((size_t)a.sc.slot_base[u] + sgi) * a.G + hl];
+      }
+      const uint64_t ex = block_exclusive_scan_u64<kSmallThreads / 64>(cnt, scan_w);
+      if (sgi < nseg) seg_off[sgi] = (int)(carry + ex);
+      if (tid == kSmallThreads - 1) total_sh = ex + cnt;
+      __syncthreads();
+      carry += total_sh;
+      __syncthreads();
+    }
+    if (tid == 0) seg_off[nseg] = (int)carry;
+    __syncthreads();
+    E = (int)carry;
   }
-  select_top_keys<THREADS, VPT, 31>(key, L, (uint32_t)a.budget, out, sm);
+  const bool here = E >= a.budget && E <= kSmallThreads * kSmallVpt;
+  if (!here) {
+    if (tid == 0) a.deferred[1 + atomicAdd(a.deferred, 1)] = (int32_t)row;
+    return;
+  }
+  if (h == 0 && tid == 0) a.sel_lens[b] = a.budget;
+  const uint32_t *krow = a.keys + row * a.key_stride;
+  const int32_t *prow = a.cand_pos + row * a.key_stride;
+  uint32_t key[kSmallVpt];
+  int32_t pos[kSmallVpt];
+#pragma unroll
+  for (int i = 0; i < kSmallVpt; ++i) {
+    const int e = tid + kSmallThreads * i;
+    key[i] = 0u;  // candidate keys are >= their threshold > 0: zero padding is never counted
+    pos[i] = 0;
+    if (e < E) {
+      int lo = 0, hi = nseg - 1;  // last segment with seg_off <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_off[mid] <= e)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int at = seg_key0[lo] + (e - seg_off[lo]);
+      key[i] = krow[at];
+      pos[i] = prow[at];
+    }
+  }
+  select_top_keys<kSmallThreads, kSmallVpt, 31>(key, E, (uint32_t)a.budget, out, sm,
+                                                [&](int i, int) { return pos[i]; });
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_global_kernel(SnapParams a) {
+// The rows topk_rows_small_kernel left: the budget largest keys of the row,
+// ties to the lower position, ascending. The row's candidates are gathered
+// from the scoring segments of its unit (the segment boundaries follow from
+// the schedule tables), and the budget largest are selected among them in
+// registers. A row with fewer candidates than the budget (threshold above the
+// budget-th key), more than kRowsThreads * kCandVptBig candidates, or more than
+// kMaxSegs segments is recomputed in full: every score again with the
+// scoring pass's MFMA arithmetic, written over the row's key array, and
+// selected with the radix select.
+template <int D>
+__device__ void topk_row_full(const SnapParams &a, int b, int h) {
+  __shared__ TopkLds<kRowsThreads, kCandVpt> sm;
+  __shared__ TopkLds<kRowsThreads, kCandVptBig> sm_big;
+  __shared__ int32_t seg_off[kMaxSegs + 1];
+  __shared__ int32_t seg_key0[kMaxSegs];
+  __shared__ uint32_t scan_tmp[40];
   const int tid = threadIdx.x;
-  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const size_t row = (size_t)b * a.Hq + h;
   const int L = clampi(a.kv_lens[b], 0, a.len_cap);
-  int32_t *out = a.idx + ((size_t)b * a.Hq + h) * a.budget;
+  int32_t *out = a.idx + row * a.budget;
   if (h == 0 && tid == 0) a.sel_lens[b] = min(L, a.budget);
-  if (L <= a.budget) {
-    for (int t = tid; t < a.budget; t += kTopkThreads) out[t] = t < L ? t : -1;
+  const int kvh = h / a.G, hl = h % a.G;
+  uint32_t *krow = a.keys + row * a.key_stride;
+  const int32_t *prow = a.cand_pos + row * a.key_stride;
+
+  const int u = b * a.Hkv + kvh;
+  const UnitSegs us(a, b, kvh, (L + kStepTokens - 1) / kStepTokens);
+  const int nseg = us.count();
+  int E = 0;
+  if (nseg <= kMaxSegs) {
+    uint32_t carry = 0;
+    for (int base = 0; base < nseg; base += kRowsThreads) {
+      const int sgi = base + tid;
+      uint32_t cnt = 0;
+      if (sgi < nseg) {
+        seg_key0[sgi] = us.key0(sgi);
+        cnt = (uint32_t)a.counts[((size_t)a.sc.slot_base[u] + sgi) * a.G + hl];
+      }
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan(cnt, scan_tmp, &tot);
+      if (sgi < nseg) seg_off[sgi] = (int)(carry + ex);
+      carry += tot;
+    }
+    if (tid == 0) seg_off[nseg] = (int)carry;
+    __syncthreads();
+    E = (int)carry;
+  }
+  // Candidate e (in position order) sits at the start of its segment's key range.
+  auto gather = [&](int e, uint32_t &key, int32_t &pos) {
+    int lo = 0, hi = nseg - 1;  // last segment with seg_off <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_off[mid] <= e)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int at = seg_key0[lo] + (e - seg_off[lo]);
+    key = krow[at];
+    pos = prow[at];
+  };
+  // candidate keys are >= their threshold > 0, so zero padding is never counted
+  if (nseg <= kMaxSegs && E >= a.budget && E <= kRowsThreads * kCandVpt) {
+    uint32_t key[kCandVpt];
+    int32_t pos[kCandVpt];
+#pragma unroll
+    for (int i = 0; i < kCandVpt; ++i) {
+      key[i] = 0u;
+      pos[i] = 0;
+      if (tid + kRowsThreads * i < E) gather(tid + kRowsThreads * i, key[i], pos[i]);
+    }
+    select_top_keys<kRowsThreads, kCandVpt, 31>(key, E, (uint32_t)a.budget, out, sm,
+                                                [&](int i, int) { return pos[i]; });
     return;
   }
-  const uint32_t *krow = a.keys + ((size_t)b * a.Hq + h) * a.key_stride;
+  if (nseg <= kMaxSegs && E >= a.budget && E <= kRowsThreads * kCandVptBig) {
+    uint32_t key[kCandVptBig];
+    int32_t pos[kCandVptBig];
+#pragma unroll
+    for (int i = 0; i < kCandVptBig; ++i) {
+      key[i] = 0u;
+      pos[i] = 0;
+      if (tid + kRowsThreads * i < E) gather(tid + kRowsThreads * i, key[i], pos[i]);
+    }
+    select_top_keys<kRowsThreads, kCandVptBig, 31>(key, E, (uint32_t)a.budget, out, sm_big,
+                                                   [&](int i, int) { return pos[i]; });
+    return;
+  }
+
+  // Full recomputation of the row with the scoring pass's arithmetic: wave w
+  // of the block scores steps w, w + 16, ... (16 keys each, kBatch steps'
+  // loads in flight) for the G heads of the unit and keeps head hl's keys.
+  constexpr int kWaves = kRowsThreads / 64;
+  constexpr int kBatch = 4;
+  const int lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  u32x4 q[1][D / 32];
+  snap_load_q<D, 1>(a, b, kvh, q);
+  const char *kp = reinterpret_cast<const char *>(a.k_pages);
+  const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+  const int n_steps = (L + kStepTokens - 1) / kStepTokens;
+  for (int s0 = wave; s0 < n_steps; s0 += kBatch * kWaves) {
+    u32x4 k[kBatch][D / 32];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int pos = min((s0 + j * kWaves) * kStepTokens + r, L - 1);
+      const int page = clampi(pt[pos / a.page_size], 0, a.num_pages - 1);
+      const char *kb = kp + ((size_t)(page * a.Hkv + kvh) * a.page_size + pos % a.page_size) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) k[j][kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int st = s0 + j * kWaves;
+      if (st >= n_steps) break;
+      const f32x4 sc = snap_scores<D, 1>(k[j], q, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = st * kStepTokens + 4 * g + e;
+        if (r == hl && pos < L) krow[pos] = order_key(sc[e]);
+      }
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
   select_top_keys_global([&](int j) { return krow[j]; }, L, a.budget, out);
+}
+
+// One block per deferred row, in turn.
+template <int D>
+__global__ __launch_bounds__(kRowsThreads) void topk_rows_full_kernel(SnapParams a) {
+  for (int k = blockIdx.x; k < a.deferred[0]; k += gridDim.x) {
+    const int row_id = a.deferred[1 + k];
+    topk_row_full<D>(a, row_id / a.Hq, row_id % a.Hq);
+    __syncthreads();  // LDS of this row is reused by the next
+  }
 }
 
 struct SnapLayout {
@@ -1056,15 +1437,20 @@ extern "C" sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void 
 namespace {
 
 struct TopkLayout {
-  size_t keys_off, bytes;
+  size_t tau_off, def_off, counts_off, keys_off, pos_off, bytes;
   int key_stride;
 };
 
 TopkLayout topk_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len) {
   TopkLayout l;
   l.key_stride = (int)(sdh::ceil_div(std::max<int64_t>(1, max_len), 16) * 16);
-  l.keys_off = sdh::sched_table_bytes(B, Hkv);
-  l.bytes = l.keys_off + sdh::align_up((size_t)B * Hq * l.key_stride * 4);
+  const size_t row_bytes = sdh::align_up((size_t)B * Hq * l.key_stride * 4);
+  l.tau_off = sdh::sched_table_bytes(B, Hkv);
+  l.def_off = l.tau_off + sdh::align_up((size_t)B * Hq * 4);
+  l.counts_off = l.def_off + sdh::align_up((size_t)(B * Hq + 1) * 4);
+  l.keys_off = l.counts_off + sdh::align_up((size_t)sdh::sched_max_slots(B, Hkv) * (Hq / Hkv) * 4);
+  l.pos_off = l.keys_off + row_bytes;
+  l.bytes = l.pos_off + row_bytes;
   return l;
 }
 
@@ -1073,20 +1459,10 @@ void launch_topk_attn_select(SnapParams &a, int B, hipStream_t st) {
   static int cache = 0;  // resident waves of the scoring kernel, queried once
   a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(topk_scores_kernel<D>), 2 * kSimdsPerCU, &cache);
   snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+  topk_tau_kernel<D><<<(unsigned)(B * a.Hkv), kTauThreads, 0, st>>>(a);
   topk_scores_kernel<D><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
-  const unsigned blocks = (unsigned)(B * a.Hq);
-  constexpr int TH = kTopkThreads;
-  const int64_t n = a.len_cap;
-  if (n <= 8 * TH)
-    topk_rows_kernel<TH, 8><<<blocks, TH, 0, st>>>(a);
-  else if (n <= 16 * TH)
-    topk_rows_kernel<TH, 16><<<blocks, TH, 0, st>>>(a);
-  else if (n <= 32 * TH)
-    topk_rows_kernel<TH, 32><<<blocks, TH, 0, st>>>(a);
-  else if (n <= 64 * TH)
-    topk_rows_kernel<TH, 64><<<blocks, TH, 0, st>>>(a);
-  else
-    topk_rows_global_kernel<<<blocks, TH, 0, st>>>(a);
+  topk_rows_small_kernel<<<(unsigned)(B * a.Hq), kSmallThreads, 0, st>>>(a);
+  topk_rows_full_kernel<D><<<(unsigned)std::min<int64_t>((int64_t)B * a.Hq, 2 * kNumCUs), kRowsThreads, 0, st>>>(a);
 }
 
 }  // namespace
@@ -1126,7 +1502,12 @@ extern "C" sd_status sd_topk_select(const sd_kv_cache *kv, const void *q, int32_
   char *ws = reinterpret_cast<char *>(workspace);
   sdh::sched_bind(a.sc, ws, batch, kv->num_kv_heads);
   a.keys = reinterpret_cast<uint32_t *>(ws + lay.keys_off);
+  a.cand_pos = reinterpret_cast<int32_t *>(ws + lay.pos_off);
+  a.tau = reinterpret_cast<uint32_t *>(ws + lay.tau_off);
+  a.counts = reinterpret_cast<int32_t *>(ws + lay.counts_off);
+  a.deferred = reinterpret_cast<int32_t *>(ws + lay.def_off);
   a.key_stride = lay.key_stride;
+  a.head_dim = kv->head_dim;
   a.idx = idx;
   a.sel_lens = sel_lens;
   a.W = 1;

@@ -126,6 +126,39 @@ def test_topk_select_max_len_above_lengths_and_exact_ties():
     assert (idx.cpu().numpy() == want).all()
 
 
+@pytest.mark.parametrize("case", ["sample-grid-spikes", "large-budget", "recompute-by-size"])
+def test_topk_select_candidate_paths(case):
+    """The selection keeps the keys at or above a sampled threshold as
+    candidates. Spikes on exactly the sampled positions push that threshold
+    above the budget-th key, so the row is recomputed in full; a large budget
+    gives more candidates than the small register path holds; a long row with
+    a budget near half its length exceeds every register path."""
+    Hq, Hkv, d = 4, 1, 128
+    if case == "sample-grid-spikes":
+        L, budget = 32768, 2048
+    elif case == "large-budget":
+        L, budget = 32768, 8192
+    else:
+        L, budget = 70000, 30000
+    kv_t = paged_kv(35, [L], Hkv, d, BF16, "cuda", page_size=16, spike_frac=0.0)
+    q = queries(35, 2, (1, 1, Hq, d), BF16, "cuda", scale=1.0)
+    grid = None
+    if case == "sample-grid-spikes":
+        q[:] = q[:, :, :1]  # every head asks the same question
+        u = q[0, 0, 0].float()
+        # the sampled positions at L = 32768, G = 4: 64 runs of 16 at steps 32k
+        grid = (torch.arange(64, device="cuda")[:, None] * 512 + torch.arange(16, device="cuda")).reshape(-1)
+        pt = kv_t.page_table[0].long()
+        kv_t.k_pages[pt[grid // 16], 0, grid % 16, :] = (4.0 * u / u.norm()).to(BF16)
+    idx, sel = run_topk(kv_t, q, Hq, budget)
+    near = check_selection(kv_t, q, idx, sel, budget, [L], [(0, h) for h in range(Hq)])
+    say(f"  {case}: L={L} budget={budget} near-tie rows={near}")
+    if grid is not None:
+        ic = idx.cpu().numpy()
+        for h in range(Hq):  # every spike is kept
+            assert set(grid.tolist()) <= set(ic[0, h].tolist())
+
+
 @pytest.mark.parametrize("n_q", [1, 2])
 def test_per_query_head_draft_parity(n_q):
     """Draft over one index set per query head (random sets, ragged lengths,
