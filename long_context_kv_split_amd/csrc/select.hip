@@ -115,6 +115,20 @@ __device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address
 #endif
 }
 
+// Two 16-byte LDS reads at byte_off and byte_off + gap (gap an immediate
+// offset), untracked by the compiler like the word accesses below; they
+// return with their data.
+template <int GAP>
+__device__ __forceinline__ void lds_read_b128_pair_t(const char *lds, int byte_off, u32x4 &lo, u32x4 &hi) {
+  const uint32_t addr = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(addr), "n"(GAP)
+               : "memory");
+#endif
+}
+
 // LDS word access the compiler does not track (so it adds no wait for the
 // asynchronous ring loads); the read returns with its data.
 __device__ __forceinline__ void lds_write_f32(const char *lds, int byte_off, float v) {
@@ -476,14 +490,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     KStream<D> ks(a, b, kvh, s_end - 1, lds);
     ks.begin(s_begin);
     // Staged steps [w0, s] of the current batch to global memory.
+    // Lane l stores staged votes 4l..4l+3 and 256+4l..256+4l+3 of the batch
+    // as 16-byte stores (the row stride is a multiple of 4 floats).
     auto flush = [&](int w0, int s) {
       const int n = (s - w0 + 1) * kStepTokens;
+      u32x4 v[2];
+      lds_read_b128_pair_t<1024>(lds, kStageOff + 16 * lane, v[0], v[1]);
 #pragma unroll
-      for (int i = 0; i < kStageSteps * kStepTokens / 64; ++i) {
-        const int j = i * 64 + lane;
+      for (int c = 0; c < 2; ++c) {
+        const int j = 256 * c + 4 * lane;
         const int tok = w0 * kStepTokens + j;
-        const float v = lds_read_f32(lds, kStageOff + j * 4);
-        if (j < n && tok < t_hi) vrow[tok] = v;
+        if (j + 3 < n && tok + 3 < t_hi) {
+          *reinterpret_cast<u32x4 *>(vrow + tok) = v[c];
+        } else {
+          const uint32_t e4[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < n && tok + e < t_hi) vrow[tok + e] = __uint_as_float(e4[e]);
+        }
       }
     };
     for (int s = s_begin; s < s_end; ++s) {
@@ -1280,7 +1304,7 @@ struct SnapLayout {
 
 SnapLayout snap_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t max_len) {
   SnapLayout l;
-  l.vote_stride = (int)std::max<int64_t>(1, max_len);
+  l.vote_stride = (int)(sdh::ceil_div(std::max<int64_t>(1, max_len), 4) * 4);  // 16-byte aligned rows
   l.stats_off = sdh::sched_table_bytes(B, Hkv);
   l.votes_off = l.stats_off + sdh::align_up((size_t)sdh::sched_max_slots(B, Hkv) * rows * 2 * 4);
   l.pooled_off = l.votes_off + sdh::align_up((size_t)B * Hkv * l.vote_stride * 4);
