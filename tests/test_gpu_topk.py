@@ -239,3 +239,55 @@ def test_topk_full_size_sampled():
         o_ref, l_ref = oracle.sparse_attn(q[b:b + 1, :, h:h + 1].cpu(), k, v, table, ic[b:b + 1, h:h + 1],
                                           [int(sel[b])], 1.0)
         compare_attn(out[b:b + 1, :, h:h + 1], lse[b:b + 1, :, h:h + 1], o_ref, l_ref, BF16)
+
+
+def test_topk_draft_step_graph_replay_matches_eager():
+    """Top-K selection and the per-head draft captured in a HIP graph: every
+    replay (with eager work between replays) reproduces the eager results bit
+    for bit, including a row that takes the full-row path (spikes on the
+    sampled positions of sequence 0) and a sequence shorter than the budget."""
+    Hq, Hkv, d, budget = 8, 2, 128, 1500  # 1024 spikes < budget: the spiked rows are recomputed
+    lens = [32768, 20000, 700, 9000]
+    kv_t = paged_kv(36, lens, Hkv, d, BF16, "cuda", shuffle=True, spike_frac=0.1)
+    q = queries(36, 2, (len(lens), 1, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    q[0, 0, :4] = q[0, 0, 0]  # the first group asks one question; spike its sampled positions
+    u = q[0, 0, 0].float()
+    grid = (torch.arange(64, device="cuda")[:, None] * 512 + torch.arange(16, device="cuda")).reshape(-1)
+    pt = kv_t.page_table[0].long()
+    kv_t.k_pages[pt[grid // 16], 0, grid % 16, :] = (4.0 * u / u.norm()).to(BF16)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    B, L = len(lens), max(lens)
+    idx = torch.empty((B, Hq, budget), dtype=torch.int32, device="cuda")
+    sel = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws_t = sd.workspace(sd.sd_topk_select_workspace_size(B, Hq, Hkv, L))
+    ws_d = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, budget))
+
+    def step():
+        sd.sd_topk_select(kv, q, Hq, budget, L, idx, sel, ws_t)
+        sd.sd_draft_attn_sparse(kv, q, 1, Hq, idx, sel, Hq, budget, 1.0, out, None, ws_d)
+
+    step()
+    torch.cuda.synchronize()
+    want = (idx.clone(), sel.clone(), out.clone())
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx.fill_(-7)
+        sel.fill_(-7)
+        out.fill_(float("nan"))
+        ws_t.fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, want[0]) and torch.equal(sel, want[1]), rep
+        assert torch.equal(out.view(torch.int16), want[2].view(torch.int16)), rep
+    # the replays agree with the oracle on the spiked row and a short one
+    near = check_selection(kv_t, q, idx, sel, budget, lens, [(0, 0), (0, 3), (2, 5), (3, 7)])
+    assert near <= 1
