@@ -26,10 +26,15 @@
 //
 // Top-K attention (the dynamic draft of §4.4: per query head, the budget
 // positions with the largest q.k, searched again at every draft step) reuses
-// the pieces: topk_scores streams K like the SnapKV passes and writes every
-// score as an order-preserving 32-bit key (S^T = K Q^T, one 16-byte store per
-// head and step, staged in LDS), and topk_rows selects per (sequence, query
-// head) with the same bit-by-bit threshold search, from bit 31.
+// the pieces in four kernels: topk_tau scores a sample of 1024 positions per
+// row and takes a threshold that the budget-th largest key exceeds except
+// with negligible probability; topk_scores streams K like the SnapKV passes
+// and writes only the keys at or above it (order-preserving 32-bit keys with
+// their positions, staged in LDS); topk_rows_small selects the budget largest
+// candidates of a row in registers with the same bit-by-bit search (from bit
+// 31); topk_rows_full takes the rows it could not (too many candidates, or
+// too few when the threshold was too high: then it recomputes the whole row),
+// so the sample changes the speed and never the result.
 #include "sd_device.h"
 #include "sd_host.h"
 #include "sd_sched.h"
