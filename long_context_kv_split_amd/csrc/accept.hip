@@ -80,7 +80,7 @@ __device__ __forceinline__ void load_chunk(const float *z, int t0, int V, float 
     for (int e = 0; e < kPerThread / 4; ++e) {
       const int t = t0 + (e * kAccThreads + (int)threadIdx.x) * 4;
       if (t + 3 < V) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(z + t);
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + t));
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[4 * e + j] = v[j] * inv_temp;
       } else {

@@ -108,10 +108,12 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // Asynchronous copies of 16 or 4 bytes per lane from global memory to LDS at
 // dst + lane * size (dst is wave-uniform). The builtin exists only for the
-// device target; a host pass that sees it drops the kernels that use it.
+// device target; a host pass that sees it drops the kernels that use it. The
+// 16-byte copies stream K and carry the nontemporal cache policy (bit 1 of
+// the policy operand).
 __device__ __forceinline__ void lds_dma16(const void *src, __attribute__((address_space(3))) void *dst) {
 #if __HIP_DEVICE_COMPILE__
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
 #endif
 }
 __device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address_space(3))) void *dst) {
@@ -921,7 +923,8 @@ __global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(SnapParams a) {
       const int page = clampi(pt[pos / a.page_size], 0, a.num_pages - 1);
       const char *kb = kp + ((size_t)(page * a.Hkv + kvh) * a.page_size + pos % a.page_size) * D * 2;
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) k[j][kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+      for (int kk = 0; kk < D / 32; ++kk)
+        k[j][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2));
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -1273,7 +1276,8 @@ __device__ void topk_row_full(const SnapParams &a, int b, int h) {
       const int page = clampi(pt[pos / a.page_size], 0, a.num_pages - 1);
       const char *kb = kp + ((size_t)(page * a.Hkv + kvh) * a.page_size + pos % a.page_size) * D * 2;
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) k[j][kk] = *reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2);
+      for (int kk = 0; kk < D / 32; ++kk)
+        k[j][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (32 * kk + 8 * g) * 2));
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
