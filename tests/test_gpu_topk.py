@@ -96,6 +96,9 @@ TOPK_CASES = [
     ("tiles-ragged", 8, 2, 128, [4111, 9000, 16, 8200], 512, 16, True, 0.1),
     ("vpt16", 4, 1, 128, [20000, 12000], 1024, 64, True, 0.1),
     ("budget-1", 8, 2, 128, [50, 333], 1, 16, False, 0.0),
+    ("g5-odd", 10, 2, 128, [6000, 2500, 12000], 300, 16, True, 0.1),
+    ("g3-d64", 6, 2, 64, [5000, 700, 16384], 256, 32, True, 0.0),
+    ("ragged-many", 8, 2, 128, [1000 + 2531 * i for i in range(16)], 512, 16, True, 0.1),
 ]
 
 
