@@ -162,6 +162,19 @@ def test_topk_select_candidate_paths(case):
             assert set(grid.tolist()) <= set(ic[0, h].tolist())
 
 
+def test_topk_select_one_long_sequence_many_segments():
+    """One sequence of 200k tokens and one KV head: the scoring schedule splits
+    the unit over more segments than the small selection gathers, so the rows
+    go through the full-row kernel's candidate path."""
+    L, Hq, Hkv, d, budget = 200000, 4, 1, 128, 2048
+    kv_t = paged_kv(37, [L], Hkv, d, BF16, "cuda", spike_frac=0.1)
+    q = queries(37, 2, (1, 1, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    idx, sel = run_topk(kv_t, q, Hq, budget)
+    near = check_selection(kv_t, q, idx, sel, budget, [L], [(0, h) for h in range(Hq)])
+    say(f"  one sequence L={L}: near-tie rows={near}")
+    assert near <= 1
+
+
 @pytest.mark.parametrize("n_q", [1, 2])
 def test_per_query_head_draft_parity(n_q):
     """Draft over one index set per query head (random sets, ragged lengths,
