@@ -499,8 +499,8 @@ def measure_hetero(reps=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not implemented", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design, not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 
