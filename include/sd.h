@@ -223,8 +223,11 @@ sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void *q_obs, int
  *   fp32 rounding of each other at the cut, either may be kept.
  * Limits: bf16 caches; num_q_heads / num_kv_heads <= 16; batch *
  *   ceil(max_kv_len / 16) < 2^31 (else SD_ERR_UNSUPPORTED). max_kv_len bounds
- *   kv_lens as for verify. Workspace: sd_topk_select_workspace_size (it holds
- *   batch * num_q_heads * max_kv_len 32-bit score keys).
+ *   kv_lens as for verify. Workspace: sd_topk_select_workspace_size (about
+ *   8 * batch * num_q_heads * max_kv_len bytes: room for a 32-bit key and a
+ *   position per cached token of every row; a call writes only the keys at
+ *   or above a sampled per-row threshold, and recomputes a row in full when
+ *   the threshold proves too high, so the result never depends on it).
  */
 sd_status sd_topk_select(const sd_kv_cache *kv, const void *q, int32_t batch, int32_t num_q_heads,
                          int32_t budget, int32_t max_kv_len, int32_t *idx, int32_t *sel_lens,
