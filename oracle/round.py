@@ -56,8 +56,10 @@ def kv_advance(kv_lens, add, n_accepted=None):
 
 
 def draft_positions(idx, sel_lens, tail_begin, kv_lens, b, g):
-    """Positions the draft of sequence b, KV head g reads: the selection
-    idx[b, g or 0, :sel_lens[b]] followed by the tail [tail_begin[b], kv_len)."""
+    """Positions the draft of sequence b reads for idx row g (a KV head, or a
+    query head when idx has one row per query head; row 0 when shared): the
+    selection idx[b, g or 0, :sel_lens[b]] followed by the tail
+    [tail_begin[b], kv_len)."""
     idx = i64(idx)
     gi = g if idx.shape[1] > 1 else 0
     sel = idx[b, gi, :int(i64(sel_lens)[b])]
@@ -69,7 +71,9 @@ def sparse_attn_tail(q, k_pages, v_pages, page_table, idx, sel_lens, tail_begin,
                      units=None):
     """Draft attention over the selected positions plus the appended tail.
 
-    q: [B, n_q, Hq, d]; every query row sees every position read. Returns
+    q: [B, n_q, Hq, d]; every query row sees every position read. idx has one
+    row per sequence (shared), per KV head, or per query head (top-K
+    attention: head h reads its own selection, then the tail). Returns
     (o [B, n_q, Hq, d], lse [B, n_q, Hq]) in float64.
     """
     q = f64(q)
@@ -82,13 +86,16 @@ def sparse_attn_tail(q, k_pages, v_pages, page_table, idx, sel_lens, tail_begin,
     o = np.zeros((B, n_q, Hq, d))
     lse = np.full((B, n_q, Hq), -np.inf)
     todo = units if units is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    per_query_head = i64(idx).shape[1] == Hq and G > 1
     for b, g in todo:
-        pos = draft_positions(idx, sel_lens, tail_begin, kv_lens, b, g)
-        keys = token_rows(K, pt, b, pos, g)
-        vals = token_rows(V, pt, b, pos, g)
         heads = list(range(g * G, (g + 1) * G))
-        rows = q[b][:, heads, :].reshape(n_q * G, d)
-        ob, lb = attend(rows, keys, vals, scale)
-        o[b][:, heads, :] = ob.reshape(n_q, G, d)
-        lse[b][:, heads] = lb.reshape(n_q, G)
+        for hs in ([[h] for h in heads] if per_query_head else [heads]):
+            row = hs[0] if per_query_head else g
+            pos = draft_positions(idx, sel_lens, tail_begin, kv_lens, b, row)
+            keys = token_rows(K, pt, b, pos, g)
+            vals = token_rows(V, pt, b, pos, g)
+            rows = q[b][:, hs, :].reshape(n_q * len(hs), d)
+            ob, lb = attend(rows, keys, vals, scale)
+            o[b][:, hs, :] = ob.reshape(n_q, len(hs), d)
+            lse[b][:, hs] = lb.reshape(n_q, len(hs))
     return o, lse

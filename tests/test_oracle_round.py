@@ -143,3 +143,28 @@ def test_tail_from_zero_without_selection_is_dense_decode():
     o_tail, l_tail = sparse_attn_tail(q, K, K, table, sel, [0, 0], [0, 0], lens, 0.5)
     o_dec, l_dec = oracle.verify_attn(q, K, K, table, lens, 0.5)  # n_q = 1: plain decode
     assert np.allclose(o_tail, o_dec, atol=1e-13) and np.allclose(l_tail, l_dec, atol=1e-13)
+
+
+def test_tail_with_one_set_per_query_head_matches_sdpa():
+    """One selection row per query head (top-K attention): head h attends
+    over its own positions, then the shared tail (SDPA over gathered rows)."""
+    rng = np.random.default_rng(9)
+    B, Hkv, G, d, P = 2, 2, 3, 8, 16
+    lens = [60, 41]
+    dense_k = rng.standard_normal((B, max(lens), Hkv, d))
+    dense_v = rng.standard_normal((B, max(lens), Hkv, d))
+    K, table = build_cache(dense_k, lens, P, 1, np.random.default_rng(10))
+    V, _ = build_cache(dense_v, lens, P, 1, np.random.default_rng(10))
+    tail_begin = [52, 41]
+    sel = np.full((B, Hkv * G, 6), -1)
+    for b in range(B):
+        for h in range(Hkv * G):
+            sel[b, h, :5] = np.sort(rng.choice(tail_begin[b], 5, replace=False))
+    q = rng.standard_normal((B, 1, Hkv * G, d))
+    o, _ = sparse_attn_tail(q, K, V, table, sel, [5, 5], tail_begin, lens, 0.3)
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            pos = list(sel[b, h, :5]) + list(range(tail_begin[b], lens[b]))
+            ref = sdpa(q[b, :, h], dense_k[b, pos, g], dense_v[b, pos, g], 0.3)
+            assert np.allclose(o[b, :, h], ref, atol=1e-12)
