@@ -205,6 +205,34 @@ def test_per_query_head_draft_parity(n_q):
     assert (lse_a - lse_b).abs().max() <= 1e-4
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_per_query_head_draft_fp32(d):
+    """The per-query-head draft on fp32 caches, with the appended tail read
+    after each head's own set (1e-5 relative bar)."""
+    Hq, Hkv, max_sel, tail = 6, 2, 40, 9
+    lens = [300, 1200]
+    kv_t = paged_kv(38, lens, Hkv, d, torch.float32, "cuda", shuffle=True)
+    rng = np.random.default_rng(38)
+    tail_begin = [L - tail for L in lens]
+    sel_lens = [max_sel, max_sel]
+    idx = np.full((len(lens), Hq, max_sel), -1, dtype=np.int32)
+    for b in range(len(lens)):
+        for h in range(Hq):
+            idx[b, h] = np.sort(rng.choice(tail_begin[b], max_sel, replace=False))
+    q = queries(38, 3, (len(lens), 1, Hq, d), torch.float32, "cuda", scale=d ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((len(lens), 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_draft_attn_sparse_workspace_size(len(lens), 1, Hq, Hkv, d, max_sel), "cuda")
+    sd.sd_draft_attn_sparse_tail(kv, q, 1, Hq, torch.from_numpy(idx).cuda(),
+                                 torch.tensor(sel_lens, dtype=torch.int32, device="cuda"), Hq, max_sel,
+                                 torch.tensor(tail_begin, dtype=torch.int32, device="cuda"), tail, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_attn_tail(q.cpu(), kv_t.k_pages.cpu(), kv_t.v_pages.cpu(), kv_t.page_table.cpu(),
+                                           idx, sel_lens, tail_begin, lens, 1.0)
+    compare_attn(out, lse, o_ref, l_ref, torch.float32)
+
+
 @pytest.mark.parametrize("case", ["small-g4", "tiles-ragged"])
 def test_topk_draft_step_parity(case):
     """Select, then draft over the selection: equal to the oracle over the
