@@ -498,7 +498,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     ks.begin(s_begin);
     // Staged steps [w0, s] of the current batch to global memory.
     // Lane l stores staged votes 4l..4l+3 and 256+4l..256+4l+3 of the batch
-    // as 16-byte stores (the row stride is a multiple of 4 floats).
+    // as 16-byte stores (the row stride is a multiple of 4 floats). The
+    // nontemporal policy streams them past the caches: with plain stores the
+    // pass measured about 5% slower.
     auto flush = [&](int w0, int s) {
       const int n = (s - w0 + 1) * kStepTokens;
       u32x4 v[2];
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
         const int j = 256 * c + 4 * lane;
         const int tok = w0 * kStepTokens + j;
         if (j + 3 < n && tok + 3 < t_hi) {
-          *reinterpret_cast<u32x4 *>(vrow + tok) = v[c];
+          __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4 *>(vrow + tok));
         } else {
           const uint32_t e4[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll

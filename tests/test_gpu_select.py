@@ -93,6 +93,8 @@ SNAP_CASES = [
     ("rows80-two-waves", 8, 2, 128, [2500, 1900], 20, 7, 256, 0.10),
     ("rows96-two-waves", 16, 2, 128, [2100, 3300], 12, 5, 300, 0.05),
     ("d64-rows112-two-waves", 16, 2, 64, [3000, 1000], 14, 5, 300, 0.10),
+    # a kept share near one half of the prefix
+    ("prefix-30k-half-budget", 8, 2, 128, [30000, 24000], 8, 7, 15000, 0.10),
     # radix variant: prefix beyond 64 Ki keys, and a pool kernel wider than 129
     ("prefix-70k-radix", 8, 2, 64, [70000], 4, 3, 1000, 0.10),
     ("pool131-radix", 8, 2, 128, [3000, 2500], 8, 131, 300, 0.0),
@@ -112,6 +114,32 @@ def test_snapkv_select_parity(case):
     near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
     say(f"  near-tie (flagged) units: {near}")
     assert near <= max(1, len(lens) * Hkv // 8)
+
+
+@pytest.mark.parametrize("classes", [1, 5, 64])
+def test_snapkv_tied_votes(classes):
+    """Every key row is one of `classes` vectors, so the votes tie in large
+    groups (one value per vector) and the kept set rests on the rule that
+    ties go to the lower position. With one vector every prefix vote is equal
+    and the kept prefix positions are 0 .. budget - W - 1."""
+    lens, W, pool, budget = [20000, 12000], 8, 7, 512
+    say(f"snapkv tied votes: classes={classes} lens={lens}")
+    kv_t = paged_kv(77, lens, 2, 128, BF16, "cuda", shuffle=True)
+    NP, H, P, d = kv_t.k_pages.shape
+    g = torch.Generator(device="cpu").manual_seed(700 + classes)
+    base = torch.randn(classes, H, d, generator=g).to(BF16)
+    cls = (torch.arange(NP * P) * 7919 % classes).view(NP, P)
+    kv_t.k_pages.copy_(base[cls].permute(0, 2, 1, 3).contiguous().to("cuda"))
+    q_obs = queries(77, 4, (len(lens), W, 8, 128), BF16, "cuda", scale=128 ** -0.5)
+    idx, sel = run_snapkv(kv_t, q_obs, W, 8, pool, budget)
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    W, pool, budget, 1.0, return_pooled=True)
+    near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
+    assert near == 0 if classes == 1 else near <= 1
+    if classes == 1:
+        for b, L in enumerate(lens):
+            want = list(range(budget - W)) + list(range(L - W, L))
+            assert (idx[b].cpu().numpy() == np.array(want)).all()
 
 
 def test_snapkv_is_deterministic():
