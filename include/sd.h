@@ -156,6 +156,8 @@ sd_status sd_draft_attn_sparse_tail(const sd_kv_cache *kv, const void *q, int32_
  *   [0, min(sink, L)) U [max(sink, L - recent), L).
  * idx: int32 [batch, 1, sink + recent] (entries past sel_lens[b] are -1);
  * sel_lens: int32 [batch] = min(L, sink + recent).
+ * Errors: SD_ERR_INVALID_ARG for null pointers, batch <= 0, negative sink or
+ * recent, or sink + recent == 0; SD_ERR_UNSUPPORTED for sink + recent >= 2^30.
  */
 sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, int32_t sink,
                               int32_t recent, int32_t *idx, int32_t *sel_lens, void *stream);
@@ -254,7 +256,12 @@ size_t sd_topk_select_workspace_size(int32_t batch, int32_t num_q_heads, int32_t
  *   [x_0 .. x_{n-1}, y, -1 ...].
  * Softmax exponentials are float32; normalisers and cumulative sums are
  *   accumulated in float64.
- * Limits: gamma >= 0, vocab >= 1, temperature > 0.
+ * Limits: gamma >= 0, vocab >= 1, 0 < temperature < inf, null pointers
+ *   (draft_* and u_accept may be null only when gamma = 0): else
+ *   SD_ERR_INVALID_ARG; gamma <= 64, vocab < 2^30,
+ *   batch * (gamma + 1) * vocab < 2^40 and batch * (2 gamma + 1) < 2^31: else
+ *   SD_ERR_UNSUPPORTED; a workspace smaller than
+ *   sd_spec_accept_workspace_size: SD_ERR_WORKSPACE.
  */
 sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
                          const int32_t *draft_tokens, const float *u_accept,

@@ -435,6 +435,7 @@ extern "C" sd_status sd_spec_accept(const float *target_logits, const float *dra
   SD_REQUIRE(temperature > 0.f && temperature < __builtin_inff(), SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)batch * (gamma + 1) * vocab < ((int64_t)1 << 40), SD_ERR_UNSUPPORTED);
   SD_REQUIRE(vocab < (1 << 30), SD_ERR_UNSUPPORTED);
+  SD_REQUIRE((int64_t)batch * (2 * gamma + 1) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);  // grid rows
   AccPlan p = plan_accept(batch, gamma, vocab);
   SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
 

@@ -1374,7 +1374,8 @@ extern "C" sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, 
                                          int32_t recent, int32_t *idx, int32_t *sel_lens,
                                          void *stream) {
   SD_REQUIRE(kv_lens != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(batch > 0 && sink >= 0 && recent >= 0 && sink + recent > 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(batch > 0 && sink >= 0 && recent >= 0 && (int64_t)sink + recent > 0, SD_ERR_INVALID_ARG);
+  SD_REQUIRE((int64_t)sink + recent < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);  // int32 row offsets
   streaming_select_kernel<<<(unsigned)batch, 256, 0, sdh::as_stream(stream)>>>(kv_lens, sink, recent,
                                                                               idx, sel_lens);
   return sdh::launch_status();

@@ -133,6 +133,8 @@ def test_draft_rejects_invalid_arguments(L, args, want):
     (dict(sink=-1), sd.SD_ERR_INVALID_ARG),
     (dict(sink=0, recent=0), sd.SD_ERR_INVALID_ARG),
     (dict(batch=0), sd.SD_ERR_INVALID_ARG),
+    (dict(sink=2**31 - 1, recent=2**31 - 1), sd.SD_ERR_UNSUPPORTED),
+    (dict(sink=1 << 29, recent=1 << 29), sd.SD_ERR_UNSUPPORTED),
 ])
 def test_streaming_rejects_invalid_arguments(L, args, want):
     a = dict(lens=FAKE, batch=2, sink=4, recent=8)
@@ -201,11 +203,12 @@ def test_topk_workspace_sizes():
     (dict(temp=float("inf")), sd.SD_ERR_INVALID_ARG),
     (dict(vocab=0), sd.SD_ERR_INVALID_ARG),
     (dict(ws_bytes=8), sd.SD_ERR_WORKSPACE),
+    (dict(batch=1 << 28, gamma=8, vocab=1), sd.SD_ERR_UNSUPPORTED),
 ])
 def test_accept_rejects_invalid_arguments(L, args, want):
-    a = dict(zt=FAKE, zd=FAKE, gamma=3, vocab=1000, temp=1.0, ws_bytes=1 << 30)
+    a = dict(zt=FAKE, zd=FAKE, batch=4, gamma=3, vocab=1000, temp=1.0, ws_bytes=1 << 30)
     a.update(args)
-    st = L.sd_spec_accept(a["zt"], a["zd"], FAKE, FAKE, FAKE, 4, a["gamma"], a["vocab"], a["temp"],
+    st = L.sd_spec_accept(a["zt"], a["zd"], FAKE, FAKE, FAKE, a["batch"], a["gamma"], a["vocab"], a["temp"],
                           FAKE, FAKE, WS, a["ws_bytes"], None)
     assert st == want
 
