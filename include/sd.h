@@ -334,6 +334,28 @@ sd_status sd_best_gamma(double t_target, double t_draft, const double *t_verify,
                         double alpha, double t_select_fixed, double t_select_step, int32_t *gamma_out,
                         double *speedup_out);
 
+/*
+ * Streaming-read probe: the attainable HBM read bandwidth, the ceiling the
+ * attention kernels are measured against next to the nominal figure (MagicDec
+ * notes, §3.2: at long context verification and drafting are bound by loading
+ * the KV cache). Not a step of the method: a measurement tool.
+ *
+ * Reads `bytes` bytes at `buf` once with 16-byte loads (with the nontemporal
+ * hint when nontemporal = 1, plain loads when 0), each wave of `blocks`
+ * 256-thread workgroups streaming one contiguous slice (blocks = 0: as many
+ * as the chip keeps resident), and ADDS the sum of its 32-bit words, modulo
+ * 2^32, to *checksum: the caller zeroes *checksum first (it is never cleared
+ * here). The best launch size depends on the chip and the access pattern, so
+ * a measurement sweeps `blocks` and keeps the fastest.
+ * buf: device, 16-byte aligned, bytes > 0 and a multiple of 16;
+ * checksum: device, one uint32, 4-byte aligned. Read-only on buf.
+ * SD_ERR_INVALID_ARG for null pointers, a misaligned buffer, a size that is
+ * zero or not a multiple of 16, nontemporal not 0 or 1, or blocks outside
+ * [0, 65536].
+ */
+sd_status sd_hbm_read_probe(const void *buf, size_t bytes, int32_t nontemporal, int32_t blocks,
+                            uint32_t *checksum, void *stream);
+
 /* Static string for a status code (never NULL). */
 const char *sd_status_string(sd_status status);
 

@@ -28,6 +28,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_draft_attn_sparse_tail,
     sd_draft_attn_sparse_workspace_size,
     sd_expected_tokens,
+    sd_hbm_read_probe,
     sd_kv_advance,
     sd_kv_append,
     sd_kv_cache,

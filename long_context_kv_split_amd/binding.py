@@ -70,6 +70,7 @@ _SIGNATURES = {
     "sd_speedup": (ctypes.c_double, [ctypes.c_double] * 3 + [_I] + [ctypes.c_double] * 3),
     "sd_best_gamma": (_I, [ctypes.c_double, ctypes.c_double, _P, _I, ctypes.c_double, ctypes.c_double,
                            ctypes.c_double, _P, _P]),
+    "sd_hbm_read_probe": (_I, [_P, _S, _I, _I, _P, _P]),
     "sd_status_string": (ctypes.c_char_p, [_I]),
     "sd_version": (_I, []),
 }
@@ -339,6 +340,16 @@ def sd_spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample
     wp, wb = _ws(workspace, need)
     _check(lib().sd_spec_accept(tp, dp, xp, up, us, B, gamma, vocab, temperature, np_, op, wp, wb,
                                 _stream(stream)), "sd_spec_accept")
+
+
+def sd_hbm_read_probe(buf, nontemporal, checksum, blocks=0, stream=None):
+    """Adds the uint32 word sum of `buf` (mod 2^32) to checksum[0]; the caller
+    zeroes it. `buf`: any contiguous GPU tensor of a multiple of 16 bytes;
+    `blocks`: 256-thread workgroups (0 = as many as are resident)."""
+    bp = _dev(buf, "buf")
+    cp = _dev(checksum, "checksum", torch.int32, 1)
+    _check(lib().sd_hbm_read_probe(bp, buf.numel() * buf.element_size(), int(nontemporal), int(blocks), cp,
+                                   _stream(stream)), "sd_hbm_read_probe")
 
 
 def workspace(nbytes, device="cuda"):

@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 220
+    assert sd.version() == 221
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
@@ -265,3 +265,23 @@ def test_snapkv_budgets_rejects_missing_budgets(L):
     st = L.sd_snapkv_select_budgets(ctypes.byref(kv), FAKE, 2, 8, 8, 7, FAKE, 8, 64, 1.0, FAKE, FAKE, WS,
                                     1 << 30, None)
     assert st == sd.SD_ERR_INVALID_ARG  # max_budget <= window
+
+
+@no_gpu
+@pytest.mark.parametrize("args", [
+    dict(buf=None),
+    dict(checksum=None),
+    dict(nbytes=0),
+    dict(nbytes=24),                 # not a multiple of 16
+    dict(buf=0x5008),                # not 16-byte aligned
+    dict(nontemporal=2),
+    dict(nontemporal=-1),
+    dict(blocks=-1),
+    dict(blocks=65537),
+])
+def test_read_probe_rejects_invalid_arguments(L, args):
+    a = dict(buf=FAKE, nbytes=1 << 20, nontemporal=1, blocks=0, checksum=FAKE)
+    a.update(args)
+    buf = ctypes.c_void_p(a["buf"]) if isinstance(a["buf"], int) else a["buf"]
+    st = L.sd_hbm_read_probe(buf, a["nbytes"], a["nontemporal"], a["blocks"], a["checksum"], None)
+    assert st == sd.SD_ERR_INVALID_ARG
