@@ -21,7 +21,10 @@ replayed from a HIP graph, and dense decode as the attention-only target step;
 step on the ragged B=256 batch; `dynamic_topk` times a top-K attention draft
 step (selection over the whole cache, then the per-head draft);
 `speedup_model` evaluates the analytic speedup model (best speculation length
-and attention-side speedup per draft kind and budget) on measured times.
+and attention-side speedup per draft kind and budget) on measured times;
+`other_workloads` times verify at the Llama-8B 8k, ragged B=256 and Llama-70B
+16k shapes, the StreamingLLM-512 draft step and acceptance over the 128256-token
+vocabulary, warm and cold (last-level cache evicted before each call).
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
@@ -531,6 +534,101 @@ def measure_hetero(reps=5):
             "draft_GBps": d_bytes / (t_dr * 1e-3) / 1e9}
 
 
+def measure_configs(reps=10):
+    """The other workloads' timed ops, beside the headline: verify at every
+    shape, the StreamingLLM-512 draft step at the Llama-8B 8k and ragged
+    shapes, acceptance over the 128256-token vocabulary at the Llama-70B
+    shape. Each op is timed warm (back to back, mean of `reps`) and cold
+    (median of `reps` single calls, each after writing a 1 GiB buffer that
+    evicts the 256 MB last-level cache and L2); GB/s are on algorithmic bytes
+    (K/V rows read, logits read)."""
+    import torch
+
+    import long_context_kv_split_amd as sd
+    from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries, workload_lens
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def warm(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def cold(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    def timing(fn, nbytes):
+        w_ms, c_ms = warm(fn), cold(fn)
+        return {"warm_ms": w_ms, "cold_ms": c_ms, "bytes": nbytes,
+                "warm_GBps": nbytes / (w_ms * 1e-3) / 1e9, "cold_GBps": nbytes / (c_ms * 1e-3) / 1e9}
+
+    out = {}
+    for name in ("llama8b-b32-l8k", "ragged-b256-l4k-32k", "llama70b-b64-l16k"):
+        w = WORKLOADS[name]
+        B, Hq, Hkv, d, n_q = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.gamma + 1
+        lens = workload_lens(w)
+        L = max(lens)
+        kv_t = paged_kv(w.seed, lens, Hkv, d, torch.bfloat16, "cuda", shuffle=w.shuffle)
+        kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+        q = queries(w.seed, 1, (B, n_q, Hq, d), torch.bfloat16, "cuda", scale=d ** -0.5)
+        o = torch.empty_like(q)
+        ws = sd.workspace(sd.sd_verify_attn_workspace_size(B, n_q, Hq, Hkv, d, L))
+        kv_bytes = sum(lens) * Hkv * d * 2 * 2
+        rec = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "n_q": n_q, "sum_context": sum(lens),
+               "pages": "shuffled" if w.shuffle else "in order",
+               "verify": timing(lambda: sd.sd_verify_attn(kv, q, n_q, Hq, L, 1.0, o, None, ws), kv_bytes)}
+        if w.draft == "streaming" and w.sink + w.recent > 0:
+            cap = w.sink + w.recent
+            idx = torch.empty((B, 1, cap), dtype=torch.int32, device="cuda")
+            sel = torch.empty((B,), dtype=torch.int32, device="cuda")
+            sd.sd_streaming_select(kv_t.kv_lens, w.sink, w.recent, idx, sel)
+            qd = q[:, :1].contiguous()
+            od = torch.empty_like(qd)
+            wsd = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, cap))
+            d_bytes = sum(min(x, cap) for x in lens) * Hkv * d * 2 * 2
+            rec["draft"] = timing(lambda: sd.sd_draft_attn_sparse(kv, qd, 1, Hq, idx, sel, 1, cap, 1.0, od,
+                                                                  None, wsd), d_bytes)
+            rec["draft"]["set"] = f"StreamingLLM {w.sink} sink + {w.recent} recent"
+        if w.vocab:
+            g, V = w.gamma, w.vocab
+            zt = logits(w.seed, 8, (B, g + 1, V), w.target_std, "cuda")
+            zd = logits(w.seed, 9, (B, g, V), w.draft_noise_std, "cuda", base=zt[:, :g]).contiguous()
+            x = gumbel_tokens(w.seed, zd)
+            ua = dyadic_uniforms(w.seed, 11, (B, g), "cuda")
+            us = dyadic_uniforms(w.seed, 12, (B, g + 1), "cuda")
+            n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
+            toks = torch.empty((B, g + 1), dtype=torch.int32, device="cuda")
+            wsa = sd.workspace(sd.sd_spec_accept_workspace_size(B, g, V))
+            rec["accept"] = timing(lambda: sd.sd_spec_accept(zt, zd, x, ua, us, g, V, 1.0, n_acc, toks, wsa),
+                                   (zt.numel() + zd.numel()) * 4)
+            rec["accept"]["vocab"] = V
+            rec["accept"]["mean_accepted"] = float(n_acc.float().mean().item())
+        out[name] = rec
+        log(f"{name}: verify {rec['verify']['warm_ms']:.3f} ms warm / {rec['verify']['cold_ms']:.3f} cold "
+            f"({rec['verify']['cold_GBps']:.0f} GB/s cold)"
+            + (f", draft {rec['draft']['cold_ms'] * 1e3:.1f} us cold" if "draft" in rec else "")
+            + (f", accept {rec['accept']['cold_ms'] * 1e3:.1f} us cold" if "accept" in rec else ""))
+        del kv_t, kv, q, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -624,6 +722,10 @@ def main():
         het = measure_hetero()
         log(f"per-sequence budgets: select {het['select_ms']:.3f} ms, draft {het['draft_ms']:.3f} ms")
 
+    cfgs = None
+    if not args.no_round:
+        cfgs = measure_configs()
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -660,6 +762,7 @@ def main():
         "per_sequence_budgets": het,
         "dynamic_topk": topk,
         "speedup_model": model,
+        "other_workloads": cfgs,
     }
     print(json.dumps(rec), flush=True)
 
