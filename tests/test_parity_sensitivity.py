@@ -1,4 +1,4 @@
-"""The bf16 attention parity criteria catch plausible kernel mistakes at full size.
+"""The parity criteria catch plausible kernel mistakes at full size.
 
 The GPU tests hold bf16 attention to max|dO| <= 2e-2, max|dO| / max|O_ref|
 <= 1e-2 and |d lse| <= 1e-4 (tests/gpu_helpers.py). At long context |O| is
@@ -10,14 +10,20 @@ copy computes verify attention on the Llama-3.1-8B layer shape at context 8192
 16-token pages), and its output must fail the criteria against the unchanged
 oracle. A split-KV combine that forgets the max rescale is emulated directly
 (the oracle has no split): eight segments per unit, as the persistent schedule
-makes at this shape. CPU only; no GPU code runs here.
+makes at this shape. Selected indices and emitted tokens must match exactly,
+so for them it is enough that a planted mistake changes the result on the
+real workloads: the SnapKV tie-break reversed (max-pooling makes plateaus of
+equal values, so ties at the threshold are the rule) on the 32k-context
+selection, and the bonus token drawn from the last draft position's target
+distribution on the 128256-token acceptance workload. CPU only; no GPU code
+runs here.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from synth import paged_kv, queries
+from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries
 from tests.gpu_helpers import BF16_ABS, BF16_LSE, BF16_NORM
 from tests.test_oracle_mutations import _install, _planted
 
@@ -108,3 +114,41 @@ def test_split_combine_without_max_rescale_fails_the_bf16_criteria(case):
                     o_bad[b, i, h] = w_bad @ os_ / w_bad.sum()
     assert np.abs(o_good - o_ref).max() < 1e-12   # the emulated split itself is right
     assert violations(o_bad, None, o_ref, None)
+
+
+def test_reversed_snapkv_tie_break_changes_the_selection_at_full_size(monkeypatch):
+    w = WORKLOADS["llama8b-b128-l32k-snapkv"]
+    kv = paged_kv(w.seed, [w.context], w.num_kv_heads, w.head_dim, torch.bfloat16, "cpu",
+                  spike_frac=w.spike_frac)
+    q_obs = queries(w.seed, 4, (1, w.window, w.num_q_heads, w.head_dim), torch.bfloat16, "cpu",
+                    scale=w.head_dim ** -0.5)
+
+    def select():
+        return oracle.snapkv_select(q_obs, kv.k_pages, kv.page_table, kv.kv_lens, w.window, w.pool_kernel,
+                                    w.budget, 1.0)[0]
+
+    ref = select()
+    mod, copy = _planted("selection", "np.lexsort((np.arange(v.shape[0]), -v))",
+                         "np.lexsort((-np.arange(v.shape[0]), -v))")
+    _install(monkeypatch, mod, copy, [oracle, mod])
+    bad = select()
+    changed = [g for g in range(w.num_kv_heads) if not np.array_equal(ref[0, g], bad[0, g])]
+    assert len(changed) >= 4, changed
+
+
+def test_bonus_from_the_wrong_row_changes_emitted_tokens_at_full_vocab(monkeypatch):
+    w = WORKLOADS["llama70b-b64-l16k"]
+    B, g, V = w.batch, w.gamma, w.vocab
+    zt = logits(w.seed, 8, (B, g + 1, V), w.target_std)
+    zd = logits(w.seed, 9, (B, g, V), w.draft_noise_std, base=zt[:, :g]).contiguous()
+    x = gumbel_tokens(w.seed, zd)
+    ua = dyadic_uniforms(w.seed, 11, (B, g))
+    us = dyadic_uniforms(w.seed, 12, (B, g + 1))
+    n, out, _ = oracle.spec_accept(zt, zd, x, ua, us)
+    mod, copy = _planted("accept", "r = p[gamma].copy()", "r = p[gamma - 1].copy()")
+    _install(monkeypatch, mod, copy, [oracle, mod])
+    n2, out2, _ = oracle.spec_accept(zt, zd, x, ua, us)
+    assert np.array_equal(n, n2)                      # the accept tests are untouched
+    full = n == g
+    assert full.sum() >= 8                            # ~0.8^4 of the batch accepts every draft
+    assert (out[full, g] != out2[full, g]).sum() >= full.sum() // 2
