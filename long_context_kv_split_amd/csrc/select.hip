@@ -48,6 +48,12 @@ namespace {
 constexpr int kStepTokens = 16;
 constexpr int kTopkThreads = 1024;
 constexpr int kMaxPoolHalf = 64;  // register top-K: pool kernels up to 129
+// Register top-K: after the bits from 22 up (sign, exponent and the top
+// mantissa bit of the pooled votes) the search goes on among the keys that
+// share them with the threshold: about 1000 of 32736 at the 32k-context
+// workload; up to kBandCap of them are gathered in LDS.
+constexpr int kBandCut = 22;
+constexpr int kBandCap = 2048;
 
 // ---------------------------------------------------------------- StreamingLLM
 __global__ __launch_bounds__(256) void streaming_select_kernel(const int32_t *kv_lens, int sink,
@@ -625,6 +631,14 @@ struct TopkLds {
   uint64_t scan_waves[kWaves];
 };
 
+// Keys whose bits above CUT equal those of the threshold found so far (the
+// band the remaining bits are searched in), gathered in LDS: at most CAP.
+template <int CAP>
+struct TopkBand {
+  uint32_t keys[CAP];
+  uint32_t count;
+};
+
 // Writes out[0, keep) = the positions j < n with the `keep` largest keys, ties
 // to the lower position, ascending; 0 < keep <= n. key[i] is the key of
 // position threadIdx.x + THREADS * i and 0 past n (a zero is never counted
@@ -636,25 +650,93 @@ struct PosIdentity {
   __device__ int operator()(int, int j) const { return j; }
 };
 
+// One bit of the threshold search: T | (1 << bit) is kept when at least `keep`
+// keys are >= it, counting `extra` (the same on every thread) plus the block's
+// keys in k[]. The count buffer of a bit is rewritten two bits later, after
+// the next bit's barrier.
+template <int THREADS, int N, int VPT>
+__device__ __forceinline__ uint32_t search_bit(const uint32_t (&k)[N], int bit, uint32_t T, uint32_t extra,
+                                               uint32_t keep, TopkLds<THREADS, VPT> &sm) {
+  constexpr int kWaves = THREADS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t cand = T | (1u << bit);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) c += k[i] >= cand ? 1u : 0u;
+  c = wave_sum_u32(c);
+  if (lane == 0) sm.cnt[bit & 1][wave] = c;
+  __syncthreads();
+  uint32_t total = extra;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += sm.cnt[bit & 1][w];
+  return total >= keep ? cand : T;
+}
+
 // pos(i, j): the value written for the key in register i of position j.
-template <int THREADS, int VPT, int TOP_BIT, class PosFn = PosIdentity>
+// With CUT > 0 the bits below CUT are searched only among the keys whose bits
+// from CUT up equal the threshold's (gathered in `band` when they fit, else
+// the search goes on over all keys): keys above that band are >= every
+// remaining candidate and keys below it are < all of them, so the counts, and
+// the threshold, are the same as over all keys.
+template <int THREADS, int VPT, int TOP_BIT, class PosFn = PosIdentity, int CUT = 0, int CAP = 1>
 __device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int n, uint32_t keep, int32_t *out,
-                                                TopkLds<THREADS, VPT> &sm, PosFn pos = PosFn()) {
+                                                TopkLds<THREADS, VPT> &sm, PosFn pos = PosFn(),
+                                                TopkBand<CAP> *band = nullptr) {
   constexpr int kWaves = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t T = 0;
-  for (int bit = TOP_BIT; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t c = 0;
+  int bit = TOP_BIT;
+  for (; bit >= CUT; --bit) T = search_bit<THREADS>(key, bit, T, 0u, keep, sm);
+  if constexpr (CUT > 0) {
+    static_assert(CAP % THREADS == 0, "band slots per thread");
+    constexpr int kPer = CAP / THREADS;
+    const uint32_t hi = T >> CUT;
+    if (tid == 0) band->count = 0u;
+    __syncthreads();
+    // Band members: counted per wave, one LDS reservation per wave, then
+    // placed by a second pass over the same ballots. Zero keys (every key
+    // past n, and any zero value) are left out: a zero is never >= a
+    // candidate, and never above the band.
+    uint32_t above = 0, mine = 0;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) c += key[i] >= cand ? 1u : 0u;
-    c = wave_sum_u32(c);
-    if (lane == 0) sm.cnt[bit & 1][wave] = c;
-    __syncthreads();  // a buffer is rewritten two bits later, after the next barrier
-    uint32_t total = 0;
+    for (int i = 0; i < VPT; ++i) {
+      above += (key[i] >> CUT) > hi ? 1u : 0u;
+      mine += ((key[i] >> CUT) == hi && key[i] != 0u) ? 1u : 0u;
+    }
+    const uint32_t wave_cnt = wave_sum_u32(mine);
+    uint32_t base = 0u;
+    if (lane == 0 && wave_cnt > 0u) base = atomicAdd(&band->count, wave_cnt);
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (wave_cnt > 0u) {
+      const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) total += sm.cnt[bit & 1][w];
-    if (total >= keep) T = cand;
+      for (int i = 0; i < VPT; ++i) {
+        const bool in = (key[i] >> CUT) == hi && key[i] != 0u;
+        const uint64_t m = __ballot(in);
+        const uint32_t slot = base + (uint32_t)__popcll(m & below);
+        if (in && slot < (uint32_t)CAP) band->keys[slot] = key[i];
+        base += (uint32_t)__popcll(m);
+      }
+    }
+    above = wave_sum_u32(above);
+    if (lane == 0) sm.cnt[0][wave] = above;  // both count buffers are free here
+    __syncthreads();
+    uint32_t n_above = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n_above += sm.cnt[0][w];
+    const uint32_t n_band = band->count;
+    __syncthreads();  // cnt[0] and the band are read before they are reused
+    if (n_band <= (uint32_t)CAP) {
+      uint32_t bk[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t slot = (uint32_t)(tid + THREADS * j);
+        bk[j] = slot < n_band ? band->keys[slot] : 0u;  // a zero is never >= a candidate
+      }
+      for (; bit >= 0; --bit) T = search_bit<THREADS>(bk, bit, T, n_above, keep, sm);
+    } else {
+      for (; bit >= 0; --bit) T = search_bit<THREADS>(key, bit, T, 0u, keep, sm);
+    }
   }
 
   // Per (i, wave): keys above T (low word) and equal to T (high word).
@@ -696,6 +778,7 @@ __device__ __forceinline__ void select_top_keys(const uint32_t (&key)[VPT], int 
 template <int THREADS, int VPT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(VPT <= 32 ? 8 : 4))) void snap_topk_kernel(SnapParams a) {
   __shared__ TopkLds<THREADS, VPT> sm;
+  __shared__ TopkBand<kBandCap> band;
   __shared__ float pool_lds[2][THREADS + 2 * kMaxPoolHalf];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
@@ -752,7 +835,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(VPT <= 
   }
 
   // Votes are sums of exponentials (>= +0), so bit 31 is clear.
-  select_top_keys<THREADS, VPT, 30>(key, npre, keep, out, sm);
+  select_top_keys<THREADS, VPT, 30, PosIdentity, kBandCut, kBandCap>(key, npre, keep, out, sm, PosIdentity(),
+                                                                     &band);
   for (int w = tid; w < a.W; w += THREADS) out[keep + w] = npre + w;
   for (int t = budget + tid; t < a.budget; t += THREADS) out[t] = -1;  // row past this budget
 }
