@@ -27,6 +27,11 @@ def _lib():
     torch.cuda.set_device(0)
 
 
+# More sequences than the planning block covers in one pass (1024), and more
+# (sequence, KV head) units than resident waves: the schedule's multi-pass
+# prefix sums and units that share a wave.
+MANY = np.random.default_rng(5).integers(0, 91, 2500).tolist()
+
 VERIFY_CASES = [
     # name, dtype, Hq, Hkv, d, lens, n_q, shuffle, page_size
     ("tiny-f32-b2-l256", F32, 8, 2, 64, [256, 256], 4, False, 16),
@@ -40,6 +45,7 @@ VERIFY_CASES = [
     ("bf16-page32", BF16, 8, 2, 128, [100, 1000], 4, True, 32),
     ("bf16-short", BF16, 8, 2, 128, [4, 3, 0, 1], 4, False, 16),
     ("bf16-decode-exact-pages", BF16, 8, 2, 128, [512, 1024], 1, True, 16),
+    ("bf16-2500-sequences", BF16, 8, 2, 128, MANY, 4, True, 16),
 ]
 
 
@@ -117,6 +123,8 @@ DRAFT_CASES = [
     ("shared-bf16-d64", BF16, 8, 2, 64, [999, 1234], 1, "shared", 333),
     ("per-head-f32-d128", F32, 16, 2, 128, [777, 1500], 1, "per-head", 200),
     ("per-head-rows64", BF16, 16, 1, 128, [1800], 4, "per-head", 700),
+    ("stream-2500-sequences", BF16, 8, 2, 128, MANY, 1, "streaming", 48),
+    ("per-head-2500-sequences", BF16, 8, 2, 128, MANY, 1, "per-head", 40),
 ]
 
 

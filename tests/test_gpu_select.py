@@ -98,6 +98,9 @@ SNAP_CASES = [
     # radix variant: prefix beyond 64 Ki keys, and a pool kernel wider than 129
     ("prefix-70k-radix", 8, 2, 64, [70000], 4, 3, 1000, 0.10),
     ("pool131-radix", 8, 2, 128, [3000, 2500], 8, 131, 300, 0.0),
+    # more sequences than the planning block covers in one pass, most of
+    # them at or under the budget
+    ("1500-sequences", 8, 2, 128, np.random.default_rng(6).integers(0, 301, 1500).tolist(), 8, 7, 48, 0.10),
 ]
 
 
