@@ -682,6 +682,10 @@ def main():
     value = step_tokens / (ms_step * 1e-3)
     round_ms = avg["verify_ms"] + wl.gamma * avg["draft_ms"]
     draft_gbps = wl.B * wl.w.budget * KV_BYTES_PER_TOKEN / (avg["draft_ms"] * 1e-3) / 1e9
+    # SnapKV reads every cached key twice (statistics pass, votes pass); acceptance
+    # reads the target and draft logits once
+    snap_gbps = 2 * sum(wl.lens) * wl.Hkv * wl.d * 2 / (avg["select_ms"] * 1e-3) / 1e9
+    acc_gbps = (2 * wl.gamma + 1) * wl.B * wl.V * 4 / (avg["accept_ms"] * 1e-3) / 1e9
 
     att = measure_attainable(wl)
     log(f"attainable read bandwidth: {att['nontemporal_GBps']:.0f} GB/s nontemporal, "
@@ -754,6 +758,8 @@ def main():
         "verify_pct_hbm_peak": 100.0 * v_gbps / HBM_PEAK_GBPS,
         "round_kv_tokens_per_s": step_tokens / (round_ms * 1e-3),
         "draft_kv_GBps": draft_gbps,
+        "snapkv_select_K_GBps": snap_gbps,
+        "accept_logits_GBps": acc_gbps,
         "attainable_read": att,
         "per_call_ms": avg,
         "mean_accepted": float(wl.n_acc.float().mean().item()),
