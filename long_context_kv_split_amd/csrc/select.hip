@@ -16,8 +16,10 @@
 //   3. snap_topk:   one 1024-thread block per (sequence, KV head): clipped
 //      max-pool of the votes into registers, the (budget - W)-th largest
 //      pooled value found bit by bit from the top (non-negative floats order
-//      as their bit patterns; each bit is one ballot count over the block),
-//      then an order-preserving write of every value above that threshold
+//      as their bit patterns; each bit is one ballot count over the block;
+//      the low bits are searched only among the keys in the threshold's
+//      band, gathered in LDS), then an order-preserving write of every value
+//      above that threshold
 //      and of the lowest positions among the ties, from one block scan of
 //      per-wave counts; the window positions are appended (ascending).
 //      Prefixes longer than 64 Ki keys and pool kernels wider than 129 use a
