@@ -25,7 +25,9 @@ Written out (float64), per sequence with draft length gamma and temperature t:
 A sequence is flagged when a uniform lies within `flag_eps` of a decision
 threshold: |u_i - p_i(x_i)/q_i(x_i)| < eps for an evaluated test, or v*Z
 within eps*Z of either end of y's CDF interval. Flagged sequences may
-legitimately differ between float64 and lower-precision implementations.
+legitimately differ between float64 and lower-precision implementations;
+`accept_outcomes` lists the results that remain correct for such a sequence
+and `accept_valid` checks a result against that list.
 """
 import numpy as np
 
@@ -82,12 +84,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
                 n += 1
             else:
                 break
-        if n < gamma:
-            r = np.maximum(0.0, p[n] - q[n])
-            if r.sum() == 0.0:
-                r = p[n].copy()
-        else:
-            r = p[gamma].copy()
+        r, _ = _residual(p, q, n, gamma)
         y, thr, lo, hi, Z = _sample_index(r, us[b, n])
         if abs(thr - lo) < flag_eps * Z or abs(thr - hi) < flag_eps * Z:
             flagged[b] = True
@@ -95,3 +92,116 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
         out[b, n] = y
         n_acc[b] = n
     return n_acc, out, flagged
+
+
+def _residual(p, q, n, gamma):
+    """Weights the emitted token is drawn from at acceptance count n, and
+    whether the residual was identically zero (the weights are then p_n)."""
+    if n < gamma:
+        r = np.maximum(0.0, p[n] - q[n])
+        if r.sum() == 0.0:
+            return p[n].copy(), True
+        return r, False
+    r = p[gamma].copy()
+    return r, False
+
+
+def _draws_in_band(r, v, eps, maybe_mass=None):
+    """Tokens an inverse-CDF draw with uniform v can return when v*Z may move by
+    up to eps*Z: every token with mass whose interval [C_{t-1}, C_t] meets
+    [v*Z - eps*Z, v*Z + eps*Z]; `maybe_mass` adds zero-weight tokens whose
+    weight a lower-precision evaluation could make positive (their interval is
+    the point C_t)."""
+    c = np.cumsum(r)
+    Z = c[-1]
+    lo = np.concatenate(([0.0], c[:-1]))
+    thr = v * Z
+    live = r > 0
+    if maybe_mass is not None:
+        live = live | maybe_mass
+    hit = live & (lo <= thr + eps * Z) & (c >= thr - eps * Z)
+    return set(np.nonzero(hit)[0].tolist())
+
+
+def accept_outcomes(target_logits, draft_logits, draft_tokens, u_accept, u_sample, b,
+                    temperature=1.0, flag_eps=1e-6, zero_eps=1e-5):
+    """All results (n, out_tokens row as a tuple) that sequence b may take when
+    each decision threshold may move by less than flag_eps (relative), i.e. the
+    results an implementation that evaluates p, q, the residual and its CDF to
+    about single precision can legitimately return (the explainer's
+    verification round, with the flag band of the exactness criterion):
+
+      - accept test i with p_i(x_i) > 0 and q_i(x_i) > 0 can go either way when
+        |u_i - p_i(x_i)/q_i(x_i)| < flag_eps; with p_i(x_i) = 0 it rejects and
+        with q_i(x_i) = 0 < p_i(x_i) it accepts for every uniform in [0, 1);
+      - n is reachable when every test before it can accept and test n can
+        reject (or n = gamma);
+      - the emitted token at n is any token with mass whose CDF interval meets
+        [v Z - eps Z, v Z + eps Z]; a token with zero residual weight counts
+        only when p and q agree there to zero_eps relative (single-precision
+        evaluation could leave it a sliver of mass); a residual that is zero,
+        or whose every weight is such a sliver, may also be replaced by p_n.
+
+    The result the oracle itself returns is always in the set; a sequence the
+    oracle does not flag has exactly that one result.
+    """
+    return _outcomes(f64(target_logits[b]), f64(draft_logits[b]), i64(draft_tokens[b]),
+                     f64(u_accept[b]), f64(u_sample[b]), temperature, flag_eps, zero_eps)
+
+
+def _outcomes(zt, zd, x, ua, us, temperature, flag_eps, zero_eps):
+    """accept_outcomes for one sequence's float64 rows."""
+    gamma = zt.shape[0] - 1
+    p = softmax(zt, temperature)
+    q = softmax(zd, temperature) if gamma > 0 else np.zeros((0, zt.shape[1]))
+    can_acc, can_rej = [], []
+    for i in range(gamma):
+        t = int(x[i])
+        pi, qi = p[i, t], q[i, t]
+        acc = bool(ua[i] * qi < pi)
+        band = pi > 0 and qi > 0 and abs(ua[i] - pi / qi) < flag_eps
+        can_acc.append(acc or band)
+        can_rej.append((not acc) or band)
+    results = set()
+    for n in range(gamma + 1):
+        if not all(can_acc[:n]):
+            break
+        if n < gamma and not can_rej[n]:
+            continue
+        r, fallback = _residual(p, q, n, gamma)
+        if n == gamma:
+            ys = _draws_in_band(r, us[n], flag_eps)
+        else:
+            close = (p[n] > 0) & (np.abs(p[n] - q[n]) <= zero_eps * np.maximum(p[n], q[n]))
+            if fallback or not ((r > 0) & ~close).any():
+                # every residual weight is zero or within rounding of zero: a
+                # single-precision residual may keep any of them, or none (then
+                # the draw is from p_n)
+                ys = set(np.nonzero(close)[0].tolist()) | _draws_in_band(p[n], us[n], flag_eps)
+            else:
+                ys = _draws_in_band(r, us[n], flag_eps, (r == 0) & close)
+        for y in ys:
+            row = [int(v) for v in x[:n]] + [int(y)] + [-1] * (gamma - n)
+            results.add((n, tuple(row)))
+    return results
+
+
+def accept_valid(target_logits, draft_logits, draft_tokens, u_accept, u_sample, n_accepted,
+                 out_tokens, temperature=1.0, flag_eps=1e-6, zero_eps=1e-5):
+    """Check a computed acceptance result per sequence against accept_outcomes.
+
+    Returns (valid bool [B], ambiguous bool [B]): valid[b] when (n_accepted[b],
+    out_tokens[b]) is one of sequence b's correct results, ambiguous[b] when
+    that sequence has more than one."""
+    n_in = i64(n_accepted)
+    out_in = i64(out_tokens)
+    zt, zd, x = f64(target_logits), f64(draft_logits), i64(draft_tokens)
+    ua, us = f64(u_accept), f64(u_sample)
+    B = n_in.shape[0]
+    valid = np.zeros(B, dtype=bool)
+    ambiguous = np.zeros(B, dtype=bool)
+    for b in range(B):
+        res = _outcomes(zt[b], zd[b], x[b], ua[b], us[b], temperature, flag_eps, zero_eps)
+        valid[b] = (int(n_in[b]), tuple(int(v) for v in out_in[b])) in res
+        ambiguous[b] = len(res) > 1
+    return valid, ambiguous

@@ -180,3 +180,118 @@ def test_gamma_zero_is_inverse_cdf_sampling_from_softmax():
     n, out, _ = oracle.spec_accept(zt, np.zeros((trials, 0, 7)), np.zeros((trials, 0), int),
                                    np.zeros((trials, 0)), rng.random((trials, 1)))
     assert _chi2_ok(out[:, 0], q) > 1e-3
+
+
+# ---- the set of correct results when a uniform sits in the flag band ----
+
+def test_golden_outcome_sets():
+    """Hand-derived sets of correct results (each fixture's "outcomes")."""
+    cases = json.load(open(os.path.join(GOLDEN, "accept_cases.json")))["cases"]
+    for c in cases:
+        zt = np.array(c["target_logits"])[None]
+        zd = np.array(c["draft_logits"])[None]
+        got = oracle.accept_outcomes(zt, zd, np.array(c["x"])[None], np.array(c["u_accept"])[None],
+                                     np.array(c["u_sample"])[None], 0)
+        want = {(n, tuple(o)) for n, o in c["outcomes"]}
+        assert got == want, c["name"]
+
+
+def _near_threshold_batch(seed, B, V, gamma):
+    """Random distributions whose uniforms sit within 0.5e-6 of a decision
+    threshold: the accept uniform of a random position next to p/q of its
+    draft token, the sampling uniform next to a random CDF boundary of the
+    weights the emitted token is drawn from."""
+    rng = np.random.default_rng(seed)
+    zt = rng.standard_normal((B, gamma + 1, V)) * 1.5
+    zd = zt[:, :gamma] + rng.standard_normal((B, gamma, V)) * 0.7
+    x = rng.integers(0, V, (B, gamma))
+    ua = rng.random((B, gamma))
+    us = rng.random((B, gamma + 1))
+    for b in range(B):
+        p = oracle.softmax(zt[b])
+        q = oracle.softmax(zd[b])
+        i = int(rng.integers(0, gamma))
+        ratio = p[i, x[b, i]] / q[i, x[b, i]]
+        if ratio < 0.999:
+            ua[b, i] = ratio + rng.uniform(-0.5e-6, 0.5e-6)
+        n, _, _ = oracle.spec_accept(zt[b:b + 1], zd[b:b + 1], x[b:b + 1], ua[b:b + 1], us[b:b + 1])
+        n = int(n[0])
+        r = np.maximum(0.0, p[n] - q[n]) if n < gamma else p[gamma]
+        c = np.cumsum(r) / r.sum()
+        t = int(rng.integers(0, V - 1))
+        if 1e-3 < c[t] < 0.999:
+            us[b, n] = c[t] + rng.uniform(-0.5e-6, 0.5e-6)
+    return zt, zd, x, ua, us
+
+
+def test_results_within_the_band_are_correct():
+    """Moving every uniform by less than the band keeps the result in the set:
+    the set holds what a slightly different rounding can return. Both sides of
+    the planted thresholds are reached, so the set is not a single result."""
+    B, V, gamma = 300, 40, 3
+    zt, zd, x, ua, us = _near_threshold_batch(81, B, V, gamma)
+    n0, out0, flagged = oracle.spec_accept(zt, zd, x, ua, us)
+    valid, ambiguous = oracle.accept_valid(zt, zd, x, ua, us, n0, out0)
+    assert valid.all()
+    assert flagged.sum() > B // 2 and ambiguous.sum() > B // 2
+    differ = 0
+    for shift in (-0.45e-6, 0.45e-6):
+        ua2 = np.clip(ua + shift, 0.0, 1.0 - 2 ** -24)
+        us2 = np.clip(us + shift, 0.0, 1.0 - 2 ** -24)
+        n2, out2, _ = oracle.spec_accept(zt, zd, x, ua2, us2)
+        v2, _ = oracle.accept_valid(zt, zd, x, ua, us, n2, out2)
+        assert v2.all(), np.nonzero(~v2)[0][:10]
+        differ += int(((n2 != n0) | (out2 != out0).any(axis=1)).sum())
+    assert differ > B // 4
+
+
+def test_results_outside_the_band_are_rejected():
+    """A result reached only by moving a uniform well past the band is not in
+    the set, and an unflagged sequence has exactly one correct result: every
+    other (n, token) pair, enumerated, is rejected."""
+    B, V, gamma = 200, 12, 2
+    rng = np.random.default_rng(91)
+    zt = rng.standard_normal((B, gamma + 1, V)) * 1.5
+    zd = zt[:, :gamma] + rng.standard_normal((B, gamma, V)) * 0.7
+    x = rng.integers(0, V, (B, gamma))
+    ua = rng.random((B, gamma))
+    us = rng.random((B, gamma + 1))
+    n0, out0, flagged = oracle.spec_accept(zt, zd, x, ua, us)
+    _, ambiguous = oracle.accept_valid(zt, zd, x, ua, us, n0, out0)
+    assert not (ambiguous & ~flagged).any()
+    moved = 0
+    for shift in (-3e-3, 3e-3):
+        n2, out2, _ = oracle.spec_accept(zt, zd, x, np.clip(ua + shift, 0, 0.999),
+                                         np.clip(us + shift, 0, 0.999))
+        changed = (n2 != n0) | (out2 != out0).any(axis=1)
+        v2, _ = oracle.accept_valid(zt, zd, x, ua, us, n2, out2)
+        assert not (v2 & changed & ~ambiguous).any()
+        moved += int((changed & ~ambiguous).sum())
+    assert moved > 10
+    for b in np.nonzero(~flagged)[0][:40]:
+        count = 0
+        for n in range(gamma + 1):
+            for y in range(V):
+                row = np.array([list(x[b, :n]) + [y] + [-1] * (gamma - n)])
+                v, _ = oracle.accept_valid(zt[b:b + 1], zd[b:b + 1], x[b:b + 1], ua[b:b + 1],
+                                           us[b:b + 1], np.array([n]), row)
+                count += int(v[0])
+        assert count == 1, b
+
+
+def test_band_flags_are_rare_at_large_vocabulary():
+    """At V = 128256 the band is reached mostly by the draw (about 2e-6 per
+    interval of the drawn row); the share of sequences with more than one
+    correct result stays near that expectation."""
+    rng = np.random.default_rng(95)
+    B, V, gamma = 48, 128256, 4
+    zt = rng.standard_normal((B, gamma + 1, V)) * 2.0
+    zd = zt[:, :gamma] + rng.standard_normal((B, gamma, V)) * 0.5
+    x = np.array([[np.searchsorted(np.cumsum(oracle.softmax(zd[b, i])), rng.random())
+                   for i in range(gamma)] for b in range(B)]).clip(0, V - 1)
+    ua = rng.random((B, gamma))
+    us = rng.random((B, gamma + 1))
+    n0, out0, flagged = oracle.spec_accept(zt, zd, x, ua, us)
+    valid, ambiguous = oracle.accept_valid(zt, zd, x, ua, us, n0, out0)
+    assert valid.all()
+    assert ambiguous.sum() <= flagged.sum() <= 20

@@ -101,6 +101,17 @@ MUTATIONS = [
     ("no-stop-at-first-reject", "accept",
      "                n += 1\n            else:\n                break",
      "                n += 1\n            else:\n                continue", ["accept"]),
+    # correct results inside the flag band (accept_outcomes)
+    ("band-ignores-zero-target-mass", "accept",
+     "band = pi > 0 and qi > 0 and abs(ua[i] - pi / qi) < flag_eps",
+     "band = qi > 0 and abs(ua[i] - pi / qi) < flag_eps", ["accept"]),
+    ("zero-weight-tokens-drawable", "accept",
+     "    live = r > 0\n", "    live = r >= 0\n", ["accept"]),
+    ("draw-band-not-widened", "accept",
+     "hit = live & (lo <= thr + eps * Z) & (c >= thr - eps * Z)",
+     "hit = live & (lo <= thr) & (c > thr)", ["accept"]),
+    ("band-test-decided-by-oracle-only", "accept",
+     "can_acc.append(acc or band)", "can_acc.append(acc)", ["accept"]),
     # round bookkeeping
     ("append-one-slot-late", "round",
      "t = int(lens[b]) + j", "t = int(lens[b]) + j + 1", ["round"]),
