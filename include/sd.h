@@ -18,10 +18,13 @@
  *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and
  *    returns without synchronising. A failed validation returns a non-zero
  *    status before any launch and before any write.
- *  - The library allocates no memory and keeps no mutable global state; calls
- *    are thread-safe and re-entrant. Scratch space is the caller's
- *    `workspace` of at least the size its *_workspace_size function returns;
- *    concurrent calls need distinct workspaces.
+ *  - The library allocates no memory. Its only mutable global state is a
+ *    per-device cache of resident-wave counts (an occupancy query made once
+ *    per kernel and device; a race stores the same value): it sets launch
+ *    sizes and the split-KV schedule only, so a device always computes the
+ *    same bits. Calls are thread-safe and re-entrant. Scratch space is the
+ *    caller's `workspace` of at least the size its *_workspace_size function
+ *    returns; concurrent calls need distinct workspaces.
  *  - Device-resident integers (page_table, kv_lens, idx, sel_lens,
  *    draft_tokens) are the caller's responsibility and are not validated;
  *    kernels clamp them into range so that bad values give wrong numbers,
@@ -83,7 +86,9 @@ typedef struct {
  *   n_q verify tokens are the last n_q tokens of each sequence's cache and
  *   query i (0-based) attends causally to positions 0 .. kv_len - n_q + i.
  * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
- * softmax_scale multiplies q.k (pass 1.0 when the scale is folded into q).
+ * softmax_scale multiplies q.k (pass 1.0 when the scale is folded into q); it
+ *   must be finite and > 0 (softmax_scale * log2(e) finite), else
+ *   SD_ERR_INVALID_ARG.
  * max_kv_len: an upper bound on kv_lens (sizes the split-KV plan; must not
  *   exceed max_pages * page_size).
  * out: [batch, n_q, num_q_heads, head_dim] of kv->dtype (bf16 results are
@@ -115,7 +120,8 @@ size_t sd_verify_attn_workspace_size(int32_t batch, int32_t n_q, int32_t num_q_h
  *   entries of idx[b, idx_heads > 1 ? g : 0, :]; with one set per query head
  *   (and num_q_heads > num_kv_heads), query head h uses idx[b, h, :].
  * Every query row attends to every selected position (q: [batch, n_q,
- *   num_q_heads, head_dim], normally n_q = 1). out/lse as for verify.
+ *   num_q_heads, head_dim], normally n_q = 1). softmax_scale, out and lse as
+ *   for verify.
  * Limits: (num_q_heads / num_kv_heads) * n_q <= 64; batch * ceil(max_sel / 16)
  *   < 2^31 (else SD_ERR_UNSUPPORTED).
  */
@@ -175,7 +181,9 @@ sd_status sd_streaming_select(const int32_t *kv_lens, int32_t batch, int32_t sin
  *     kept, ties toward the lower position;
  *  5. idx[b, g, :] = ascending union of those and the window (budget entries).
  *  If L <= budget every position 0..L-1 is kept (rest -1).
- * q_obs: [batch, window, num_q_heads, head_dim] of kv->dtype.
+ * q_obs: [batch, window, num_q_heads, head_dim] of kv->dtype. softmax_scale
+ *   multiplies q_obs.k inside the softmax of step 1 (1.0 when the scale is
+ *   folded into q_obs); finite and > 0 as for verify, else SD_ERR_INVALID_ARG.
  * idx: int32 [batch, num_kv_heads, budget]; sel_lens: int32 [batch] = min(L, budget).
  * Limits: budget > window >= 1; (num_q_heads / num_kv_heads) * window <= 128;
  *   pool_kernel odd and >= 1; max_kv_len bounds kv_lens; batch *

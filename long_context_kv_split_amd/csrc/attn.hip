@@ -464,9 +464,9 @@ WsLayout ws_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t D) {
 
 template <typename T, int D, int NB, bool SPARSE>
 sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
-  static int cache = 0;  // resident waves of this instantiation, queried once
+  static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>),
-                                   kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, &cache);
+                                   kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
   attn_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
   attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   const int total_rows = a.B * a.Hkv * a.rows;
@@ -503,7 +503,7 @@ sd_status common_checks(const sd_kv_cache *kv, const void *q, int32_t batch, int
   SD_REQUIRE(batch > 0 && n_q > 0 && num_q_heads > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)(num_q_heads / kv->num_kv_heads) * n_q <= 64, SD_ERR_UNSUPPORTED);
-  SD_REQUIRE(softmax_scale > 0.f && softmax_scale < __builtin_inff(), SD_ERR_INVALID_ARG);
+  SD_REQUIRE(softmax_scale > 0.f && softmax_scale * kLog2e < __builtin_inff(), SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)batch * kv->num_kv_heads + kMaxWaves < ((int64_t)1 << 30), SD_ERR_UNSUPPORTED);
   return SD_OK;
 }

@@ -65,14 +65,17 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const u32
 template <bool NT>
 sd_status launch_probe(const void *buf, int64_t n16, int blocks, uint32_t *checksum, hipStream_t st) {
   if (blocks == 0) {
-    static int cache = 0;  // resident 256-thread blocks of this instantiation, queried once
-    blocks = __atomic_load_n(&cache, __ATOMIC_RELAXED);
+    // resident 256-thread blocks of this instantiation, queried once per device
+    static int cache[sdh::kMaxDevices] = {};
+    int dev = 0, per_cu = 0, cus = 0;
+    const bool have_dev = hipGetDevice(&dev) == hipSuccess && dev >= 0;
+    int *slot = have_dev && dev < sdh::kMaxDevices ? cache + dev : nullptr;
+    blocks = slot ? __atomic_load_n(slot, __ATOMIC_RELAXED) : 0;
     if (blocks <= 0) {
-      int per_cu = 0, dev = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      if (!have_dev ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(
               &per_cu, reinterpret_cast<const void *>(hbm_read_probe_kernel<NT>), kProbeThreads, 0) !=
               hipSuccess ||
-          hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
           per_cu <= 0 || cus <= 0) {
         (void)hipGetLastError();
@@ -80,7 +83,7 @@ sd_status launch_probe(const void *buf, int64_t n16, int blocks, uint32_t *check
         cus = kNumCUs;
       }
       blocks = per_cu * cus;
-      __atomic_store_n(&cache, blocks, __ATOMIC_RELAXED);
+      if (slot) __atomic_store_n(slot, blocks, __ATOMIC_RELAXED);
     }
   }
   hbm_read_probe_kernel<NT><<<(unsigned)blocks, kProbeThreads, 0, st>>>(reinterpret_cast<const u32x4 *>(buf),

@@ -166,14 +166,25 @@ inline void sched_bind(sdk::Sched &s, void *tables, int32_t B, int32_t Hkv) {
   s.Hkv = Hkv;
 }
 
-// Resident one-wave blocks of `kernel` on the current device (queried once per
-// kernel and cached; a failed query falls back to `fallback_per_cu` per CU).
+constexpr int kMaxDevices = 64;  // devices with a cached occupancy entry
+
+// Resident one-wave blocks of `kernel` on the current device, queried once per
+// kernel and device and kept in cache[device] (cache has kMaxDevices entries;
+// devices past that are queried every call). A failed query falls back to
+// `fallback_per_cu` per CU. The count only sets the launch size and the
+// split-KV schedule; a device always gets the same count, so results stay
+// reproducible, and the workspace is sized for kMaxWaves whatever it is.
 inline int resident_waves(const void *kernel, int fallback_per_cu, int *cache) {
-  int w = __atomic_load_n(cache, __ATOMIC_RELAXED);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
+  }
+  int *slot = dev >= 0 && dev < kMaxDevices ? cache + dev : nullptr;
+  int w = slot ? __atomic_load_n(slot, __ATOMIC_RELAXED) : 0;
   if (w > 0) return w;
-  int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
-      hipGetDevice(&dev) != hipSuccess ||
+  int per_cu = 0, cus = 0;
+  if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       per_cu <= 0 || cus <= 0) {
     (void)hipGetLastError();
@@ -181,7 +192,7 @@ inline int resident_waves(const void *kernel, int fallback_per_cu, int *cache) {
     cus = sdk::kNumCUs;
   }
   w = per_cu * cus < sdk::kMaxWaves ? per_cu * cus : sdk::kMaxWaves;
-  __atomic_store_n(cache, w, __ATOMIC_RELAXED);  // a race stores the same value
+  if (slot) __atomic_store_n(slot, w, __ATOMIC_RELAXED);  // a race stores the same value
   return w;
 }
 

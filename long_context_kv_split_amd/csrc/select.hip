@@ -1427,9 +1427,9 @@ void launch_topk_reg(SnapParams &a, unsigned blocks, int64_t npre_cap, hipStream
 
 template <int D, int NB>
 void launch_snap_pair(SnapParams &a, hipStream_t st) {
-  static int cache = 0;  // resident waves of this instantiation, queried once
+  static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(snap_stats_kernel<D, NB>), 2 * kSimdsPerCU,
-                                   &cache);
+                                   cache);
   snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
   snap_stats_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   snap_votes_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
@@ -1495,7 +1495,9 @@ sd_status snapkv_impl(const sd_kv_cache *kv, const void *q_obs, int32_t batch, i
   SD_REQUIRE(pool_kernel >= 1 && (pool_kernel & 1) == 1, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
              SD_ERR_INVALID_ARG);
-  SD_REQUIRE(softmax_scale == softmax_scale, SD_ERR_INVALID_ARG);
+  // the scaled scores (and the stats pass's lazily rebased row maxima) are
+  // meaningful only for a finite positive scale
+  SD_REQUIRE(softmax_scale > 0.f && softmax_scale * kLog2e < __builtin_inff(), SD_ERR_INVALID_ARG);
   SD_REQUIRE(kv->dtype == SD_BF16, SD_ERR_UNSUPPORTED);
   const int G = num_q_heads / kv->num_kv_heads;
   SD_REQUIRE((int64_t)G * window <= 128, SD_ERR_UNSUPPORTED);
@@ -1581,8 +1583,8 @@ TopkLayout topk_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len) {
 
 template <int D>
 void launch_topk_attn_select(SnapParams &a, int B, hipStream_t st) {
-  static int cache = 0;  // resident waves of the scoring kernel, queried once
-  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(topk_scores_kernel<D>), 2 * kSimdsPerCU, &cache);
+  static int cache[sdh::kMaxDevices] = {};  // resident waves of the scoring kernel per device
+  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(topk_scores_kernel<D>), 2 * kSimdsPerCU, cache);
   snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
   topk_tau_kernel<D><<<(unsigned)(B * a.Hkv), kTauThreads, 0, st>>>(a);
   topk_scores_kernel<D><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);

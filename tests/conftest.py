@@ -9,3 +9,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    from tests import parity_log
+
+    rows = parity_log.lines()
+    if rows:
+        terminalreporter.section("parity statistics")
+        for r in rows:
+            terminalreporter.write_line(r)

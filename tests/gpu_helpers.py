@@ -18,7 +18,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import long_context_kv_split_amd as sd  # noqa: E402
+import oracle  # noqa: E402
 from long_context_kv_split_amd.binding import LIB_PATH  # noqa: E402
+from tests.parity_log import record  # noqa: E402
 
 BF16_ABS, BF16_NORM, BF16_LSE = 2e-2, 1e-2, 1e-4
 F32_NORM, F32_LSE = 1e-5, 1e-5
@@ -109,3 +111,68 @@ def unit_cache(kv_t, b, g):
     v = kv_t.v_pages[pages][:, g:g + 1].cpu()
     table = np.arange(npg, dtype=np.int64)[None, :]
     return k, v, table, np.array([L])
+
+
+def _band_probability(r, eps):
+    """Probability over v ~ U[0, 1) that v*Z lies within eps*Z of a boundary of
+    the CDF of weights r: the length of the union of the bands around 0, Z and
+    the upper end of every interval with mass, in units of Z."""
+    c = np.cumsum(r)
+    Z = c[-1]
+    if Z <= 0:
+        return 0.0
+    b = np.concatenate(([0.0], c[r > 0] / Z))
+    lo, hi = np.clip(b - eps, 0.0, 1.0), np.clip(b + eps, 0.0, 1.0)
+    prev = np.maximum.accumulate(np.concatenate(([0.0], hi[:-1])))
+    return float(np.clip(hi - np.maximum(lo, prev), 0.0, None).sum())
+
+
+def expected_draw_flags(zt, zd, n_ref, temperature=1.0, eps=1e-6):
+    """Expected number of sequences whose emitted-token draw falls in the flag
+    band, from each sequence's drawn weights (residual at n, or the target row
+    for the bonus): sum over sequences of the band probability."""
+    zt, zd = oracle.f64(zt), oracle.f64(zd)
+    gamma = zt.shape[1] - 1
+    tot = 0.0
+    for b, n in enumerate(n_ref):
+        p = oracle.softmax(zt[b, n], temperature)
+        r = np.maximum(0.0, p - oracle.softmax(zd[b, n], temperature)) if n < gamma else p
+        tot += _band_probability(r if r.sum() > 0 else p, eps)
+    return tot
+
+
+def check_accept(label, n, out, zt, zd, x, ua, us, temperature=1.0, planted=False):
+    """Acceptance parity for every sequence of a batch.
+
+    Unflagged sequences must match the oracle exactly. A flagged sequence (a
+    uniform within 1e-6 of a decision threshold) must return one of the
+    results the oracle lists as correct for it (accept_outcomes: either side
+    of an accept test in the band, the prefix unchanged, and a draw whose CDF
+    interval meets the band around v*Z); sequences with exactly one correct
+    result must return it. The flagged count must stay within 5 standard
+    deviations of its expectation from the draws' band probabilities (unless
+    the uniforms were planted next to thresholds on purpose). Returns the counts, also recorded for the terminal summary."""
+    n = np.asarray(n)
+    out = np.asarray(out)
+    n_ref, out_ref, flagged = oracle.spec_accept(zt, zd, x, ua, us, temperature=temperature)
+    valid, ambiguous = oracle.accept_valid(zt, zd, x, ua, us, n, out, temperature=temperature)
+    exact = (n == n_ref) & (out == out_ref).all(axis=1)
+    B = int(n.shape[0])
+    expect = expected_draw_flags(zt, zd, n_ref, temperature)
+    stats = dict(batch=B, flagged=int(flagged.sum()), ambiguous=int(ambiguous.sum()),
+                 exact=int(exact.sum()), flagged_exact=int((exact & flagged).sum()),
+                 flagged_other_valid=int((valid & ~exact).sum()), invalid=int((~valid).sum()),
+                 expected_flagged=round(expect, 2), mean_accepted=float(n.mean()))
+    msg = f"{label}: {stats}"
+    bad = np.nonzero(~exact & ~flagged)[0]
+    assert bad.size == 0, f"{msg}; unflagged mismatch at {bad[:8]}: gpu n {n[bad[:8]]} " \
+        f"ref {n_ref[bad[:8]]}, gpu {out[bad[:4]]} ref {out_ref[bad[:4]]}"
+    bad = np.nonzero(~valid)[0]
+    assert bad.size == 0, f"{msg}; flagged sequences with a result outside the band at {bad[:8]}: " \
+        f"gpu {out[bad[:4]]} ref {out_ref[bad[:4]]}"
+    assert (exact | ambiguous).all(), msg
+    cap = expect + 5.0 * np.sqrt(expect) + 3.0 + 0.002 * B
+    assert planted or flagged.sum() <= cap, f"{msg}; more flagged sequences than the band allows ({cap:.1f})"
+    record(label, **stats)
+    say(msg)
+    return stats

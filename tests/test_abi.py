@@ -98,6 +98,10 @@ WS = ctypes.c_void_p(0x6000)
     ({}, dict(ws=None), sd.SD_ERR_WORKSPACE),
     ({}, dict(ws_bytes=1), sd.SD_ERR_WORKSPACE),
     ({}, dict(scale=float("nan")), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=float("inf")), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=0.0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=-0.125), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=3e38), sd.SD_ERR_INVALID_ARG),     # scale * log2(e) overflows
     # batch * ceil(max_len / 16) steps would overflow the schedule's int32 prefix sums
     ({"max_pages": 4096}, dict(batch=1 << 20, max_len=1 << 16), sd.SD_ERR_UNSUPPORTED),
 ])
@@ -152,13 +156,18 @@ def test_streaming_rejects_invalid_arguments(L, args, want):
     ({"dtype": binding.SD_F32}, {}, sd.SD_ERR_UNSUPPORTED),
     ({}, dict(ws_bytes=16), sd.SD_ERR_WORKSPACE),
     ({}, dict(max_len=1000), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=float("nan")), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=float("inf")), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=0.0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=-1.0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(scale=3e38), sd.SD_ERR_INVALID_ARG),
 ])
 def test_snapkv_rejects_invalid_arguments(L, over, args, want):
     kv = _kv(**over)
-    a = dict(window=8, pool=7, budget=32, max_len=64, ws_bytes=1 << 30)
+    a = dict(window=8, pool=7, budget=32, max_len=64, ws_bytes=1 << 30, scale=1.0)
     a.update(args)
     st = L.sd_snapkv_select(ctypes.byref(kv), FAKE, 2, a["window"], 8, a["pool"], a["budget"],
-                            a["max_len"], 1.0, FAKE, FAKE, WS, a["ws_bytes"], None)
+                            a["max_len"], a["scale"], FAKE, FAKE, WS, a["ws_bytes"], None)
     assert st == want
 
 

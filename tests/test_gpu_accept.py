@@ -2,7 +2,11 @@
 
 n_accepted and out_tokens must match exactly on every sequence the oracle does
 not flag (a uniform within 1e-6 of a decision threshold; see the oracle's
-accept module). Flagged sequences are counted and must stay rare.
+accept module). Every flagged sequence must return one of the results the
+oracle lists as correct for it (oracle.accept_outcomes), and the flagged count
+must stay near its expectation (tests/gpu_helpers.check_accept). The
+hand-worked fixtures, flagged ones included, must return one of their
+hand-derived correct results.
 """
 import json
 import os
@@ -14,7 +18,7 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import dyadic_uniforms, gumbel_tokens, logits
-from tests.gpu_helpers import dirty_workspace, ensure_lib, say
+from tests.gpu_helpers import check_accept, dirty_workspace, ensure_lib, say
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "accept_cases.json")
@@ -37,33 +41,24 @@ def run_accept(zt, zd, x, ua, us, temperature=1.0):
     return n.cpu().numpy(), out.cpu().numpy()
 
 
-def compare(n, out, n_ref, out_ref, flagged, vocab=None):
-    """Exact on unflagged sequences. The flag band (a uniform within 1e-6 of a
-    threshold) is hit by the sampling step with probability about 2e-6 per
-    vocabulary entry carrying residual mass, so its rate grows with vocab."""
-    max_flag_frac = 0.01 + (4e-6 * vocab if vocab else 0.0)
-    ok = ~flagged
-    bad = np.nonzero((n != n_ref) & ok)[0]
-    assert bad.size == 0, f"n_accepted differs at {bad[:10]}: gpu {n[bad[:10]]} ref {n_ref[bad[:10]]}"
-    bad = np.nonzero((out != out_ref).any(axis=1) & ok)[0]
-    assert bad.size == 0, f"tokens differ at {bad[:10]}: gpu {out[bad[:5]]} ref {out_ref[bad[:5]]}"
-    assert flagged.mean() <= max_flag_frac, flagged.mean()
-    return int(flagged.sum())
-
-
 def test_golden_cases_on_gpu():
+    """Every hand-worked case, flagged ones included: the result must be one of
+    the case's hand-derived correct results. The cases with one correct result
+    (zero-mass tokens never drawn, even at v = 0; p(x) = 0 rejects at u = 0)
+    therefore must match it exactly."""
     cases = json.load(open(GOLDEN))["cases"]
     for c in cases:
-        if c.get("flagged"):
-            continue
         zt = torch.tensor(c["target_logits"], dtype=torch.float32, device="cuda")[None]
         zd = torch.tensor(c["draft_logits"], dtype=torch.float32, device="cuda")[None]
         x = torch.tensor(c["x"], dtype=torch.int32, device="cuda")[None]
         ua = torch.tensor(c["u_accept"], dtype=torch.float32, device="cuda")[None]
         us = torch.tensor(c["u_sample"], dtype=torch.float32, device="cuda")[None]
         n, out = run_accept(zt, zd, x, ua, us)
-        assert n[0] == c["n"], c["name"]
-        assert out[0].tolist() == c["out"], c["name"]
+        got = (int(n[0]), tuple(int(t) for t in out[0]))
+        allowed = {(m, tuple(o)) for m, o in c["outcomes"]}
+        assert got in allowed, (c["name"], got, allowed)
+        if len(allowed) == 1:
+            assert got == (c["n"], tuple(c["out"])), c["name"]
 
 
 @pytest.mark.parametrize("B,gamma,V,std,noise,temp", [
@@ -87,10 +82,7 @@ def test_accept_parity(B, gamma, V, std, noise, temp):
     ua = dyadic_uniforms(seed, 11, (B, gamma), "cuda")
     us = dyadic_uniforms(seed, 12, (B, gamma + 1), "cuda")
     n, out = run_accept(zt, zd, x, ua, us, temp)
-    n_ref, out_ref, flagged = oracle.spec_accept(zt, zd, x, ua, us, temperature=temp)
-    nf = compare(n, out, n_ref, out_ref, flagged, V)
-    fl_match = ((n == n_ref) & (out == out_ref).all(axis=1))[flagged].mean() if nf else 1.0
-    say(f"  mean accepted {n.mean():.3f}, flagged {nf} (of which matching {fl_match:.2f})")
+    check_accept(f"accept B={B} gamma={gamma} V={V} noise={noise} T={temp}", n, out, zt, zd, x, ua, us, temp)
 
 
 def test_identical_and_disjoint_distributions():
@@ -102,8 +94,7 @@ def test_identical_and_disjoint_distributions():
     us = dyadic_uniforms(5, 12, (B, gamma + 1), "cuda")
     n, out = run_accept(zt, zd, x, ua, us)
     assert (n == gamma).all()
-    n_ref, out_ref, flagged = oracle.spec_accept(zt, zd, x, ua, us)
-    compare(n, out, n_ref, out_ref, flagged)
+    check_accept("accept q == p", n, out, zt, zd, x, ua, us)
     # disjoint supports: draft mass only on the upper half of the vocabulary
     zt2 = zt.clone()
     zt2[:, :, V // 2:] = -1e30
@@ -112,8 +103,48 @@ def test_identical_and_disjoint_distributions():
     x2 = gumbel_tokens(6, zd2)
     n, out = run_accept(zt2, zd2, x2, ua, us)
     assert (n == 0).all() and (out[:, 0] < V // 2).all() and (out[:, 1:] == -1).all()
-    n_ref, out_ref, flagged = oracle.spec_accept(zt2, zd2, x2, ua, us)
-    compare(n, out, n_ref, out_ref, flagged)
+    check_accept("accept disjoint supports", n, out, zt2, zd2, x2, ua, us)
+
+
+def test_uniforms_planted_next_to_thresholds():
+    """Every sequence has an accept uniform within 0.5e-6 of p/q of its draft
+    token and a sampling uniform within 0.5e-6 of a CDF boundary of the weights
+    it draws from (the float32 uniforms both sides read). Almost every sequence
+    is flagged; each must return one of its correct results, and where a
+    sequence has exactly one (p(x) = 0 at u = 0 among them) it must be that."""
+    rng = np.random.default_rng(101)
+    B, V, gamma = 512, 3000, 3
+    zt = (rng.standard_normal((B, gamma + 1, V)) * 1.5).astype(np.float32)
+    zd = (zt[:, :gamma] + rng.standard_normal((B, gamma, V)) * 0.7).astype(np.float32)
+    zt[:16, 0, :64] = -1e30                  # p_0(x) = 0 exactly for tokens < 64 ...
+    x = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    x[:16, 0] = rng.integers(0, 64, 16)      # ... drafted there, with u = 0: must reject
+    ua = rng.random((B, gamma))
+    us = rng.random((B, gamma + 1))
+    for b in range(B):
+        p = oracle.softmax(zt[b])
+        q = oracle.softmax(zd[b])
+        i = int(rng.integers(0, gamma))
+        ratio = p[i, x[b, i]] / q[i, x[b, i]]
+        if ratio < 0.999:
+            ua[b, i] = ratio + rng.uniform(-0.5e-6, 0.5e-6)
+    ua[:16, 0] = 0.0
+    ua = np.float32(np.clip(ua, 0.0, 1.0 - 2 ** -24))
+    n0, _, _ = oracle.spec_accept(zt, zd, x, ua, us)
+    for b in range(B):
+        n = int(n0[b])
+        p = oracle.softmax(zt[b, n])
+        r = np.maximum(0.0, p - oracle.softmax(zd[b, n])) if n < gamma else p
+        c = np.cumsum(r) / r.sum()
+        t = int(rng.integers(0, V - 1))
+        if 1e-3 < c[t] < 0.999:
+            us[b, n] = c[t] + rng.uniform(-0.5e-6, 0.5e-6)
+    us = np.float32(np.clip(us, 0.0, 1.0 - 2 ** -24))
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (zt, zd, x, ua, us)]
+    n, out = run_accept(*dev)
+    stats = check_accept("accept uniforms next to thresholds", n, out, zt, zd, x, ua, us, planted=True)
+    assert stats["flagged"] > B // 2
+    assert (n[:16] == 0).all()
 
 
 def test_accept_is_deterministic_and_reuses_workspace():

@@ -15,7 +15,8 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries, workload_lens
-from tests.gpu_helpers import compare_attn, dirty_workspace, ensure_lib, say, unit_cache
+from tests.gpu_helpers import check_accept, compare_attn, dirty_workspace, ensure_lib, say, unit_cache
+from tests.parity_log import record
 
 pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
@@ -27,13 +28,15 @@ def _lib():
     torch.cuda.set_device(0)
 
 
-def sample_units(lens, Hkv, seed, n_random=3):
+def sample_sequences(lens, Hkv, seed, n_seq=8):
+    """Every KV head of n_seq sequences: the first, the last, the shortest, the
+    longest and random others (n_seq * Hkv units)."""
     B = len(lens)
     rng = np.random.default_rng(seed)
-    units = {(0, 0), (B - 1, Hkv - 1), (int(np.argmin(lens)), 1 % Hkv), (int(np.argmax(lens)), 2 % Hkv)}
-    for _ in range(n_random):
-        units.add((int(rng.integers(B)), int(rng.integers(Hkv))))
-    return sorted(units)
+    seqs = {0, B - 1, int(np.argmin(lens)), int(np.argmax(lens))}
+    while len(seqs) < min(n_seq, B):
+        seqs.add(int(rng.integers(B)))
+    return [(b, g) for b in sorted(seqs) for g in range(Hkv)]
 
 
 def build(name):
@@ -45,14 +48,17 @@ def build(name):
     return w, lens, kv_t, q
 
 
-def check_units_verify(w, lens, kv_t, q, out, lse, units):
+def check_units_verify(w, lens, kv_t, q, out, lse, units, label):
     G = w.num_q_heads // w.num_kv_heads
+    worst = np.zeros(3)
     for b, g in units:
         k, v, table, L = unit_cache(kv_t, b, g)
         heads = slice(g * G, (g + 1) * G)
         o_ref, l_ref = oracle.verify_attn(q[b:b + 1, :, heads].cpu(), k, v, table, L, 1.0)
         err = compare_attn(out[b:b + 1, :, heads], lse[b:b + 1, :, heads], o_ref, l_ref, BF16)
-        say(f"  unit b={b} g={g} L={lens[b]}: max|dO|={err[0]:.2e} norm={err[1]:.2e} lse={err[2]:.2e}")
+        worst = np.maximum(worst, err)
+    record(label, units=len(units), max_abs=float(worst[0]), max_norm=float(worst[1]), max_lse=float(worst[2]))
+    say(f"  {label}: {len(units)} units, worst max|dO|={worst[0]:.2e} norm={worst[1]:.2e} lse={worst[2]:.2e}")
 
 
 @pytest.mark.parametrize("name", ["llama8b-b32-l8k", "llama8b-b128-l32k-snapkv", "ragged-b256-l4k-32k",
@@ -70,7 +76,8 @@ def test_verify_full_size_sampled(name):
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     # |o| is a convex combination of V rows: bounded by the largest |V| entry
     assert out.float().abs().max() <= kv_t.v_pages.float().nan_to_num(0).abs().max() + 1e-2
-    check_units_verify(w, lens, kv_t, q, out, lse, sample_units(lens, w.num_kv_heads, w.seed))
+    check_units_verify(w, lens, kv_t, q, out, lse, sample_sequences(lens, w.num_kv_heads, w.seed),
+                       f"verify {name} (full size)")
 
 
 @pytest.mark.parametrize("name", ["llama8b-b32-l8k", "ragged-b256-l4k-32k"])
@@ -93,13 +100,17 @@ def test_streaming_draft_full_size_sampled(name):
     assert (idx.cpu().numpy() == idx_ref).all() and (sel.cpu().numpy() == sel_ref).all()
     assert torch.isfinite(out).all()
     G = w.num_q_heads // w.num_kv_heads
-    for b, g in sample_units(lens, w.num_kv_heads, w.seed + 1):
+    units = sample_sequences(lens, w.num_kv_heads, w.seed + 1)
+    worst = np.zeros(3)
+    for b, g in units:
         k, v, table, L = unit_cache(kv_t, b, g)
         heads = slice(g * G, (g + 1) * G)
         o_ref, l_ref = oracle.sparse_attn(qd[b:b + 1, :, heads].cpu(), k, v, table, idx_ref[b:b + 1],
                                           sel_ref[b:b + 1], 1.0)
         err = compare_attn(out[b:b + 1, :, heads], lse[b:b + 1, :, heads], o_ref, l_ref, BF16)
-        say(f"  unit b={b} g={g}: max|dO|={err[0]:.2e} norm={err[1]:.2e}")
+        worst = np.maximum(worst, err)
+    record(f"StreamingLLM draft {name} (full size)", units=len(units), max_abs=float(worst[0]),
+           max_norm=float(worst[1]), max_lse=float(worst[2]))
 
 
 def test_snapkv_select_and_draft_full_size_sampled():
@@ -128,7 +139,9 @@ def test_snapkv_select_and_draft_full_size_sampled():
     assert (np.diff(idx_np, axis=2) > 0).all() and idx_np.min() >= 0 and idx_np.max() < L
     assert (idx_np[:, :, -w.window:] == np.arange(L - w.window, L)).all()
     near, compared = 0, 0
-    for b, g in sample_units(lens, Hkv, w.seed + 2, n_random=2):
+    worst = np.zeros(3)
+    units = sample_sequences(lens, Hkv, w.seed + 2)
+    for b, g in units:
         k, v, table, Lb = unit_cache(kv_t, b, g)
         heads = slice(g * G, (g + 1) * G)
         idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs[b:b + 1, :, heads].cpu(), k, table, Lb, w.window,
@@ -140,13 +153,18 @@ def test_snapkv_select_and_draft_full_size_sampled():
             for t in set(got.tolist()) ^ set(ref.tolist()):
                 assert abs(pv[t] - thr) <= 1e-5 * thr, (b, g, t, pv[t], thr)
             near += 1
-            say(f"  unit b={b} g={g}: near-tie selection difference (flagged)")
             continue
         o_ref, l_ref = oracle.sparse_attn(qd[b:b + 1, :, heads].cpu(), k, v, table, idx_ref, sel_ref, 1.0)
         err = compare_attn(out[b:b + 1, :, heads], lse[b:b + 1, :, heads], o_ref, l_ref, BF16)
+        worst = np.maximum(worst, err)
         compared += 1
-        say(f"  unit b={b} g={g}: selection exact; draft max|dO|={err[0]:.2e} norm={err[1]:.2e}")
-    assert compared >= 3 and near <= 2
+    stats = dict(units=len(units), selection_exact=compared, near_tie=near, draft_max_abs=float(worst[0]),
+                 draft_max_norm=float(worst[1]), draft_max_lse=float(worst[2]))
+    record("snapkv select + draft B=128 L=32k (full size)", **stats)
+    say(f"  {stats}")
+    # fp32 vs fp64 ordering of pooled votes within 1e-5 of the cut: about one
+    # unit in a hundred is expected at this shape
+    assert len(units) >= 64 and near <= 3, stats
 
 
 def test_accept_bench_shape():
@@ -162,9 +180,5 @@ def test_accept_bench_shape():
     ws = dirty_workspace(sd.sd_spec_accept_workspace_size(B, gamma, V), "cuda")
     sd.sd_spec_accept(zt, zd, x, ua, us, gamma, V, 1.0, n, toks, ws)
     torch.cuda.synchronize()
-    n_ref, t_ref, flagged = oracle.spec_accept(zt, zd, x, ua, us)
-    ok = ~flagged
-    assert (n.cpu().numpy()[ok] == n_ref[ok]).all()
-    assert (toks.cpu().numpy()[ok] == t_ref[ok]).all()
-    say(f"  mean accepted {n.float().mean().item():.3f} (closed form for draft noise 0.5: 0.803 per position), "
-        f"flagged {int(flagged.sum())}")
+    check_accept("accept B=128 gamma=4 V=128256 (bench shape)", n.cpu().numpy(), toks.cpu().numpy(),
+                 zt, zd, x, ua, us)

@@ -12,7 +12,7 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import dyadic_uniforms, logits, paged_kv, queries
-from tests.gpu_helpers import compare_attn, dirty_workspace, ensure_lib, say
+from tests.gpu_helpers import check_accept, compare_attn, dirty_workspace, ensure_lib, say
 
 pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
@@ -156,7 +156,7 @@ def test_round_end_to_end_matches_oracle_chain():
     ws_s = dirty_workspace(sd.sd_spec_accept_workspace_size(B, 0, V), "cuda")
     n0 = torch.empty((B,), dtype=torch.int32, device="cuda")
     drafted = torch.empty((B, gamma), dtype=torch.int32, device="cuda")
-    flagged_any = np.zeros(B, dtype=bool)
+    flagged_any = False
     for i in range(gamma):
         k_i, v_i = kv_new[i]
         sd.sd_kv_append(kv, k_i, v_i, 1)
@@ -174,13 +174,12 @@ def test_round_end_to_end_matches_oracle_chain():
         tok = torch.empty((B, 1), dtype=torch.int32, device="cuda")
         sd.sd_spec_accept(zd[:, i:i + 1].contiguous(), None, None, None, u_draw[:, i:i + 1].contiguous(), 0, V,
                           1.0, n0, tok, ws_s)
-        _, t_ref, fl = oracle.spec_accept(zd[:, i:i + 1].cpu(), np.zeros((B, 0, V)), np.zeros((B, 0), int),
-                                          np.zeros((B, 0)), u_draw[:, i:i + 1].cpu())
         torch.cuda.synchronize()
-        ok = ~fl
-        assert (tok.cpu().numpy()[ok, 0] == t_ref[ok, 0]).all()
-        flagged_any |= fl
-        # a flagged draw may differ; the chain continues with the GPU's token on both sides
+        st = check_accept(f"round draft-token draw {i}", np.zeros(B, dtype=np.int32), tok.cpu().numpy(),
+                          zd[:, i:i + 1].cpu(), np.zeros((B, 0, V)), np.zeros((B, 0), int),
+                          np.zeros((B, 0)), u_draw[:, i:i + 1].cpu())
+        flagged_any |= st["flagged"] > 0
+        # a flagged draw may differ within its band; the chain continues with the GPU's token on both sides
         drafted[:, i] = tok[:, 0]
     # verification: the last draft's K/V, then gamma + 1 causal queries over the full cache
     k_g, v_g = kv_new[gamma]
@@ -201,15 +200,14 @@ def test_round_end_to_end_matches_oracle_chain():
     n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
     toks = torch.empty((B, gamma + 1), dtype=torch.int32, device="cuda")
     sd.sd_spec_accept(zt, zd, drafted, u_acc, u_smp, gamma, V, 1.0, n_acc, toks, ws_a)
-    n_ref, t_ref, fl = oracle.spec_accept(zt.cpu(), zd.cpu(), drafted.cpu(), u_acc.cpu(), u_smp.cpu())
     torch.cuda.synchronize()
-    ok = ~fl
-    assert (n_acc.cpu().numpy()[ok] == n_ref[ok]).all() and (toks.cpu().numpy()[ok] == t_ref[ok]).all()
+    st = check_accept("round acceptance", n_acc.cpu().numpy(), toks.cpu().numpy(), zt.cpu(), zd.cpu(),
+                      drafted.cpu(), u_acc.cpu(), u_smp.cpu())
     sd.sd_kv_advance(kv_lens, n_acc, -gamma)
     lens = oracle.kv_advance(lens, -gamma, n_acc.cpu().numpy())
     torch.cuda.synchronize()
     assert kv_lens.cpu().tolist() == list(lens)
-    say(f"  accepted {n_acc.cpu().tolist()}, flagged {int(fl.sum())} + draws {int(flagged_any.sum())}")
+    say(f"  accepted {n_acc.cpu().tolist()}, flagged {st['flagged']} + draws {int(flagged_any)}")
 
 
 def test_draft_steps_graph_replay_matches_eager():

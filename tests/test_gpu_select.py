@@ -17,6 +17,7 @@ import long_context_kv_split_amd as sd
 import oracle
 from synth import paged_kv, queries
 from tests.gpu_helpers import dirty_workspace, ensure_lib, say
+from tests.parity_log import record
 
 pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
@@ -42,14 +43,14 @@ def test_streaming_select_parity(sink, recent):
     assert (idx.cpu().numpy() == idx_ref).all()
 
 
-def run_snapkv(kv_t, q_obs, window, Hq, pool, budget, max_kv_len=None):
+def run_snapkv(kv_t, q_obs, window, Hq, pool, budget, max_kv_len=None, scale=1.0):
     kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
     B = kv.batch
     mk = max(1, kv_t.max_kv_len) if max_kv_len is None else max_kv_len
     idx = torch.full((B, kv.num_kv_heads, budget), 7, dtype=torch.int32, device="cuda")
     sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
     ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, window, Hq, kv.num_kv_heads, mk), "cuda")
-    sd.sd_snapkv_select(kv, q_obs, window, Hq, pool, budget, mk, 1.0, idx, sel, ws)
+    sd.sd_snapkv_select(kv, q_obs, window, Hq, pool, budget, mk, scale, idx, sel, ws)
     torch.cuda.synchronize()
     return idx, sel
 
@@ -116,7 +117,38 @@ def test_snapkv_select_parity(case):
                                                     W, pool, budget, 1.0, return_pooled=True)
     near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
     say(f"  near-tie (flagged) units: {near}")
+    record(f"snapkv {name}", units=len(lens) * Hkv, near_tie=near)
     assert near <= max(1, len(lens) * Hkv // 8)
+
+
+SCALE_CASES = [
+    # name, q_obs scale folded in, softmax_scale passed
+    ("unscaled-q-inv-sqrt-d", 1.0, 128 ** -0.5),
+    ("scaled-q-0.37", 128 ** -0.5, 0.37),
+    ("scaled-q-2.5", 128 ** -0.5, 2.5),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
+def test_snapkv_softmax_scale(case):
+    """The scale enters both passes (row statistics and the normalised votes):
+    the standard 1/sqrt(d) applied by the call to unscaled window queries, and
+    two other scales. Each case is checked to be sensitive first: the oracle's
+    selection with the scale dropped differs from the one with it."""
+    name, q_scale, scale = case
+    Hq, Hkv, d, lens, W, pool, budget = 32, 8, 128, [3000, 2100, 4500], 32, 7, 256
+    say(f"snapkv scale {name}: q scale {q_scale:.4f}, softmax_scale {scale}")
+    kv_t = paged_kv(303, lens, Hkv, d, BF16, "cuda", shuffle=True, spike_frac=0.10)
+    q_obs = queries(303, 4, (len(lens), W, Hq, d), BF16, "cuda", scale=q_scale)
+    idx, sel = run_snapkv(kv_t, q_obs, W, Hq, pool, budget, scale=scale)
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    W, pool, budget, scale, return_pooled=True)
+    idx_noscale, _ = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens, W, pool,
+                                          budget, 1.0)
+    assert (idx_noscale != idx_ref).any(axis=2).sum() >= len(lens) * Hkv // 2
+    near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
+    record(f"snapkv scale {name}", units=len(lens) * Hkv, near_tie=near)
+    assert near <= 1
 
 
 @pytest.mark.parametrize("classes", [1, 5, 64])
