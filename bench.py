@@ -9,11 +9,15 @@ Llama-3.1's 128256-token vocabulary with draft logits = target + N(0, 0.5).
 One step = one pass of every kernel of the hot path, in call order:
   sd_snapkv_select, sd_streaming_select (64 + 448), gamma x sd_draft_attn_sparse
   (n_q = 1 over the SnapKV set), sd_verify_attn (n_q = gamma + 1), sd_spec_accept.
-`value` = draft+verify KV token reads per step / step time (selection counted
-as overhead). Per-call HIP event times, verify GB/s against the 8 TB/s HBM
-peak and against the attainable read bandwidth (the library's streaming-read
-probe over the 8.6 GB K pool), and the CPU oracle's rate on a bounded sample
-are reported beside it.
+`value` = draft+verify KV token reads of one round, B (L + gamma K), over
+t_verify + gamma t_draft, both from HIP events around those calls inside the
+timed steps (MagicDec notes §4.1: a round costs gamma draft steps plus one
+verification; the SnapKV set is built once at prefill, Appendix A.1, so its
+selection is reported apart, as is acceptance). `step_kv_tokens_per_s` charges
+the same tokens to the whole step. Per-call HIP event times, verify GB/s
+against the 8 TB/s HBM peak and against the attainable read bandwidth (the
+library's streaming-read probe over the 8.6 GB K pool), and the CPU oracle's
+rates on bounded samples are reported beside it.
 After that, `round` times one whole self-speculative round at the same shape
 (draft steps with KV append and sampling, verify, accept, roll back), eager and
 replayed from a HIP graph, and dense decode as the attention-only target step;
@@ -215,6 +219,27 @@ def measured_traffic():
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
+def profiled_verify():
+    """The verify call's kernels as the committed kernel trace of this bench
+    command measured them (average duration per launch, and the roofline
+    fraction of the whole call from their sum), or None if the attention
+    sources changed since the trace was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "verify_attn_b128_l32k_kernel_trace.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    call_ms = sum(k["avg_ms"] for k in rec["kernels"])
+    return {"kernels": rec["kernels"], "call_ms": call_ms, "command": rec["command"],
+            "frac": rec["algorithmic_bytes_per_launch"] / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
 def unit_cache(kv_t, b, g):
     """One (sequence b, KV head g) of the paged cache copied to the host, with
     its pages in table order and an identity page table."""
@@ -228,23 +253,27 @@ def unit_cache(kv_t, b, g):
     return k, v, np.arange(npg, dtype=np.int64)[None, :], np.array([L])
 
 
-def cpu_baseline(wl, n_units):
-    """Time the oracle (verify + gamma sparse drafts) on a bounded sample of
-    (sequence, KV head) units of the same workload; returns KV tokens/s."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(wl, n_units, n_select_units=8, n_accept_seqs=16):
+    """Time the oracle on bounded samples of the bench workload: verify + gamma
+    sparse drafts on (sequence, KV head) units (the metric's unit, KV tokens/s),
+    SnapKV selection on a few units and acceptance on a few sequences (each in
+    its own unit, beside it). Host copies are made before each clock starts."""
     import numpy as np
-    import torch
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas_threads = _blas_threads()
     cores = len(os.sched_getaffinity(0))
     G = wl.Hq // wl.Hkv
     units = [((7 * i) % wl.B, (3 * i) % wl.Hkv) for i in range(n_units)]
-    # host copies are made before the clock starts
     prepared = []
     idx = wl.idx.cpu().numpy()
     sel = wl.sel.cpu().numpy()
@@ -263,13 +292,64 @@ def cpu_baseline(wl, n_units):
             oracle.sparse_attn(x, k, v, table, ix, sl, 1.0)
             toks += int(sl[0])
     dt = time.perf_counter() - t0
-    # tokens here are per (sequence, KV head) unit; a KV token of the metric
+
+    # SnapKV selection (window scores, pooling, top-K) on a few units
+    sel_units = [((11 * i + 5) % wl.B, (5 * i + 1) % wl.Hkv) for i in range(n_select_units)]
+    sel_prep = []
+    for b, g in sel_units:
+        k, v, table, lens = unit_cache(wl.kv_t, b, g)
+        sel_prep.append((wl.q_obs[b:b + 1, :, g * G:(g + 1) * G].cpu(), k, table, lens))
+    w = wl.w
+    t1 = time.perf_counter()
+    for qo, k, table, lens in sel_prep:
+        oracle.snapkv_select(qo, k, table, lens, w.window, w.pool_kernel, w.budget, 1.0)
+    dt_sel = time.perf_counter() - t1
+    sel_tokens = sum(int(p[3][0]) for p in sel_prep)
+
+    # acceptance on a few sequences of the 128256-token vocabulary
+    zt = wl.zt[:n_accept_seqs].cpu()
+    zd = wl.zd[:n_accept_seqs].cpu()
+    x, ua, us = (t[:n_accept_seqs].cpu() for t in (wl.x, wl.ua, wl.us))
+    t2 = time.perf_counter()
+    oracle.spec_accept(zt, zd, x, ua, us)
+    dt_acc = time.perf_counter() - t2
+    acc_bytes = (zt.numel() + zd.numel()) * 4
+
+    # tokens above are per (sequence, KV head) unit; a KV token of the metric
     # spans all KV heads, so divide by Hkv to use the same unit.
     return {"value": toks / wl.Hkv / dt, "unit": "KV tokens/s", "cores": int(min(cores, max(blas_threads, 1))),
             "host_cores_available": cores, "blas_threads": blas_threads, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{n_units} (sequence, KV head) units of the same workload: fp64 verify over "
-                      f"{wl.L} tokens + {wl.gamma} sparse drafts over {wl.w.budget} SnapKV tokens each"}
+                      f"{wl.L} tokens + {wl.gamma} sparse drafts over {wl.w.budget} SnapKV tokens each",
+            "per_op": {
+                "snapkv_select": {"units": n_select_units, "seconds": round(dt_sel, 2),
+                                  "context_tokens_per_s": sel_tokens / dt_sel,
+                                  "K_GBps": sel_tokens * wl.d * 2 / dt_sel / 1e9},
+                "spec_accept": {"sequences": n_accept_seqs, "vocab": wl.V, "seconds": round(dt_acc, 3),
+                                "sequences_per_s": n_accept_seqs / dt_acc,
+                                "logits_GBps": acc_bytes / dt_acc / 1e9}}}
+
+
+def oracle_verify_rate(kv_t, q, G, units):
+    """The oracle's verify rate (KV tokens/s over all KV heads, and GB/s) on a
+    few (sequence, KV head) units of a workload."""
+    import oracle
+
+    prep = []
+    for b, g in units:
+        k, v, table, lens = unit_cache(kv_t, b, g)
+        prep.append((q[b:b + 1, :, g * G:(g + 1) * G].cpu(), k, v, table, lens))
+    t0 = time.perf_counter()
+    toks = 0
+    for qq, k, v, table, lens in prep:
+        oracle.verify_attn(qq, k, v, table, lens, 1.0)
+        toks += int(lens[0])
+    dt = time.perf_counter() - t0
+    Hkv = kv_t.k_pages.shape[1]
+    d = kv_t.k_pages.shape[3]
+    return {"units": len(units), "seconds": round(dt, 3), "kv_tokens_per_s": toks / Hkv / dt,
+            "GBps": toks * d * 2 * 2 / dt / 1e9}
 
 
 def measure_round(wl, reps=10):
@@ -534,14 +614,15 @@ def measure_hetero(reps=5):
             "draft_GBps": d_bytes / (t_dr * 1e-3) / 1e9}
 
 
-def measure_configs(reps=10):
+def measure_configs(reps=10, oracle_units=0):
     """The other workloads' timed ops, beside the headline: verify at every
     shape, the StreamingLLM-512 draft step at the Llama-8B 8k and ragged
     shapes, acceptance over the 128256-token vocabulary at the Llama-70B
     shape. Each op is timed warm (back to back, mean of `reps`) and cold
     (median of `reps` single calls, each after writing a 1 GiB buffer that
     evicts the 256 MB last-level cache and L2); GB/s are on algorithmic bytes
-    (K/V rows read, logits read)."""
+    (K/V rows read, logits read). With oracle_units > 0 the oracle's verify
+    rate on that many (sequence, KV head) units is reported per workload."""
     import torch
 
     import long_context_kv_split_amd as sd
@@ -593,6 +674,10 @@ def measure_configs(reps=10):
         rec = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "n_q": n_q, "sum_context": sum(lens),
                "pages": "shuffled" if w.shuffle else "in order",
                "verify": timing(lambda: sd.sd_verify_attn(kv, q, n_q, Hq, L, 1.0, o, None, ws), kv_bytes)}
+        if oracle_units:
+            G = Hq // Hkv
+            units = [((13 * i + 3) % B, (5 * i + 2) % Hkv) for i in range(oracle_units)]
+            rec["verify"]["oracle"] = oracle_verify_rate(kv_t, q, G, units)
         if w.draft == "streaming" and w.sink + w.recent > 0:
             cap = w.sink + w.recent
             idx = torch.empty((B, 1, cap), dtype=torch.int32, device="cuda")
@@ -679,8 +764,8 @@ def main():
     v_bytes = wl.verify_bytes()
     v_gbps = v_bytes / (avg["verify_ms"] * 1e-3) / 1e9
     step_tokens = wl.verify_tokens() + wl.draft_tokens()
-    value = step_tokens / (ms_step * 1e-3)
     round_ms = avg["verify_ms"] + wl.gamma * avg["draft_ms"]
+    value = step_tokens / (round_ms * 1e-3)
     draft_gbps = wl.B * wl.w.budget * KV_BYTES_PER_TOKEN / (avg["draft_ms"] * 1e-3) / 1e9
     # SnapKV reads every cached key twice (statistics pass, votes pass); acceptance
     # reads the target and draft logits once
@@ -693,10 +778,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n_units = args.cpu_sample_units or 96
+        n_units = args.cpu_sample_units or 64
         log(f"cpu baseline: oracle on {n_units} units ...")
         cpu = cpu_baseline(wl, n_units)
-        log(f"cpu baseline {cpu['value']:.3e} KV tokens/s in {cpu['seconds']} s")
+        log(f"cpu baseline {cpu['value']:.3e} KV tokens/s in {cpu['seconds']} s; select "
+            f"{cpu['per_op']['snapkv_select']['seconds']} s, accept {cpu['per_op']['spec_accept']['seconds']} s")
 
     rnd = None
     if not args.no_round:
@@ -728,7 +814,7 @@ def main():
 
     cfgs = None
     if not args.no_round:
-        cfgs = measure_configs()
+        cfgs = measure_configs(oracle_units=0 if args.no_cpu_baseline else 4)
 
     rec = {
         "metric": METRIC,
@@ -747,16 +833,22 @@ def main():
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d, "page_size": 16,
                    "draft": f"snapkv window={wl.w.window} pool={wl.w.pool_kernel} budget={wl.w.budget}",
                    "accept_vocab": wl.V, "parallelism": "single-gpu"},
+        "value_definition": "B (L + gamma K) / (t_verify + gamma t_draft), per-call HIP events inside the "
+                            "timed steps; SnapKV selection (once per prefill) and acceptance reported apart",
         "roofline": {"bound": "hbm", "kernel": "sd_verify_attn (split + combine)",
                      "achieved": v_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": v_gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "attainable": att["nontemporal_GBps"],
                      "frac_attainable": v_gbps / att["nontemporal_GBps"],
                      "algorithmic_bytes_per_launch": v_bytes,
-                     "avg_launch_ms": avg["verify_ms"]},
+                     "avg_launch_ms": avg["verify_ms"],
+                     "kernel_trace": profiled_verify()},
         "verify_kv_GBps": v_gbps,
         "verify_pct_hbm_peak": 100.0 * v_gbps / HBM_PEAK_GBPS,
-        "round_kv_tokens_per_s": step_tokens / (round_ms * 1e-3),
+        "round_kv_tokens_per_s": value,
+        "round_ms": round_ms,
+        "step_kv_tokens_per_s": step_tokens / (ms_step * 1e-3),
+        "snapkv_select_once_per_prefill_ms": avg["select_ms"],
         "draft_kv_GBps": draft_gbps,
         "snapkv_select_K_GBps": snap_gbps,
         "accept_logits_GBps": acc_gbps,
