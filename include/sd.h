@@ -280,6 +280,32 @@ sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
 size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab);
 
 /*
+ * Allocation-free acceptance, for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation. Same arguments and results as
+ * sd_spec_accept, bit for bit, without the workspace: the scratch comes from a
+ * fixed array of SD_SPEC_ACCEPT_SCRATCH_BYTES inside the library's device
+ * memory (one copy per GPU, held until the process ends; its device address
+ * is looked up once per device on the first call there). The call allocates
+ * nothing and needs no cleared memory (every scratch byte is written before
+ * it is read).
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or other host threads) race and may return
+ * wrong results; serialise them on one stream.
+ * stream must belong to the current device (else SD_ERR_INVALID_ARG).
+ * Limits: as sd_spec_accept, and sd_spec_accept_workspace_size(batch, gamma,
+ *   vocab) <= SD_SPEC_ACCEPT_SCRATCH_BYTES, else SD_ERR_UNSUPPORTED (about
+ *   1300 sequences at gamma = 4 over a 128256-token vocabulary).
+ */
+#define SD_SPEC_ACCEPT_SCRATCH_BYTES (4u << 20)
+
+sd_status sd_spec_accept_noalloc(const float *target_logits, const float *draft_logits,
+                                 const int32_t *draft_tokens, const float *u_accept,
+                                 const float *u_sample, int32_t batch, int32_t gamma, int32_t vocab,
+                                 float temperature, int32_t *n_accepted, int32_t *out_tokens,
+                                 void *stream);
+
+/*
  * Draft-token sampling is sd_spec_accept with gamma = 0: draft_logits,
  * draft_tokens and u_accept may be NULL, n_accepted is 0 and out_tokens[b, 0]
  * is drawn from softmax(target_logits[b, 0] / temperature) by inverse CDF with

@@ -21,6 +21,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     SD_ERR_WORKSPACE,
     SD_F32,
     SD_OK,
+    SD_SPEC_ACCEPT_SCRATCH_BYTES,
     SdError,
     lib,
     sd_best_gamma,
@@ -36,6 +37,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_snapkv_select_budgets,
     sd_snapkv_select_workspace_size,
     sd_spec_accept,
+    sd_spec_accept_noalloc,
     sd_spec_accept_workspace_size,
     sd_speedup,
     sd_streaming_select,

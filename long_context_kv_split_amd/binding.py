@@ -66,6 +66,7 @@ _SIGNATURES = {
     "sd_topk_select_workspace_size": (_S, [_I, _I, _I, _I]),
     "sd_spec_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_spec_accept_workspace_size": (_S, [_I, _I, _I]),
+    "sd_spec_accept_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P]),
     "sd_expected_tokens": (ctypes.c_double, [_I, ctypes.c_double]),
     "sd_speedup": (ctypes.c_double, [ctypes.c_double] * 3 + [_I] + [ctypes.c_double] * 3),
     "sd_best_gamma": (_I, [ctypes.c_double, ctypes.c_double, _P, _I, ctypes.c_double, ctypes.c_double,
@@ -321,6 +322,35 @@ def sd_topk_select(kv, q, num_q_heads, budget, max_kv_len, idx, sel_lens, worksp
     wp, wb = _ws(workspace, need)
     _check(lib().sd_topk_select(kv.ref, qp, B, num_q_heads, budget, max_kv_len, ip, sp, wp, wb, _stream(stream)),
            "sd_topk_select")
+
+
+SD_SPEC_ACCEPT_SCRATCH_BYTES = 4 << 20
+
+
+def _accept_args(target_logits, draft_logits, draft_tokens, u_accept, u_sample, gamma, vocab, n_accepted,
+                 out_tokens):
+    B = target_logits.shape[0]
+    tp = _dev(target_logits, "target_logits", torch.float32, B * (gamma + 1) * vocab)
+    if gamma > 0:
+        dp = _dev(draft_logits, "draft_logits", torch.float32, B * gamma * vocab)
+        xp = _dev(draft_tokens, "draft_tokens", torch.int32, B * gamma)
+        up = _dev(u_accept, "u_accept", torch.float32, B * gamma)
+    else:
+        dp = xp = up = None
+    us = _dev(u_sample, "u_sample", torch.float32, B * (gamma + 1))
+    np_ = _dev(n_accepted, "n_accepted", torch.int32, B)
+    op = _dev(out_tokens, "out_tokens", torch.int32, B * (gamma + 1))
+    return B, tp, dp, xp, up, us, np_, op
+
+
+def sd_spec_accept_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample, gamma, vocab,
+                           temperature, n_accepted, out_tokens, stream=None):
+    """sd_spec_accept without a workspace (the library's fixed per-GPU scratch;
+    overlapping calls on one GPU race)."""
+    B, tp, dp, xp, up, us, np_, op = _accept_args(target_logits, draft_logits, draft_tokens, u_accept,
+                                                  u_sample, gamma, vocab, n_accepted, out_tokens)
+    _check(lib().sd_spec_accept_noalloc(tp, dp, xp, up, us, B, gamma, vocab, temperature, np_, op,
+                                        _stream(stream)), "sd_spec_accept_noalloc")
 
 
 def sd_spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, gamma, vocab,

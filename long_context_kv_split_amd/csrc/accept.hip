@@ -419,12 +419,12 @@ extern "C" size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, in
   return plan_accept(batch, gamma, vocab).ws_bytes;
 }
 
-extern "C" sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
-                                    const int32_t *draft_tokens, const float *u_accept,
-                                    const float *u_sample, int32_t batch, int32_t gamma,
-                                    int32_t vocab, float temperature, int32_t *n_accepted,
-                                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
-                                    void *stream) {
+namespace {
+
+// Host checks shared by both acceptance entry points (no HIP call).
+sd_status check_accept(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
+                       const float *u_accept, const float *u_sample, int32_t batch, int32_t gamma,
+                       int32_t vocab, float temperature, int32_t *n_accepted, int32_t *out_tokens) {
   SD_REQUIRE(batch > 0 && gamma >= 0 && vocab > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(gamma <= kMaxGamma, SD_ERR_UNSUPPORTED);
   SD_REQUIRE(target_logits != nullptr && u_sample != nullptr && n_accepted != nullptr &&
@@ -436,9 +436,14 @@ extern "C" sd_status sd_spec_accept(const float *target_logits, const float *dra
   SD_REQUIRE((int64_t)batch * (gamma + 1) * vocab < ((int64_t)1 << 40), SD_ERR_UNSUPPORTED);
   SD_REQUIRE(vocab < (1 << 30), SD_ERR_UNSUPPORTED);
   SD_REQUIRE((int64_t)batch * (2 * gamma + 1) < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);  // grid rows
-  AccPlan p = plan_accept(batch, gamma, vocab);
-  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
+  return SD_OK;
+}
 
+// Enqueue the four kernels with `workspace` (at least plan_accept's ws_bytes).
+sd_status launch_accept(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
+                        const float *u_accept, const float *u_sample, int32_t batch, int32_t gamma,
+                        int32_t vocab, float temperature, int32_t *n_accepted, int32_t *out_tokens,
+                        const AccPlan &p, void *workspace, hipStream_t st) {
   AccParams a{};
   a.zt = target_logits;
   a.zd = draft_logits;
@@ -462,7 +467,6 @@ extern "C" sd_status sd_spec_accept(const float *target_logits, const float *dra
   a.n_chunks = p.n_chunks;
   a.inv_temp = 1.f / temperature;
   a.inv_temp_d = 1.0 / (double)temperature;
-  hipStream_t st = sdh::as_stream(stream);
   // 16-byte loads need every row 16-byte aligned
   const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                    (gamma == 0 || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
@@ -481,4 +485,78 @@ extern "C" sd_status sd_spec_accept(const float *target_logits, const float *dra
     accept_sample_kernel<1><<<(unsigned)batch, 64, 0, st>>>(a);
   }
   return sdh::launch_status();
+}
+
+// Scratch of sd_spec_accept_noalloc: a fixed array in the library's device
+// memory, one copy per GPU, held until the process ends. Host code never uses
+// this name as an address: the device address comes from hipGetSymbolAddress
+// and is kept per device in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[SD_SPEC_ACCEPT_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+void *scratch_addr[kScratchDevices];  // device address of `scratch` per device, set on first use
+
+// Device address of `scratch` on `dev` (the current device): looked up once
+// per device; a race stores the same address.
+sd_status scratch_for(int dev, void **ptr) {
+  SD_REQUIRE(dev >= 0 && dev < kScratchDevices, SD_ERR_UNSUPPORTED);
+  void *p = __atomic_load_n(&scratch_addr[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return SD_ERR_HIP;
+    }
+    __atomic_store_n(&scratch_addr[dev], p, __ATOMIC_RELEASE);
+  }
+  *ptr = p;
+  return SD_OK;
+}
+
+}  // namespace
+
+extern "C" sd_status sd_spec_accept(const float *target_logits, const float *draft_logits,
+                                    const int32_t *draft_tokens, const float *u_accept,
+                                    const float *u_sample, int32_t batch, int32_t gamma,
+                                    int32_t vocab, float temperature, int32_t *n_accepted,
+                                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  sd_status s = check_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, batch, gamma,
+                             vocab, temperature, n_accepted, out_tokens);
+  if (s != SD_OK) return s;
+  AccPlan p = plan_accept(batch, gamma, vocab);
+  SD_REQUIRE(workspace != nullptr && workspace_bytes >= p.ws_bytes, SD_ERR_WORKSPACE);
+  return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, batch, gamma, vocab,
+                       temperature, n_accepted, out_tokens, p, workspace, sdh::as_stream(stream));
+}
+
+extern "C" sd_status sd_spec_accept_noalloc(const float *target_logits, const float *draft_logits,
+                                            const int32_t *draft_tokens, const float *u_accept,
+                                            const float *u_sample, int32_t batch, int32_t gamma,
+                                            int32_t vocab, float temperature, int32_t *n_accepted,
+                                            int32_t *out_tokens, void *stream) {
+  sd_status s = check_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, batch, gamma,
+                             vocab, temperature, n_accepted, out_tokens);
+  if (s != SD_OK) return s;
+  AccPlan p = plan_accept(batch, gamma, vocab);
+  SD_REQUIRE(p.ws_bytes <= SD_SPEC_ACCEPT_SCRATCH_BYTES, SD_ERR_UNSUPPORTED);
+  hipStream_t st = sdh::as_stream(stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SD_ERR_HIP;
+  }
+  if (st != nullptr) {
+    // the scratch address is per device: the stream must be the current device's
+    int sdev = -1;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return SD_ERR_HIP;
+    }
+    SD_REQUIRE(sdev == dev, SD_ERR_INVALID_ARG);
+  }
+  void *ws = nullptr;
+  s = scratch_for(dev, &ws);
+  if (s != SD_OK) return s;
+  return launch_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, batch, gamma, vocab,
+                       temperature, n_accepted, out_tokens, p, ws, st);
 }

@@ -222,6 +222,34 @@ def test_accept_rejects_invalid_arguments(L, args, want):
     assert st == want
 
 
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(zt=None), sd.SD_ERR_INVALID_ARG),
+    (dict(gamma=65), sd.SD_ERR_UNSUPPORTED),
+    (dict(temp=-1.0), sd.SD_ERR_INVALID_ARG),
+    # needs more scratch than the library's fixed array holds
+    (dict(batch=20000, gamma=4, vocab=1000), sd.SD_ERR_UNSUPPORTED),
+    (dict(batch=64, gamma=4, vocab=1 << 24), sd.SD_ERR_UNSUPPORTED),
+])
+def test_accept_noalloc_rejects_invalid_arguments(L, args, want):
+    """Host checks of the allocation-free entry point, including the scratch
+    limit, all before any HIP call."""
+    a = dict(zt=FAKE, batch=4, gamma=3, vocab=1000, temp=1.0)
+    a.update(args)
+    st = L.sd_spec_accept_noalloc(a["zt"], FAKE, FAKE, FAKE, FAKE, a["batch"], a["gamma"], a["vocab"],
+                                  a["temp"], FAKE, FAKE, None)
+    assert st == want
+
+
+def test_accept_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SD_SPEC_ACCEPT_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.SD_SPEC_ACCEPT_SCRATCH_BYTES
+    # the bench-shape acceptance fits; a batch well past it does not
+    assert sd.sd_spec_accept_workspace_size(128, 4, 128256) <= binding.SD_SPEC_ACCEPT_SCRATCH_BYTES
+    assert sd.sd_spec_accept_workspace_size(2000, 4, 128256) > binding.SD_SPEC_ACCEPT_SCRATCH_BYTES
+
+
 def test_binding_refuses_host_tensors(L):
     k = torch.zeros((2, 1, 16, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
