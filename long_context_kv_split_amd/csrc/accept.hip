@@ -5,23 +5,21 @@
 // distributions, correct from the residual target distribution at the first
 // rejection, or draw a bonus token from the target when all are accepted.
 //
-// Four kernels; the logits are streamed once, plus the one or two rows the
-// residual needs:
-//   accept_stats:    one block per (row, vocab chunk) of the 2*gamma+1 rows of
-//                    every sequence: chunk max of z/t and the sum of exp(z/t -
-//                    max) (fp32 exponentials, fp64 sums; each thread keeps its
-//                    own running max, merged once at the end);
-//   accept_decide:   one wave per sequence: lanes merge the chunk statistics of
-//                    each row into log-normalisers (fp64) in parallel, lane i
-//                    evaluates p_i(x_i), q_i(x_i) and the test
-//                    u_i q_i(x_i) < p_i(x_i) (fp64); the accepted count n is
-//                    the first failing lane;
-//   accept_residual: one block per (sequence, vocab chunk): residual weights
-//                    max(0, p_n - q_n) (or p_gamma) of the chunk, summed per
-//                    2048-entry wave segment in fp64;
-//   accept_sample:   one wave per sequence walks the segment sums to the one
-//                    holding u*Z and finds the token there with wave prefix
-//                    sums (fp64) over the segment loaded into registers.
+// Two kernels; the logits are streamed once, plus the one or two rows the
+// draw needs:
+//   accept_stats:  one block per (row, vocab chunk) of the 2*gamma+1 rows of
+//                  every sequence: chunk max of z/t and the sum of exp(z/t -
+//                  max) (fp32 exponentials, fp64 sums; each thread keeps its
+//                  own running max, merged once at the end);
+//   accept_finish: one 1024-thread block per sequence: its waves merge the
+//                  chunk statistics of each row into log-normalisers (fp64),
+//                  wave 0 evaluates u_i q_i(x_i) < p_i(x_i) for every draft
+//                  (fp64; n = the first failure), then the block streams the
+//                  drawn row pair once, residual weights max(0, p_n - q_n) (or
+//                  p_gamma) summed per (slot, wave) piece in vocabulary order
+//                  into LDS (fp64), scans the piece sums for the one holding
+//                  u*Z, and the wave owning that piece rescans it for the
+//                  token.
 #include "sd_device.h"
 #include "sd_host.h"
 
@@ -34,10 +32,7 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kPerThread = 32;
 constexpr int kChunk = kAccThreads * kPerThread;  // vocab entries per block
-constexpr int kSegsPerChunk = kAccThreads / 64;   // wave segments of 64 * kPerThread entries
-constexpr int kSeg = 64 * kPerThread;
 constexpr int kMaxGamma = 64;                     // one decide lane per draft position
-constexpr double kLog2eD = 1.4426950408889634;
 
 struct AccParams {
   const float *zt;  // [B, gamma+1, V]
@@ -48,9 +43,6 @@ struct AccParams {
   int32_t *n_accepted;
   int32_t *out_tokens;
   double *stats;      // [B, 2*gamma+1, n_chunks, 2]  (max, sum)
-  double *dec;        // [B, 4]: n, log-normaliser of the p row, of the q row, unused
-  double *seg_z;      // [B, n_chunks * kSegsPerChunk] residual mass per wave segment
-  int32_t *seg_last;  // [B, n_chunks * kSegsPerChunk] last index with mass (-1)
   int32_t B, gamma, V, n_chunks;
   float inv_temp;
   double inv_temp_d;
@@ -71,28 +63,34 @@ __device__ __forceinline__ void merge_ms(float &m, double &s, float m2, double s
   m = M;
 }
 
-// VEC = 4: 16-byte loads (rows 16-byte aligned), else 4-byte loads.
+// VEC = 4: 16-byte loads (rows 16-byte aligned, V a multiple of 4), else
+// 4-byte loads. Addresses past the row are clamped onto its last entries and
+// the values masked, so every load is issued unconditionally and all of a
+// thread's loads are in flight together.
 template <int VEC>
 __device__ __forceinline__ void load_chunk(const float *z, int t0, int V, float inv_temp,
                                            float (&x)[kPerThread]) {
   if constexpr (VEC == 4) {
+    f32x4 v[kPerThread / 4];
 #pragma unroll
     for (int e = 0; e < kPerThread / 4; ++e) {
       const int t = t0 + (e * kAccThreads + (int)threadIdx.x) * 4;
-      if (t + 3 < V) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + t));
+      v[e] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + min(t, V - 4)));
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[4 * e + j] = v[j] * inv_temp;
-      } else {
+    for (int e = 0; e < kPerThread / 4; ++e) {
+      const int t = t0 + (e * kAccThreads + (int)threadIdx.x) * 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[4 * e + j] = t + j < V ? z[t + j] * inv_temp : kNegInf;
-      }
+      for (int j = 0; j < 4; ++j) x[4 * e + j] = t + j < V ? v[e][j] * inv_temp : kNegInf;
     }
   } else {
+    float v[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) v[e] = z[min(t0 + e * kAccThreads + (int)threadIdx.x, V - 1)];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       const int t = t0 + e * kAccThreads + (int)threadIdx.x;
-      x[e] = t < V ? z[t] * inv_temp : kNegInf;
+      x[e] = t < V ? v[e] * inv_temp : kNegInf;
     }
   }
 }
@@ -134,50 +132,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) 
   }
 }
 
-// Log of the softmax normaliser of row k (max of z/t plus log of the sum).
-__device__ __forceinline__ double row_lse(const AccParams &a, int b, int k) {
-  const int nrow = 2 * a.gamma + 1;
-  const double *st = a.stats + ((size_t)b * nrow + k) * a.n_chunks * 2;
-  double M = -__builtin_inf();
-  for (int c = 0; c < a.n_chunks; ++c) M = fmax(M, st[2 * c]);
-  double l = 0.0;
-  for (int c = 0; c < a.n_chunks; ++c)
-    if (st[2 * c] != -__builtin_inf()) l += st[2 * c + 1] * exp(st[2 * c] - M);
-  return M + log(l);
-}
-
-// One wave per sequence.
-__global__ __launch_bounds__(64) void accept_decide_kernel(AccParams a) {
-  __shared__ double lse[2 * kMaxGamma + 1];
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int g = a.gamma;
-  for (int k = lane; k < 2 * g + 1; k += 64) lse[k] = row_lse(a, b, k);
-  __syncthreads();
-  bool acc = false;  // lanes at or past gamma count as rejections (they stop the scan)
-  if (lane < g) {
-    const int x = clampi(a.tokens[(size_t)b * g + lane], 0, a.V - 1);
-    const double p = exp((double)row_ptr(a, b, lane)[x] * a.inv_temp_d - lse[lane]);
-    const double q = exp((double)row_ptr(a, b, g + 1 + lane)[x] * a.inv_temp_d - lse[g + 1 + lane]);
-    acc = (double)a.u_accept[(size_t)b * g + lane] * q < p;
-  }
-  const uint64_t rej = ~__ballot(acc);
-  const int n = min(g, rej != 0 ? (int)__builtin_ctzll(rej) : 64);
-  if (lane == 0) {
-    a.dec[(size_t)b * 4 + 0] = (double)n;
-    a.dec[(size_t)b * 4 + 1] = lse[n];
-    a.dec[(size_t)b * 4 + 2] = n < g ? lse[g + 1 + n] : 0.0;
-    a.n_accepted[b] = n;
-  }
-  // accepted drafts and the -1 padding; slot n gets the sampled token later
-  for (int t = lane; t <= g; t += 64) {
-    if (t < n)
-      a.out_tokens[(size_t)b * (g + 1) + t] = clampi(a.tokens[(size_t)b * g + t], 0, a.V - 1);
-    else if (t > n)
-      a.out_tokens[(size_t)b * (g + 1) + t] = -1;
-  }
-}
-
 __device__ __forceinline__ double wave_incl_scan_f64(double v) {
   const int lane = lane_id();
 #pragma unroll
@@ -188,227 +142,336 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v) {
   return v;
 }
 
-template <typename X>
-__device__ __forceinline__ X prior_load(const X *p) {
-  return *p;  // written by an earlier kernel on the same stream
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
 }
 
-template <int VEC>
-__global__ __launch_bounds__(kAccThreads) void accept_residual_kernel(AccParams a) {
-  const int c = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = a.gamma;
-  const int n = (int)a.dec[(size_t)b * 4 + 0];
-  const bool residual = n < g;
-  const double cp = a.dec[(size_t)b * 4 + 1];
-  const double cq = a.dec[(size_t)b * 4 + 2];
-  const float *zp = row_ptr(a, b, n);
-  const float *zq = residual ? row_ptr(a, b, g + 1 + n) : nullptr;
-  // p(t) = exp(z_t/T - lse): the offset stays fp64 so that the p and q
-  // normalisers carry no systematic fp32 rounding (it would not cancel in
-  // p - q); only the final exponential is fp32.
-  auto prob = [&](const float *z, double off, int t) -> float {
-    return __builtin_amdgcn_exp2f((float)(((double)z[t] * a.inv_temp_d - off) * kLog2eD));
-  };
-  auto weight = [&](int t, bool target_only) -> float {
-    const float p = prob(zp, cp, t);
-    if (!residual || target_only) return p;
-    return fmaxf(0.f, p - prob(zq, cq, t));
-  };
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
 
-  // Wave segment: entries seg0 + e*64 + lane, e < kPerThread (coalesced, and
-  // consecutive in (e, lane) order).
-  const int nseg = a.n_chunks * kSegsPerChunk;
-  const int seg = c * kSegsPerChunk + wave;
-  const int seg0 = seg * kSeg;
-  double part = 0.0;
-  int last = -1;
+// The finishing kernel: one 1024-thread block per sequence. In vocabulary
+// order the drawn row is cut into iterations of kFinSpan entries; wave wv
+// owns entries [e * kFinSpan + wv * kWaveSpan, + kWaveSpan) of iteration e,
+// lane l four consecutive ones. A "slot" is G consecutive iterations of one
+// wave (G = 1 up to a million entries), so (slot, wave) pieces are in
+// vocabulary order and their sums fit in LDS.
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinEnt = 4;                       // consecutive entries per lane and iteration
+constexpr int kWaveSpan = 64 * kFinEnt;          // 256
+constexpr int kFinSpan = kFinThreads * kFinEnt;  // 4096
+constexpr int kFinSlots = 256;                   // slots per wave held in LDS
+constexpr int kFinUnroll = 4;                    // iterations per pipelined batch of loads
+
+// Weights of entries t..t+3 (t a multiple of 4) of the drawn row:
+// max(0, p - q) (RESID) or p, p(t) = exp(z_t / T - lse). The fp64 normaliser
+// enters as an fp32 pair (hi + lo = lse to about 2^-48 relative), so it
+// carries no systematic fp32 rounding (that would scale p and q by different
+// constants, an error that does not cancel in p - q); the exponent itself is
+// formed in fp32 with one fused multiply-add, rounded per token like the
+// final exponential.
+// Loads are unconditional (clamped into the row, masked afterwards).
+template <int VEC, bool RESID>
+__device__ __forceinline__ void draw_load(const AccParams &a, const float *zp, const float *zq, int t,
+                                          float (&zpv)[kFinEnt], float (&zqv)[kFinEnt]) {
   if constexpr (VEC == 4) {
-    // lane owns 4 consecutive entries per step: seg0 + e*256 + 4*lane + j
-#pragma unroll 4
-    for (int e = 0; e < kPerThread / 4; ++e) {
-      const int t = seg0 + e * 256 + 4 * lane;
-      float w[4];
-      if (t + 3 < a.V) {
-        const f32x4 pv = *reinterpret_cast<const f32x4 *>(zp + t);
-        f32x4 qv = {0.f, 0.f, 0.f, 0.f};
-        if (residual) qv = *reinterpret_cast<const f32x4 *>(zq + t);
+    const int tc = min(t, a.V - 4);
+    const f32x4 pv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zp + tc));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f((float)(((double)pv[j] * a.inv_temp_d - cp) * kLog2eD));
-          const float q = residual ? __builtin_amdgcn_exp2f((float)(((double)qv[j] * a.inv_temp_d - cq) * kLog2eD)) : 0.f;
-          w[j] = residual ? fmaxf(0.f, p - q) : p;
-        }
-      } else {
+    for (int j = 0; j < 4; ++j) zpv[j] = pv[j];
+    if constexpr (RESID) {
+      const f32x4 qv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zq + tc));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = t + j < a.V ? weight(t + j, false) : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        part += (double)w[j];
-        if (w[j] > 0.f) last = t + j;
-      }
+      for (int j = 0; j < 4; ++j) zqv[j] = qv[j];
     }
   } else {
-#pragma unroll 8
-    for (int e = 0; e < kPerThread; ++e) {
-      const int t = seg0 + e * 64 + lane;
-      if (t < a.V) {
-        const float w = weight(t, false);
-        part += (double)w;
-        if (w > 0.f) last = t;
-      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tc = min(t + j, a.V - 1);
+      zpv[j] = zp[tc];
+      if constexpr (RESID) zqv[j] = zq[tc];
     }
-  }
-  part = wave_sum_f64(part);
-  for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if (lane == 0) {
-    a.seg_z[(size_t)b * nseg + seg] = part;
-    a.seg_last[(size_t)b * nseg + seg] = last;
   }
 }
 
-// One wave per sequence: segment sums -> segment holding u*Z -> token.
+struct Offset {
+  float hi, lo;
+};
+__device__ __forceinline__ Offset split_offset(double c) {
+  const float hi = (float)c;
+  return Offset{hi, (float)(c - (double)hi)};
+}
+
+template <bool RESID>
+__device__ __forceinline__ void draw_weights(const AccParams &a, Offset cp, Offset cq, int t,
+                                             const float (&zpv)[kFinEnt], const float (&zqv)[kFinEnt],
+                                             float (&w)[kFinEnt]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float p = __builtin_amdgcn_exp2f((fmaf(zpv[j], a.inv_temp, -cp.hi) - cp.lo) * kLog2e);
+    float r = p;
+    if constexpr (RESID)
+      r = fmaxf(0.f, p - __builtin_amdgcn_exp2f((fmaf(zqv[j], a.inv_temp, -cq.hi) - cq.lo) * kLog2e));
+    w[j] = t + j < a.V ? r : 0.f;
+  }
+}
+
+// One sweep over the drawn row: the (slot, wave) piece sums into seg, and the
+// last entry with mass of this thread. Software-pipelined: the loads of the
+// next kFinUnroll iterations are in flight while the current ones are
+// summed (two register buffers used alternately; loads past the row are
+// clamped into it and their results dropped).
+template <int VEC, bool RESID>
+__device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, const float *zq, Offset cp,
+                                          Offset cq, int iters, int G, double *seg) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int t_lane = wv * kWaveSpan + kFinEnt * lane;
+  int last = -1;
+  double gsum = 0.0;
+  struct Buf {
+    float p[kFinUnroll][kFinEnt], q[kFinUnroll][kFinEnt];
+  };
+  auto fetch = [&](int e0, Buf &bf) {
+#pragma unroll
+    for (int u = 0; u < kFinUnroll; ++u) draw_load<VEC, RESID>(a, zp, zq, (e0 + u) * kFinSpan + t_lane, bf.p[u], bf.q[u]);
+  };
+  auto consume = [&](int e0, const Buf &bf) {
+#pragma unroll
+    for (int u = 0; u < kFinUnroll; ++u) {
+      const int e = e0 + u;
+      if (e < iters) {
+        const int t = e * kFinSpan + t_lane;
+        float w[kFinEnt];
+        draw_weights<RESID>(a, cp, cq, t, bf.p[u], bf.q[u], w);
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < kFinEnt; ++j) {
+          s += (double)w[j];
+          if (w[j] > 0.f) last = t + j;
+        }
+        gsum += wave_sum_f64(s);
+        if ((e + 1) % G == 0 || e == iters - 1) {
+          if (lane == 0) seg[(e / G) * kFinWaves + wv] = gsum;
+          gsum = 0.0;
+        }
+      }
+    }
+  };
+  Buf A, B;
+  fetch(0, A);
+  for (int e0 = 0; e0 < iters; e0 += 2 * kFinUnroll) {
+    fetch(min(e0 + kFinUnroll, iters), B);
+    consume(e0, A);
+    if (e0 + kFinUnroll >= iters) break;
+    fetch(min(e0 + 2 * kFinUnroll, iters), A);
+    consume(e0 + kFinUnroll, B);
+  }
+  return last;
+}
+
+// The owning wave's rescan of piece (slot, wave): the first token with mass
+// whose cumulative weight exceeds thr, or -1; *seg_last gets the piece's last
+// token with mass.
+template <int VEC, bool RESID>
+__device__ __forceinline__ int draw_rescan(const AccParams &a, const float *zp, const float *zq, Offset cp,
+                                           Offset cq, int e_begin, int e_end, double before, double thr,
+                                           int *seg_last) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  int y = -1, sl = -1;
+  for (int e = e_begin; e < e_end && y < 0; ++e) {
+    const int t = e * kFinSpan + wv * kWaveSpan + kFinEnt * lane;
+    float zpv[kFinEnt], zqv[kFinEnt], w[kFinEnt];
+    draw_load<VEC, RESID>(a, zp, zq, t, zpv, zqv);
+    draw_weights<RESID>(a, cp, cq, t, zpv, zqv, w);
+    double loc[kFinEnt], r = 0.0;
+#pragma unroll
+    for (int j = 0; j < kFinEnt; ++j) {
+      r += (double)w[j];
+      loc[j] = r;
+      if (w[j] > 0.f) sl = t + j;
+    }
+    const double inc = wave_incl_scan_f64(r);
+    const double exc = before + (inc - r);
+    int hj = kFinEnt;
+#pragma unroll
+    for (int j = kFinEnt - 1; j >= 0; --j)
+      if (w[j] > 0.f && exc + loc[j] > thr) hj = j;
+    const uint64_t h = __ballot(hj < kFinEnt);
+    if (h != 0) {
+      const int l = (int)__builtin_ctzll(h);
+      y = e * kFinSpan + wv * kWaveSpan + kFinEnt * l + __shfl(hj, l, 64);
+    }
+    before += __shfl(inc, 63, 64);
+  }
+  *seg_last = wave_max_i32(sl);
+  return y;
+}
+
 template <int VEC>
-__global__ __launch_bounds__(64) void accept_sample_kernel(AccParams a) {
+__global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a) {
+  __shared__ double seg[kFinSlots * kFinWaves];  // (slot, wave) weight sums, vocabulary order
+  __shared__ double lse[2 * kMaxGamma + 1];
+  __shared__ double scan_w[kFinWaves];
+  __shared__ int last_w[kFinWaves];
+  __shared__ int hit_w[kFinWaves];
+  __shared__ int n_s;
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int g = a.gamma;
-  const int n = (int)a.dec[(size_t)b * 4 + 0];
-  const bool residual = n < g;
-  const double cp = a.dec[(size_t)b * 4 + 1];
-  const double cq = a.dec[(size_t)b * 4 + 2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = a.gamma, nrow = 2 * g + 1;
+
+  // Draft tokens and their logits depend on the inputs only: wave 0 fetches
+  // them first, so their loads overlap the normalisers' merge below.
+  int x = 0;
+  float zpx = 0.f, zqx = 0.f;
+  if (wv == 0 && lane < g) {
+    x = clampi(a.tokens[(size_t)b * g + lane], 0, a.V - 1);
+    zpx = row_ptr(a, b, lane)[x];
+    zqx = row_ptr(a, b, g + 1 + lane)[x];
+  }
+
+  // 1. Row normalisers: one wave per row merges the row's chunk statistics
+  //    (max of the chunk maxima, then the rescaled sum).
+  for (int k = wv; k < nrow; k += kFinWaves) {
+    const double *st = a.stats + ((size_t)b * nrow + k) * a.n_chunks * 2;
+    double M = -__builtin_inf();
+    for (int c = lane; c < a.n_chunks; c += 64) M = fmax(M, st[2 * c]);
+    M = wave_max_f64(M);
+    double l = 0.0;
+    for (int c = lane; c < a.n_chunks; c += 64)
+      if (st[2 * c] != -__builtin_inf()) l += st[2 * c + 1] * exp(st[2 * c] - M);
+    l = wave_sum_f64(l);
+    if (lane == 0) lse[k] = M + log(l);
+  }
+  __syncthreads();
+
+  // 2. Accept tests: lane i of wave 0 evaluates u_i q_i(x_i) < p_i(x_i) (fp64);
+  //    n is the first failing lane. Accepted drafts and the -1 padding are
+  //    written here, the drawn token at the end.
+  if (wv == 0) {
+    bool acc = false;  // lanes at or past gamma count as rejections (they stop the scan)
+    if (lane < g) {
+      const double p = exp((double)zpx * a.inv_temp_d - lse[lane]);
+      const double q = exp((double)zqx * a.inv_temp_d - lse[g + 1 + lane]);
+      acc = (double)a.u_accept[(size_t)b * g + lane] * q < p;
+    }
+    const uint64_t rej = ~__ballot(acc);
+    const int n = min(g, rej != 0 ? (int)__builtin_ctzll(rej) : 64);
+    if (lane == 0) {
+      n_s = n;
+      a.n_accepted[b] = n;
+    }
+    for (int t = lane; t <= g; t += 64) {
+      if (t < n)
+        a.out_tokens[(size_t)b * (g + 1) + t] = clampi(a.tokens[(size_t)b * g + t], 0, a.V - 1);
+      else if (t > n)
+        a.out_tokens[(size_t)b * (g + 1) + t] = -1;
+    }
+  }
+  __syncthreads();
+  const int n = n_s;
   const float *zp = row_ptr(a, b, n);
-  const float *zq = residual ? row_ptr(a, b, g + 1 + n) : nullptr;
-  auto prob = [&](const float *z, double off, int t) -> float {
-    return __builtin_amdgcn_exp2f((float)(((double)z[t] * a.inv_temp_d - off) * kLog2eD));
-  };
-  auto weight = [&](int t, bool target_only) -> float {
-    const float p = prob(zp, cp, t);
-    if (!residual || target_only) return p;
-    return fmaxf(0.f, p - prob(zq, cq, t));
-  };
-  const int nseg = a.n_chunks * kSegsPerChunk;
-  const double *zs = a.seg_z + (size_t)b * nseg;
-  const int32_t *ls = a.seg_last + (size_t)b * nseg;
+  const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
+  const Offset cp = split_offset(lse[n]);
+  const Offset cq = split_offset(n < g ? lse[g + 1 + n] : 0.0);
+  const int iters = (a.V + kFinSpan - 1) / kFinSpan;
+  const int G = (iters + kFinSlots - 1) / kFinSlots;  // iterations per slot
+  const int nslots = (iters + G - 1) / G;
+  const int npieces = nslots * kFinWaves;
+
+  // 3. One sweep over the drawn row: (slot, wave) sums in LDS, and the last
+  //    entry with mass. The residual of a row pair with no mass at all
+  //    (p_n == q_n) is replaced by p_n, as the pages' reading prescribes.
+  bool residual = n < g;
   int glast = -1;
-  for (int k = lane; k < nseg; k += 64) glast = max(glast, prior_load(ls + k));
-  for (int o = 32; o >= 1; o >>= 1) glast = max(glast, __shfl_xor(glast, o, 64));
-  // Segment prefix sums, 64 segments per wave scan; the same scan (same
-  // summation order) gives Z and then locates the segment holding u*Z.
-  auto seg_scan = [&](int k0, double carry, double &incl, double &excl) {
-    const double z = k0 + lane < nseg ? prior_load(zs + k0 + lane) : 0.0;
-    incl = wave_incl_scan_f64(z) + carry;
-    const double up = __shfl_up(incl, 1, 64);
-    excl = lane == 0 ? carry : up;
-  };
-  double Z = 0.0;
-  for (int k0 = 0; k0 < nseg; k0 += 64) {
-    double incl, excl;
-    seg_scan(k0, Z, incl, excl);
-    Z = __shfl(incl, 63, 64);
+  for (int pass = 0; pass < 2; ++pass) {
+    int last = residual ? draw_sweep<VEC, true>(a, zp, zq, cp, cq, iters, G, seg)
+                        : draw_sweep<VEC, false>(a, zp, zq, cp, cq, iters, G, seg);
+    last = wave_max_i32(last);
+    if (lane == 0) last_w[wv] = last;
+    __syncthreads();
+    glast = -1;
+    for (int w2 = 0; w2 < kFinWaves; ++w2) glast = max(glast, last_w[w2]);
+    __syncthreads();
+    if (glast >= 0 || !residual) break;
+    residual = false;  // no residual mass anywhere: draw from p_n
   }
+
+  // 4. Scan of the piece sums (fp64, vocabulary order): thread i takes
+  //    pieces 4i .. 4i+3; the first piece whose inclusive sum exceeds u*Z
+  //    holds the token.
+  constexpr int kPer = kFinSlots * kFinWaves / kFinThreads;  // 4
+  double ps[kPer], run = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = kPer * tid + j;
+    run += i < npieces ? seg[i] : 0.0;
+    ps[j] = run;
+  }
+  const double incl = wave_incl_scan_f64(run);
+  if (lane == 63) scan_w[wv] = incl;
+  __syncthreads();
+  double before_w = 0.0, Z = 0.0;
+  for (int w2 = 0; w2 < kFinWaves; ++w2) {
+    if (w2 < wv) before_w += scan_w[w2];
+    Z += scan_w[w2];
+  }
+  const double excl_t = before_w + incl - run;  // sum of the pieces before 4*tid
   const double v = (double)a.u_sample[(size_t)b * (g + 1) + n];
-  const bool target_only = glast < 0;  // no residual mass at all (p_n == q_n): draw from p_n
-  int k_first = -1, k_end = nseg;
-  double before = 0.0, thr;
-  if (target_only) {
-    double tot = 0.0;
-    for (int k = 0; k < nseg; ++k) {
-      double ps = 0.0;
-      for (int e = 0; e < kPerThread; ++e) {
-        const int t = k * kSeg + e * 64 + lane;
-        if (t < a.V) ps += (double)weight(t, true);
-      }
-      tot += wave_sum_f64(ps);
-    }
-    thr = v * tot;
-    k_first = 0;
-  } else {
-    thr = v * Z;
-    double carry = 0.0;
-    for (int k0 = 0; k0 < nseg && k_first < 0; k0 += 64) {
-      double incl, excl;
-      seg_scan(k0, carry, incl, excl);
-      const uint64_t hit = __ballot(k0 + lane < nseg && incl > thr);
-      if (hit != 0) {
-        const int j = (int)__builtin_ctzll(hit);
-        k_first = k0 + j;
-        before = __shfl(excl, j, 64);
-      }
-      carry = __shfl(incl, 63, 64);
-    }
-    k_end = k_first + 1;
-  }
+  const double thr = v * Z;
+  int hit = kPer;
+#pragma unroll
+  for (int j = kPer - 1; j >= 0; --j)
+    if (kPer * tid + j < npieces && excl_t + ps[j] > thr) hit = j;
+  const uint64_t hb = __ballot(hit < kPer);
+  if (lane == 0) hit_w[wv] = hb != 0 ? (64 * wv + (int)__builtin_ctzll(hb)) : 0x7fffffff;
+  __syncthreads();
+  int first_t = 0x7fffffff;
+  for (int w2 = 0; w2 < kFinWaves; ++w2) first_t = min(first_t, hit_w[w2]);
   int y = -1;
-  if (k_first >= 0 && !target_only) {
-    // The crossing segment: all its weights are loaded at once (lane owns the
-    // same entries as in the summing pass), then scanned in order in registers.
-    constexpr int J = VEC;                 // consecutive entries per lane per group
-    constexpr int NG = kPerThread / J;     // groups of 64*J entries
-    const int base = k_first * kSeg;
-    float w[kPerThread];
-#pragma unroll
-    for (int eg = 0; eg < NG; ++eg)
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int t = base + eg * 64 * J + J * lane + j;
-        w[eg * J + j] = t < a.V ? weight(t, false) : 0.f;
-      }
-    for (int eg = 0; eg < NG && y < 0; ++eg) {
-      double local[J];
-      double run = 0.0;
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        run += (double)w[eg * J + j];
-        local[j] = run;
-      }
-      const double incl = wave_incl_scan_f64(run);
-      const double excl = before + (incl - run);
-      int hit_j = J;
-#pragma unroll
-      for (int j = J - 1; j >= 0; --j)
-        if (w[eg * J + j] > 0.f && excl + local[j] > thr) hit_j = j;
-      const uint64_t hit = __ballot(hit_j < J);
-      if (hit != 0) {
-        const int l = (int)__builtin_ctzll(hit);
-        y = base + eg * 64 * J + J * l + __shfl(hit_j, l, 64);
-      }
-      before += __shfl(incl, 63, 64);
+  if (first_t != 0x7fffffff) {
+    // the thread that found the first crossing publishes its piece and the
+    // sum of the pieces before it
+    __shared__ int piece_s;
+    __shared__ double before_s;
+    if (tid == first_t) {
+      piece_s = kPer * tid + hit;
+      before_s = excl_t + (hit > 0 ? ps[hit - 1] : 0.0);
     }
-    // rounding left no crossing inside the chosen segment: its last token with mass
-    if (y < 0) y = prior_load(ls + k_first);
-  } else if (k_first >= 0) {
-    for (int k = k_first; k < k_end && y < 0; ++k) {
-      for (int e = 0; e < kPerThread && y < 0; ++e) {
-        const int t = k * kSeg + e * 64 + lane;
-        const float wt = t < a.V ? weight(t, true) : 0.f;
-        const double cum = before + wave_incl_scan_f64((double)wt);
-        const uint64_t hit = __ballot(wt > 0.f && cum > thr);
-        if (hit != 0) y = k * kSeg + e * 64 + (int)__builtin_ctzll(hit);
-        before = __shfl(cum, 63, 64);
-      }
+    __syncthreads();
+    const int piece = piece_s;
+    const int slot = piece / kFinWaves, pw = piece % kFinWaves;
+    if (wv == pw) {
+      // the owning wave reloads its entries of the slot's iterations and
+      // scans them in vocabulary order
+      const int e_end = min(iters, (slot + 1) * G);
+      int seg_last = -1;
+      y = residual ? draw_rescan<VEC, true>(a, zp, zq, cp, cq, slot * G, e_end, before_s, thr, &seg_last)
+                   : draw_rescan<VEC, false>(a, zp, zq, cp, cq, slot * G, e_end, before_s, thr, &seg_last);
+      // rounding left no crossing inside the piece: its last token with mass
+      if (y < 0) y = seg_last;
+      if (y < 0) y = glast;
+      if (lane == 0) a.out_tokens[(size_t)b * (g + 1) + n] = max(0, y);
     }
+  } else if (tid == 0) {
+    // rounding left v*Z at or above the total: the last token with mass
+    a.out_tokens[(size_t)b * (g + 1) + n] = max(0, glast);
   }
-  if (y < 0) y = target_only ? a.V - 1 : glast;
-  if (lane == 0) a.out_tokens[(size_t)b * (g + 1) + n] = max(0, y);
 }
 
 struct AccPlan {
   int n_chunks;
-  size_t stats_bytes, dec_bytes, segz_bytes, seglast_bytes, ws_bytes;
+  size_t ws_bytes;  // the chunk statistics
 };
 
 AccPlan plan_accept(int64_t B, int64_t gamma, int64_t V) {
   AccPlan p;
   p.n_chunks = (int)sdh::ceil_div(V, kChunk);
-  const int64_t nseg = (int64_t)p.n_chunks * kSegsPerChunk;
-  p.stats_bytes = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
-  p.dec_bytes = sdh::align_up((size_t)B * 4 * 8);
-  p.segz_bytes = sdh::align_up((size_t)B * nseg * 8);
-  p.seglast_bytes = sdh::align_up((size_t)B * nseg * 4);
-  p.ws_bytes = p.stats_bytes + p.dec_bytes + p.segz_bytes + p.seglast_bytes;
+  p.ws_bytes = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
   return p;
 }
 
@@ -452,15 +515,7 @@ sd_status launch_accept(const float *target_logits, const float *draft_logits, c
   a.u_sample = u_sample;
   a.n_accepted = n_accepted;
   a.out_tokens = out_tokens;
-  char *ws = reinterpret_cast<char *>(workspace);
-  size_t off = 0;
-  a.stats = reinterpret_cast<double *>(ws + off);
-  off += p.stats_bytes;
-  a.dec = reinterpret_cast<double *>(ws + off);
-  off += p.dec_bytes;
-  a.seg_z = reinterpret_cast<double *>(ws + off);
-  off += p.segz_bytes;
-  a.seg_last = reinterpret_cast<int32_t *>(ws + off);
+  a.stats = reinterpret_cast<double *>(workspace);
   a.B = batch;
   a.gamma = gamma;
   a.V = vocab;
@@ -471,18 +526,12 @@ sd_status launch_accept(const float *target_logits, const float *draft_logits, c
   const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                    (gamma == 0 || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
   const dim3 g_stats((unsigned)p.n_chunks, (unsigned)(batch * (2 * gamma + 1)));
-  const dim3 g_res((unsigned)p.n_chunks, (unsigned)batch);
-  if (vec)
-    accept_stats_kernel<4><<<g_stats, kAccThreads, 0, st>>>(a);
-  else
-    accept_stats_kernel<1><<<g_stats, kAccThreads, 0, st>>>(a);
-  accept_decide_kernel<<<(unsigned)batch, 64, 0, st>>>(a);
   if (vec) {
-    accept_residual_kernel<4><<<g_res, kAccThreads, 0, st>>>(a);
-    accept_sample_kernel<4><<<(unsigned)batch, 64, 0, st>>>(a);
+    accept_stats_kernel<4><<<g_stats, kAccThreads, 0, st>>>(a);
+    accept_finish_kernel<4><<<(unsigned)batch, kFinThreads, 0, st>>>(a);
   } else {
-    accept_residual_kernel<1><<<g_res, kAccThreads, 0, st>>>(a);
-    accept_sample_kernel<1><<<(unsigned)batch, 64, 0, st>>>(a);
+    accept_stats_kernel<1><<<g_stats, kAccThreads, 0, st>>>(a);
+    accept_finish_kernel<1><<<(unsigned)batch, kFinThreads, 0, st>>>(a);
   }
   return sdh::launch_status();
 }

@@ -41,7 +41,15 @@ using namespace sdk;
 namespace {
 
 constexpr int kStepTokens = 16;
-constexpr int kMaxChunkSteps = 128;  // sub-chunk: LDS row-id table of 128 steps x 16 tokens x 4 B = 8 KB
+// Row-id table of a sub-chunk in LDS (8 KB): verify keeps one base row per
+// step (the 16 tokens of a step are consecutive slots of one page), so a
+// sub-chunk is up to 2048 steps; the draft keeps one row per token, 128 steps.
+constexpr int kTableInts = 2048;
+template <bool SPARSE>
+constexpr int chunk_steps() {
+  return SPARSE ? kTableInts / kStepTokens : kTableInts;
+}
+constexpr int kResolveBatch = 16;  // independent table lookups per lane in flight
 
 struct AttnParams {
   const void *k_pages;
@@ -115,23 +123,57 @@ __device__ __forceinline__ void load_dwords(uint32_t (&dst)[N], const char *p) {
   }
 }
 
-// Row id (page*pool_heads + pkvh)*P + slot of cached token `t` of the chunk's
-// token list: position t (verify) or idx_row[t] (draft), through the page table.
+// Fill the sub-chunk's row table, rows (page * pool_heads + pkvh) * P + slot
+// through the page table: for verify the first row of each of steps
+// [sc_begin, sc_begin + n_steps); for the draft the row of each token of
+// those steps (entry t of the selection, then the tail in order). Lookups go
+// out kResolveBatch per lane before any is waited for, so a sub-chunk costs
+// one or two memory round trips instead of one per token.
 template <bool SPARSE>
-__device__ __forceinline__ int token_row(const AttnParams &a, int b, int pkvh, int t, int len, int sel,
-                                         const int32_t *idx_row) {
-  int pos;
-  if constexpr (SPARSE) {
-    // token t of the draft: entry t of the selection, then the tail in order
-    const int tt = clampi(t, 0, len - 1);
-    pos = tt < sel ? idx_row[tt] : a.tail_begin[b] + (tt - sel);
-    pos = clampi(pos, 0, a.max_pages * a.page_size - 1);
+__device__ __forceinline__ void resolve_rows(const AttnParams &a, int b, int pkvh, int sc_begin, int n_steps,
+                                             int len, int sel, const int32_t *idx_row, int *rows) {
+  const int lane = lane_id();
+  const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+  const int P = a.page_size;
+  if constexpr (!SPARSE) {
+    for (int k0 = 0; k0 < n_steps; k0 += 64 * kResolveBatch) {
+      int e[kResolveBatch];
+#pragma unroll
+      for (int i = 0; i < kResolveBatch; ++i) {
+        const int k = min(k0 + 64 * i + lane, n_steps - 1);
+        e[i] = pt[clampi((sc_begin + k) * kStepTokens / P, 0, a.max_pages - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < kResolveBatch; ++i) {
+        const int k = k0 + 64 * i + lane;
+        if (k < n_steps)
+          rows[k] = (clampi(e[i], 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + (sc_begin + k) * kStepTokens % P;
+      }
+    }
   } else {
-    pos = t;
+    const int n_tok = n_steps * kStepTokens;
+    const int t_base = sc_begin * kStepTokens;
+    const int tail0 = a.tail_begin ? a.tail_begin[b] : 0;
+    const int last_sel = max(sel - 1, 0);
+    const int pos_cap = a.max_pages * P - 1;
+    for (int t0 = 0; t0 < n_tok; t0 += 64 * kResolveBatch) {
+      int pos[kResolveBatch];
+#pragma unroll
+      for (int i = 0; i < kResolveBatch; ++i) {
+        const int t = clampi(t_base + t0 + 64 * i + lane, 0, len - 1);
+        const int from_idx = idx_row[min(t, last_sel)];
+        pos[i] = clampi(t < sel ? from_idx : tail0 + (t - sel), 0, pos_cap);
+      }
+      int e[kResolveBatch];
+#pragma unroll
+      for (int i = 0; i < kResolveBatch; ++i) e[i] = pt[pos[i] / P];
+#pragma unroll
+      for (int i = 0; i < kResolveBatch; ++i) {
+        const int tt = t0 + 64 * i + lane;
+        if (tt < n_tok) rows[tt] = (clampi(e[i], 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + pos[i] % P;
+      }
+    }
   }
-  int page = a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
-  page = clampi(page, 0, a.num_pages - 1);
-  return (page * a.pool_heads + pkvh) * a.page_size + pos % a.page_size;
 }
 
 // Issue the K and V loads of one 16-token step whose row ids sit in LDS at
@@ -139,14 +181,22 @@ __device__ __forceinline__ int token_row(const AttnParams &a, int b, int pkvh, i
 // 4g..4g+3 (the four ids are one 16-byte LDS read). K/V are streamed once per
 // call, so the loads carry the nontemporal hint (measured: about 5% more read
 // bandwidth than plain loads on this access pattern).
-template <typename T, int D>
+template <typename T, int D, bool SPARSE>
 __device__ __forceinline__ void load_step(const AttnParams &a, const int *rows, StepRegs<T, D> &R) {
   constexpr int EB = EltInfo<T>::bytes;
   constexpr int DPL = D / 16;
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
-  const int rowK = rows[r];
-  const int4 rowV = *reinterpret_cast<const int4 *>(rows + 4 * g);
+  int rowK;
+  int4 rowV;
+  if constexpr (SPARSE) {
+    rowK = rows[r];
+    rowV = *reinterpret_cast<const int4 *>(rows + 4 * g);
+  } else {  // one page: the step's rows are base .. base + 15
+    const int base = __builtin_amdgcn_readfirstlane(rows[0]);
+    rowK = base + r;
+    rowV = int4{base + 4 * g, base + 4 * g + 1, base + 4 * g + 2, base + 4 * g + 3};
+  }
   const char *kb = reinterpret_cast<const char *>(a.k_pages) + (size_t)rowK * D * EB;
   if constexpr (EB == 2) {
 #pragma unroll
@@ -294,7 +344,7 @@ void attn_split_kernel(AttnParams a) {
   constexpr int DPL = D / 16;
   constexpr int QV = StepRegs<T, D>::kVec;
   constexpr int NBUF = AttnTuning<T, NB>::kBufs;
-  __shared__ __attribute__((aligned(16))) int rows_lds[kMaxChunkSteps * kStepTokens];
+  __shared__ __attribute__((aligned(16))) int rows_lds[kTableInts];
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
 
@@ -337,15 +387,14 @@ void attn_split_kernel(AttnParams a) {
     }
     const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
 
-    // The segment is processed in sub-chunks of at most kMaxChunkSteps steps:
-    // the row ids of every token of a sub-chunk are resolved into LDS first, so
-    // that no K/V load of the main loop waits on a dependent vector load.
-    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kMaxChunkSteps) {
-      const int sc_end = min(s_end, sc_begin + kMaxChunkSteps);
-      const int n_tok = (sc_end - sc_begin) * kStepTokens;
+    // The segment is processed in sub-chunks of at most chunk_steps steps:
+    // the row ids of a sub-chunk are resolved into LDS first, so that no K/V
+    // load of the main loop waits on a dependent vector load.
+    constexpr int kChunk = chunk_steps<SPARSE>();
+    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kChunk) {
+      const int sc_end = min(s_end, sc_begin + kChunk);
       __syncthreads();  // the previous sub-chunk's table reads are done
-      for (int tt = lane; tt < n_tok; tt += 64)
-        rows_lds[tt] = token_row<SPARSE>(a, b, pkvh, sc_begin * kStepTokens + tt, len, sel, idx_row);
+      resolve_rows<SPARSE>(a, b, pkvh, sc_begin, sc_end - sc_begin, len, sel, idx_row, rows_lds);
       __syncthreads();
       // Main loop: groups of NBUF steps that need no mask, with a ring of NBUF
       // step buffers unrolled so every buffer has a fixed role and the loop
@@ -355,22 +404,22 @@ void attn_split_kernel(AttnParams a) {
       const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
       const int n_plain = max(0, min(sc_end, first_masked) - sc_begin);
       const int n_groups = n_plain / NBUF;
-      auto rows_of = [&](int k) { return rows_lds + min(k, last) * kStepTokens; };
+      auto rows_of = [&](int k) { return rows_lds + min(k, last) * (SPARSE ? kStepTokens : 1); };
       StepRegs<T, D> buf[NBUF];
       if (n_groups > 0) {
 #pragma unroll
-        for (int k = 0; k < NBUF - 1; ++k) load_step<T, D>(a, rows_of(k), buf[k]);
+        for (int k = 0; k < NBUF - 1; ++k) load_step<T, D, SPARSE>(a, rows_of(k), buf[k]);
         for (int k0 = 0; k0 < n_groups * NBUF; k0 += NBUF) {
 #pragma unroll
           for (int j = 0; j < NBUF; ++j) {
-            load_step<T, D>(a, rows_of(k0 + j + NBUF - 1), buf[(j + NBUF - 1) % NBUF]);
+            load_step<T, D, SPARSE>(a, rows_of(k0 + j + NBUF - 1), buf[(j + NBUF - 1) % NBUF]);
             compute_step<T, D, NB, SPARSE, false>(a, st, buf[j], sc_begin + k0 + j, len);
           }
         }
       }
       // Tail: the remaining steps, one at a time, with the mask.
       for (int k = n_groups * NBUF; k <= last; ++k) {
-        load_step<T, D>(a, rows_of(k), buf[0]);
+        load_step<T, D, SPARSE>(a, rows_of(k), buf[0]);
         compute_step<T, D, NB, SPARSE, true>(a, st, buf[0], sc_begin + k, len);
       }
     }

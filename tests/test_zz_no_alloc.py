@@ -56,7 +56,7 @@ def test_noalloc_matches_workspace_entry_on_two_calls(first, second):
 
 
 def test_noalloc_rejects_more_scratch_than_it_holds():
-    B, gamma, V = 20000, 4, 1000
+    B, gamma, V = 30000, 4, 1000
     assert sd.sd_spec_accept_workspace_size(B, gamma, V) > sd.SD_SPEC_ACCEPT_SCRATCH_BYTES
     zt, zd, x, ua, us = _inputs(47, B, gamma, V)
     n = torch.full((B,), -5, dtype=torch.int32, device="cuda")
