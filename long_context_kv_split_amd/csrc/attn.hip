@@ -35,6 +35,7 @@
 #include "sd_sched.h"
 
 #include <algorithm>
+#include <type_traits>
 
 using namespace sdk;
 
@@ -450,6 +451,303 @@ void attn_split_kernel(AttnParams a) {
   });
 }
 
+// ---------------------------------------------------------------------------
+// bf16 caches with head_dim 128: K and V streamed through a per-wave LDS ring.
+//
+// Every 16-token step is copied global -> LDS by asynchronous 16-byte copies
+// (4 per lane for K, 4 for V), so loads in flight hold no registers and the
+// wave decides its own waits: each step issues the same 8 copies, and
+// "at most (kStreamRing - 1) * 8 newer vector-memory operations outstanding"
+// means the step has landed (any other memory operation only makes that
+// stricter). The ring is read with inline ds_read blocks that end in their
+// own LDS wait, so the compiler adds no wait of its own for the copies.
+// LDS layout of a step: K as 16 rows of 16 chunks with chunk c of token t at
+// position c ^ t (the MFMA operand reads, 16 tokens x one chunk, fall in
+// distinct banks), then V as 16 plain rows (the V^T operand reads four whole
+// rows per instruction).
+// Row ids: verify keeps the first row of each step (its 16 tokens share a
+// page) in a 64-step register window, lane i holding step wb + i, read with
+// readlane; the page-table entries of the window after next are copied into
+// LDS one window early, so sliding the window never waits on a load issued in
+// the same iteration. The draft resolves a sub-chunk of steps into an LDS
+// table first, stored so that lane (g, r) finds the rows of tokens g, g + 4,
+// g + 8, g + 12 (the tokens of its four copies) in one 16-byte read.
+// Steps per wave in the LDS ring, and with it the resident waves: a deeper
+// ring keeps more bytes in flight per wave but leaves room for fewer waves
+// per CU. Two 16-step tiles (20 query rows at gamma = 4) measured best with
+// two steps (eight waves per CU); one, three or four tiles with four steps
+// (four waves per CU): e.g. the 8k-context batch 0.186 against 0.207 ms,
+// the 70B shape 0.709 against 0.766 ms.
+template <int NB>
+constexpr int stream_ring() {
+  return NB == 2 ? 2 : 4;
+}
+constexpr int kStreamChunks = 256;   // 16-byte chunks per 16-token step of one tensor (d = 128, bf16)
+constexpr int kStreamWin = 64;       // steps per row window (verify)
+constexpr int kSparseSubSteps = 48;  // draft row table: 48 steps x 16 tokens x 4 B = 3 KB
+
+template <bool SPARSE, int RING>
+struct StreamLayout {
+  static constexpr int kRingBytes = RING * 2 * kStreamChunks * 16;
+  static constexpr int kTableBytes = SPARSE ? kSparseSubSteps * kStepTokens * 4 : kStreamWin * 4;
+  static constexpr int kBytes = kRingBytes + kTableBytes;
+};
+
+__device__ __forceinline__ int lds_read_i32(const lds_char *p) {
+  int v = 0;
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"((uint32_t)(size_t)p) : "memory");
+#endif
+  return v;
+}
+__device__ __forceinline__ int4 lds_read_i32x4(const lds_char *p) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"((uint32_t)(size_t)p) : "memory");
+#endif
+  return int4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+}
+__device__ __forceinline__ void lds_write_i32(lds_char *p, int v) {
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("ds_write_b32 %0, %1" ::"v"((uint32_t)(size_t)p), "v"(v) : "memory");
+#endif
+}
+
+// Operands of one step from ring slot `sl`: K chunk 4 kk + g of token r
+// (MFMA A operand of S^T = K Q^T) and V d-range [8r, 8r + 8) of tokens
+// 4g .. 4g + 3 (rows of the V^T operand).
+__device__ __forceinline__ void stream_operands(const lds_u32x4 *ring, int sl, StepRegs<__bf16, 128> &cur) {
+  const int lane = lane_id(), g = lane >> 4, r = lane & 15;
+  const lds_u32x4 *kb = ring + sl * 2 * kStreamChunks;
+  const lds_u32x4 *vb = kb + kStreamChunks;
+  uint32_t ad[8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ad[kk] = (uint32_t)(size_t)(kb + r * 16 + ((4 * kk + g) ^ r));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ad[4 + j] = (uint32_t)(size_t)(vb + (4 * g + j) * 16 + r);
+  u32x4 v[4];
+#if __HIP_DEVICE_COMPILE__
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(cur.k[0]), "=&v"(cur.k[1]), "=&v"(cur.k[2]), "=&v"(cur.k[3]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+#endif
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cur.v[j][0] = v[j].x;
+    cur.v[j][1] = v[j].y;
+    cur.v[j][2] = v[j].z;
+    cur.v[j][3] = v[j].w;
+  }
+}
+
+template <int NB, bool SPARSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB <= 3 ? 2 : 1)))
+void attn_stream_kernel(AttnParams a) {
+  constexpr int D = 128;
+  constexpr int QV = StepRegs<__bf16, D>::kVec;
+  constexpr int DPL = D / 16;
+  constexpr int kStreamRing = stream_ring<NB>();
+  using Lay = StreamLayout<SPARSE, kStreamRing>;
+  __shared__ __attribute__((aligned(16))) char lds_raw[Lay::kBytes];
+  lds_char *lds = (lds_char *)lds_raw;
+  lds_u32x4 *ring = (lds_u32x4 *)lds;
+  lds_char *table = lds + Lay::kRingBytes;
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const char *kp = reinterpret_cast<const char *>(a.k_pages);
+  const char *vp = reinterpret_cast<const char *>(a.v_pages);
+
+  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
+    s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+    s_end = __builtin_amdgcn_readfirstlane(s_end);
+    const int len = __builtin_amdgcn_readfirstlane(attn_len(a, b));
+    const int sel = clampi(a.lens[b], 0, a.len_cap);
+    const int pkvh = kvh / a.unit_div;
+    const int32_t *idx_row = nullptr;
+    if constexpr (SPARSE)
+      idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
+
+    AttnState<__bf16, D, NB> st;
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int R = rb * 16 + r;
+      int i = 0, hl = 0;
+      const bool live = R < a.rows;
+      if (live) {
+        i = R / a.G;
+        hl = R % a.G;
+      }
+      st.lim[rb] = SPARSE ? len - 1 : (live ? len - a.n_q + i : len - 1);
+      const char *qb = reinterpret_cast<const char *>(a.q) +
+                       ((((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl) * D) * 2;
+#pragma unroll
+      for (int c = 0; c < QV; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (live) v = *reinterpret_cast<const u32x4 *>(qb + (32 * c + 8 * g) * 2);
+        st.q[rb][c] = v;
+      }
+      st.m[rb] = kNegInf;
+      st.l[rb] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DPL; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
+    const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
+
+    // this lane's chunk of copy i: token 4i + g, chunk position r (K: global chunk r ^ t)
+    auto issue_rows = [&](int4 rows4, int sl) {
+      lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
+      const int rw[4] = {rows4.x, rows4.y, rows4.z, rows4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * i + g;
+        lds_dma16(kp + (size_t)rw[i] * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma16(vp + (size_t)rw[i] * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
+    };
+    // the step's rows are base .. base + 15 (wave-uniform base): per-lane byte
+    // offsets of the eight copies relative to row `base`
+    auto issue_base = [&](int base, int sl) {
+      lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
+      const char *kb = kp + (size_t)base * (D * 2);
+      const char *vb = vp + (size_t)base * (D * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * i + g;
+        lds_dma16(kb + t * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma16(vb + (4 * i + g) * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
+    };
+    // one step: start the copies of step `ahead`, wait for step s, compute it
+    auto step = [&](auto masked, int s, int sl, auto &&start_ahead) {
+      start_ahead();
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStreamRing - 1) * 8) : "memory");
+      StepRegs<__bf16, D> cur;
+      stream_operands(ring, sl, cur);
+      compute_step<__bf16, D, NB, SPARSE, decltype(masked)::value>(a, st, cur, s, len);
+    };
+    using Plain = std::integral_constant<bool, false>;
+    using Masked = std::integral_constant<bool, true>;
+
+    if constexpr (!SPARSE) {
+      // ------------------------------------------------------------- verify
+      const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+      const int P = a.page_size;
+      const int last = s_end - 1;
+      auto entry_ptr = [&](int s) { return pt + clampi(min(s, last) * kStepTokens / P, 0, a.max_pages - 1); };
+      auto row_from = [&](int entry, int s) {
+        return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + min(s, last) * kStepTokens % P;
+      };
+      int wb = s_begin;
+      int rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
+      int rows_b = row_from(*entry_ptr(wb + kStreamWin + lane), wb + kStreamWin + lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table of a previous segment is free
+      lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
+      auto base_of = [&](int s) {
+        const int d = s - wb;
+        return d < kStreamWin ? __builtin_amdgcn_readlane(rows_a, d) : __builtin_amdgcn_readlane(rows_b, d - kStreamWin);
+      };
+      auto issue_step = [&](int s, int sl) { issue_base(base_of(min(s, last)), sl); };
+      auto ahead = [&](int s) {
+        return [&, s] {
+          if (s - wb == kStreamWin) {
+            // entries of this window were requested kStreamWin steps ago and
+            // waited for since (every step waits for its own copies)
+            wb += kStreamWin;
+            rows_a = rows_b;
+            rows_b = row_from(lds_read_i32(table + 4 * lane), wb + kStreamWin + lane);
+            lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
+          }
+          issue_step(s + kStreamRing - 1, (s + kStreamRing - 1) % kStreamRing);
+        };
+      };
+#pragma unroll
+      for (int i = 0; i < kStreamRing - 1; ++i) issue_step(s_begin + i, (s_begin + i) % kStreamRing);
+      const int plain_end = max(s_begin, min(s_end, first_masked));
+      for (int s = s_begin; s < plain_end; ++s) step(Plain{}, s, s % kStreamRing, ahead(s));
+      for (int s = plain_end; s < s_end; ++s) step(Masked{}, s, s % kStreamRing, ahead(s));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies into the ring or table have landed
+    } else {
+      // -------------------------------------------------------------- draft
+      const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+      const int P = a.page_size;
+      const int tail0 = a.tail_begin ? a.tail_begin[b] : 0;
+      const int last_sel = max(sel - 1, 0);
+      const int pos_cap = a.max_pages * P - 1;
+      for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kSparseSubSteps) {
+        const int sc_end = min(s_end, sc_begin + kSparseSubSteps);
+        const int n_tok = (sc_end - sc_begin) * kStepTokens;
+        // rows of the sub-chunk's tokens; token t of step k at table entry
+        // 16k + 4 (t % 4) + t / 4, so lane g reads tokens g, g+4, g+8, g+12 at 16k + 4g
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous copies have landed
+        for (int t0 = 0; t0 < n_tok; t0 += 64 * kResolveBatch) {
+          int pos[kResolveBatch];
+#pragma unroll
+          for (int i = 0; i < kResolveBatch; ++i) {
+            const int t = clampi(sc_begin * kStepTokens + t0 + 64 * i + lane, 0, len - 1);
+            const int from_idx = idx_row[min(t, last_sel)];
+            pos[i] = clampi(t < sel ? from_idx : tail0 + (t - sel), 0, pos_cap);
+          }
+          int e[kResolveBatch];
+#pragma unroll
+          for (int i = 0; i < kResolveBatch; ++i) e[i] = pt[pos[i] / P];
+#pragma unroll
+          for (int i = 0; i < kResolveBatch; ++i) {
+            const int tt = t0 + 64 * i + lane;
+            if (tt < n_tok) {
+              const int k = tt / kStepTokens, t = tt % kStepTokens;
+              lds_write_i32(table + 4 * (k * kStepTokens + 4 * (t % 4) + t / 4),
+                            (clampi(e[i], 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + pos[i] % P);
+            }
+          }
+        }
+        const int last_k = sc_end - sc_begin - 1;
+        auto issue_step = [&](int k, int sl) {
+          issue_rows(lds_read_i32x4(table + 4 * (min(k, last_k) * kStepTokens + 4 * g)), sl);
+        };
+        auto ahead = [&](int k) { return [&, k] { issue_step(k + kStreamRing - 1, (k + kStreamRing - 1) % kStreamRing); }; };
+#pragma unroll
+        for (int i = 0; i < kStreamRing - 1; ++i) issue_step(i, i % kStreamRing);
+        const int plain_end = max(0, min(last_k + 1, first_masked - sc_begin));
+        for (int k = 0; k < plain_end; ++k) step(Plain{}, sc_begin + k, k % kStreamRing, ahead(k));
+        for (int k = plain_end; k <= last_k; ++k) step(Masked{}, sc_begin + k, k % kStreamRing, ahead(k));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+
+    // Partial of this segment: unnormalised o (relative to m), (m, l) in log2 units.
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int R = rb * 16 + r;
+      const float l = rows4_sum(st.l[rb]);
+      if (R < a.rows) {
+        float *dst = a.part_o + (slot * a.rows + R) * D + 4 * DPL * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float vals[DPL];
+#pragma unroll
+          for (int dt = 0; dt < DPL; ++dt) vals[dt] = st.o[rb][dt][e];
+#pragma unroll
+          for (int v4 = 0; v4 < DPL; v4 += 4)
+            *reinterpret_cast<f32x4 *>(dst + DPL * e + v4) =
+                f32x4{vals[v4], vals[v4 + 1], vals[v4 + 2], vals[v4 + 3]};
+        }
+        if (g == 0) {
+          a.part_ml[(slot * a.rows + R) * 2 + 0] = st.m[rb];
+          a.part_ml[(slot * a.rows + R) * 2 + 1] = l;
+        }
+      }
+    }
+  });
+}
+
 // One wave per output row (b, kvh, R): merge the unit's partials by log-sum-exp.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *out, float *lse,
@@ -513,11 +811,18 @@ WsLayout ws_layout(int64_t B, int64_t Hkv, int64_t rows, int64_t D) {
 
 template <typename T, int D, int NB, bool SPARSE>
 sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
+  // bf16 with head_dim 128 streams K/V through the LDS ring; fp32 caches and
+  // head_dim 64 use the register ring
+  constexpr bool kStream = EltInfo<T>::bytes == 2 && D == 128;
+  const void *kernel = kStream ? reinterpret_cast<const void *>(attn_stream_kernel<NB, SPARSE>)
+                               : reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>);
   static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
-  a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>),
-                                   kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
+  a.sc.waves = sdh::resident_waves(kernel, kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
   attn_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
-  attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  if constexpr (kStream)
+    attn_stream_kernel<NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  else
+    attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   const int total_rows = a.B * a.Hkv * a.rows;
   attn_combine_kernel<T, D><<<(total_rows + 3) / 4, 256, 0, st>>>(a, out, lse, total_rows);
   return sdh::launch_status();

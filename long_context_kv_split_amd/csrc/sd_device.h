@@ -85,4 +85,24 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Asynchronous copies of 16 or 4 bytes per lane from global memory to LDS at
+// dst + lane * size (dst is wave-uniform). They hold no registers while in
+// flight and count in the vector-memory counter like any load. The builtin
+// exists only for the device target; a host pass that sees it drops the
+// kernels that use it. The 16-byte copies stream the KV cache and carry the
+// nontemporal cache policy (bit 1 of the policy operand).
+__device__ __forceinline__ void lds_dma16(const void *src, __attribute__((address_space(3))) void *dst) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+#endif
+}
+__device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address_space(3))) void *dst) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+#endif
+}
+
 }  // namespace sdk

@@ -112,24 +112,6 @@ constexpr int kWinSteps = 64;  // steps per row-id window (lane i holds the firs
 constexpr int kStageSteps = 32;  // votes staged in LDS and stored every 32 steps
 constexpr float kHeadroom = 8.f;  // log2 slack of the lazily moved row max in the stats pass
 
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-
-// Asynchronous copies of 16 or 4 bytes per lane from global memory to LDS at
-// dst + lane * size (dst is wave-uniform). The builtin exists only for the
-// device target; a host pass that sees it drops the kernels that use it. The
-// 16-byte copies stream K and carry the nontemporal cache policy (bit 1 of
-// the policy operand).
-__device__ __forceinline__ void lds_dma16(const void *src, __attribute__((address_space(3))) void *dst) {
-#if __HIP_DEVICE_COMPILE__
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
-#endif
-}
-__device__ __forceinline__ void lds_dma4(const void *src, __attribute__((address_space(3))) void *dst) {
-#if __HIP_DEVICE_COMPILE__
-  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
-#endif
-}
-
 // Two 16-byte LDS reads at byte_off and byte_off + gap (gap an immediate
 // offset), untracked by the compiler like the word accesses below; they
 // return with their data.
