@@ -8,13 +8,14 @@
 // (verify) or from 16 entries of a selection list (draft).
 //
 // Schedule (persistent split-KV): the launch has exactly as many waves as the
-// chip keeps resident for the instantiation. A plan kernel turns the device
-// lengths into prefix sums; wave w then takes the w-th equal share of the
+// chip keeps resident for the instantiation. Each wave scans the device
+// lengths itself (no plan launch) and takes the w-th equal share of the
 // flattened (sequence, KV head, step) space, so the work is balanced to one
 // step whatever the length mix, and writes one (m, l, o) partial per unit
 // segment it covers into a slot table of at most waves + units entries. The
 // assignment depends only on shapes and lengths, so results are bitwise
-// reproducible. A combine kernel merges each unit's partials by log-sum-exp.
+// reproducible. A combine kernel merges each unit's partials by log-sum-exp;
+// the call is two launches.
 //
 // Per step a wave computes S^T = K Q^T with 16x16x32 bf16 MFMA (tokens on M,
 // the G*n_q query rows of the KV head on N, padded to NB tiles of 16), applies
@@ -334,8 +335,12 @@ __device__ __forceinline__ int unit_steps(const AttnParams &a, int b) {
   return (attn_len(a, b) + kStepTokens - 1) / kStepTokens;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams a) {
-  sched_plan(a.sc, [&](int b) { return unit_steps(a, b); });
+// Each wave of a split kernel finds its own unit segments (no plan kernel);
+// wave 0 also writes the per-sequence step prefix the combine reads.
+template <class F>
+__device__ __forceinline__ void attn_for_each_segment(const AttnParams &a, F &&f) {
+  sched_inline_for_each_segment(a.B, a.Hkv, a.sc.waves, blockIdx.x, [&](int b) { return unit_steps(a, b); },
+                                blockIdx.x == 0 ? a.sc.seq_prefix : nullptr, f);
 }
 
 template <typename T, int D, int NB, bool SPARSE>
@@ -349,7 +354,7 @@ void attn_split_kernel(AttnParams a) {
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
 
-  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
+  attn_for_each_segment(a, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     const int len = attn_len(a, b);
     const int sel = clampi(a.lens[b], 0, a.len_cap);  // draft: entries of idx read before the tail
     const int pkvh = kvh / a.unit_div;                // pool head of the unit
@@ -562,7 +567,7 @@ void attn_stream_kernel(AttnParams a) {
   const char *kp = reinterpret_cast<const char *>(a.k_pages);
   const char *vp = reinterpret_cast<const char *>(a.v_pages);
 
-  sched_for_each_segment(a.sc, blockIdx.x, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
+  attn_for_each_segment(a, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     s_begin = __builtin_amdgcn_readfirstlane(s_begin);
     s_end = __builtin_amdgcn_readfirstlane(s_end);
     const int len = __builtin_amdgcn_readfirstlane(attn_len(a, b));
@@ -759,7 +764,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
   const int u = wave / a.rows;
   const int kvh = u % a.Hkv;
   const int b = u / a.Hkv;
-  const int s0 = a.sc.slot_base[u], s1 = a.sc.slot_base[u + 1];
+  int s0, s1;
+  sched_inline_unit_slots(a.sc.seq_prefix, a.B, a.Hkv, a.sc.waves, b, kvh, s0, s1);
 
   float M = kNegInf;
   for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_ml[((size_t)s * a.rows + R) * 2]);
@@ -818,7 +824,6 @@ sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
                                : reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>);
   static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(kernel, kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
-  attn_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
   if constexpr (kStream)
     attn_stream_kernel<NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   else

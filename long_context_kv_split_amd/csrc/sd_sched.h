@@ -147,6 +147,93 @@ __device__ __forceinline__ void sched_for_each_segment(const Sched &s, int64_t w
   }
 }
 
+// Inclusive wave scan of int64 values (lane order).
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The same partition as sched_for_each_segment without a plan kernel: wave
+// w scans the per-sequence step counts 64 at a time, first for the total T,
+// then up to the end of its own range, and visits f(b, kvh, s_begin, s_end,
+// slot) for each unit segment it owns. A unit's partials go to slots
+// w + u (u = b * Hkv + kvh) for the waves w in [lo(u), hi(u)] that own its
+// steps: consecutive units' wave ranges share at most one wave, so these
+// runs never overlap, and every slot is below W + U. When prefix_out is set
+// (one wave of the launch), it receives the exclusive step prefix per
+// sequence and the total at [B] for the combine.
+template <class StepsFn, class F>
+__device__ __forceinline__ void sched_inline_for_each_segment(int B, int Hkv, int waves, int64_t w, StepsFn steps,
+                                                              int32_t *prefix_out, F &&f) {
+  const int lane = lane_id();
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int64_t n = b < B ? (int64_t)steps(b) : 0;
+    const int64_t incl = wave_incl_scan_i64(n);
+    if (prefix_out != nullptr && b < B) prefix_out[b] = (int32_t)(carry + incl - n);
+    carry += readlane_i64(incl, 63);
+  }
+  if (prefix_out != nullptr && lane == 0) prefix_out[B] = (int32_t)carry;
+  const int64_t T = (int64_t)Hkv * carry;
+  if (T == 0) return;
+  const int64_t W = max<int64_t>(1, min<int64_t>(waves, (T + kMinStepsPerWave - 1) / kMinStepsPerWave));
+  if (w >= W) return;
+  const int64_t t_begin = (w * T + W - 1) / W;
+  const int64_t t_end = ((w + 1) * T + W - 1) / W;
+  if (t_begin >= t_end) return;
+  carry = 0;
+  for (int b0 = 0; b0 < B && (int64_t)Hkv * carry < t_end; b0 += 64) {
+    const int b = b0 + lane;
+    const int64_t n = b < B ? (int64_t)steps(b) : 0;
+    const int64_t incl = wave_incl_scan_i64(n);
+    const int64_t base = (int64_t)Hkv * (carry + incl - n), end = (int64_t)Hkv * (carry + incl);
+    uint64_t hit = __ballot(b < B && n > 0 && end > t_begin && base < t_end);
+    while (hit != 0) {
+      const int j = (int)__builtin_ctzll(hit);
+      hit &= hit - 1;
+      const int bb = b0 + j;
+      const int64_t nb = readlane_i64(n, j);
+      const int64_t base_b = readlane_i64(base, j);
+      for (int kvh = (int)max<int64_t>(0, (t_begin - base_b) / nb); kvh < Hkv; ++kvh) {
+        const int64_t A = base_b + (int64_t)kvh * nb;
+        if (A >= t_end) break;
+        const int64_t sb = max(t_begin, A), se = min(t_end, A + nb);
+        if (sb < se) f(bb, kvh, (int)(sb - A), (int)(se - A), (size_t)(w + (int64_t)bb * Hkv + kvh));
+      }
+    }
+    carry += readlane_i64(incl, 63);
+  }
+}
+
+// Partial slots [s0, s1) of unit (b, kvh) under sched_inline_for_each_segment,
+// from the per-sequence prefix it wrote (empty when the unit has no steps).
+__device__ __forceinline__ void sched_inline_unit_slots(const int32_t *prefix, int B, int Hkv, int waves, int b,
+                                                        int kvh, int &s0, int &s1) {
+  const int64_t T = (int64_t)Hkv * prefix[B];
+  const int64_t n = prefix[b + 1] - prefix[b];
+  s0 = s1 = 0;
+  if (T == 0 || n == 0) return;
+  const int64_t W = max<int64_t>(1, min<int64_t>(waves, (T + kMinStepsPerWave - 1) / kMinStepsPerWave));
+  const int64_t A = (int64_t)Hkv * prefix[b] + (int64_t)kvh * n;
+  int64_t lo, hi;
+  sched_unit_waves(A, n, T, W, lo, hi);
+  const int64_t u = (int64_t)b * Hkv + kvh;
+  s0 = (int)(lo + u);
+  s1 = (int)(hi + u + 1);
+}
+
 }  // namespace sdk
 
 namespace sdh {
