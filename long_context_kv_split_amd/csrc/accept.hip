@@ -154,12 +154,13 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return v;
 }
 
-// The finishing kernel: one 1024-thread block per sequence. In vocabulary
-// order the drawn row is cut into iterations of kFinSpan entries; wave wv
-// owns entries [e * kFinSpan + wv * kWaveSpan, + kWaveSpan) of iteration e,
-// lane l four consecutive ones. A "slot" is G consecutive iterations of one
-// wave (G = 1 up to a million entries), so (slot, wave) pieces are in
-// vocabulary order and their sums fit in LDS.
+// The finishing kernel: one 1024-thread block per sequence. The drawn row is
+// cut into slots of G * kFinSpan entries (G = 1 up to a million entries), and
+// slot k into one piece of G * kWaveSpan consecutive entries per wave: wave
+// wv owns [k G kFinSpan + wv G kWaveSpan, + G kWaveSpan), which it reads in G
+// iterations of kWaveSpan entries (lane l four consecutive ones). Pieces
+// ordered by (slot, wave) are therefore in vocabulary order, and their sums
+// fit in LDS. Entries past the row read as zero weight.
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinEnt = 4;                       // consecutive entries per lane and iteration
@@ -199,6 +200,12 @@ __device__ __forceinline__ void draw_load(const AccParams &a, const float *zp, c
   }
 }
 
+// First entry of lane `lane` of wave wv in iteration e (G iterations per slot).
+__device__ __forceinline__ int fin_entry(int e, int G, int wv, int lane) {
+  const int k = e / G;
+  return k * G * kFinSpan + wv * G * kWaveSpan + (e - k * G) * kWaveSpan + kFinEnt * lane;
+}
+
 struct Offset {
   float hi, lo;
 };
@@ -230,7 +237,6 @@ template <int VEC, bool RESID>
 __device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, const float *zq, Offset cp,
                                           Offset cq, int iters, int G, double *seg) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  const int t_lane = wv * kWaveSpan + kFinEnt * lane;
   int last = -1;
   double gsum = 0.0;
   struct Buf {
@@ -238,14 +244,14 @@ __device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, c
   };
   auto fetch = [&](int e0, Buf &bf) {
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) draw_load<VEC, RESID>(a, zp, zq, (e0 + u) * kFinSpan + t_lane, bf.p[u], bf.q[u]);
+    for (int u = 0; u < kFinUnroll; ++u) draw_load<VEC, RESID>(a, zp, zq, fin_entry(e0 + u, G, wv, lane), bf.p[u], bf.q[u]);
   };
   auto consume = [&](int e0, const Buf &bf) {
 #pragma unroll
     for (int u = 0; u < kFinUnroll; ++u) {
       const int e = e0 + u;
       if (e < iters) {
-        const int t = e * kFinSpan + t_lane;
+        const int t = fin_entry(e, G, wv, lane);
         float w[kFinEnt];
         draw_weights<RESID>(a, cp, cq, t, bf.p[u], bf.q[u], w);
         double s = 0.0;
@@ -255,7 +261,7 @@ __device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, c
           if (w[j] > 0.f) last = t + j;
         }
         gsum += wave_sum_f64(s);
-        if ((e + 1) % G == 0 || e == iters - 1) {
+        if ((e + 1) % G == 0) {
           if (lane == 0) seg[(e / G) * kFinWaves + wv] = gsum;
           gsum = 0.0;
         }
@@ -279,12 +285,12 @@ __device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, c
 // token with mass.
 template <int VEC, bool RESID>
 __device__ __forceinline__ int draw_rescan(const AccParams &a, const float *zp, const float *zq, Offset cp,
-                                           Offset cq, int e_begin, int e_end, double before, double thr,
+                                           Offset cq, int e_begin, int e_end, int G, double before, double thr,
                                            int *seg_last) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   int y = -1, sl = -1;
   for (int e = e_begin; e < e_end && y < 0; ++e) {
-    const int t = e * kFinSpan + wv * kWaveSpan + kFinEnt * lane;
+    const int t = fin_entry(e, G, wv, lane);
     float zpv[kFinEnt], zqv[kFinEnt], w[kFinEnt];
     draw_load<VEC, RESID>(a, zp, zq, t, zpv, zqv);
     draw_weights<RESID>(a, cp, cq, t, zpv, zqv, w);
@@ -304,7 +310,7 @@ __device__ __forceinline__ int draw_rescan(const AccParams &a, const float *zp, 
     const uint64_t h = __ballot(hj < kFinEnt);
     if (h != 0) {
       const int l = (int)__builtin_ctzll(h);
-      y = e * kFinSpan + wv * kWaveSpan + kFinEnt * l + __shfl(hj, l, 64);
+      y = fin_entry(e, G, wv, l) + __shfl(hj, l, 64);
     }
     before += __shfl(inc, 63, 64);
   }
@@ -378,9 +384,10 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a)
   const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
   const Offset cp = split_offset(lse[n]);
   const Offset cq = split_offset(n < g ? lse[g + 1 + n] : 0.0);
-  const int iters = (a.V + kFinSpan - 1) / kFinSpan;
-  const int G = (iters + kFinSlots - 1) / kFinSlots;  // iterations per slot
-  const int nslots = (iters + G - 1) / G;
+  const int row_iters = (a.V + kFinSpan - 1) / kFinSpan;
+  const int G = (row_iters + kFinSlots - 1) / kFinSlots;  // iterations per slot
+  const int nslots = (row_iters + G - 1) / G;
+  const int iters = nslots * G;  // whole slots; entries past the row weigh zero
   const int npieces = nslots * kFinWaves;
 
   // 3. One sweep over the drawn row: (slot, wave) sums in LDS, and the last
@@ -448,10 +455,10 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a)
     if (wv == pw) {
       // the owning wave reloads its entries of the slot's iterations and
       // scans them in vocabulary order
-      const int e_end = min(iters, (slot + 1) * G);
+      const int e_end = (slot + 1) * G;
       int seg_last = -1;
-      y = residual ? draw_rescan<VEC, true>(a, zp, zq, cp, cq, slot * G, e_end, before_s, thr, &seg_last)
-                   : draw_rescan<VEC, false>(a, zp, zq, cp, cq, slot * G, e_end, before_s, thr, &seg_last);
+      y = residual ? draw_rescan<VEC, true>(a, zp, zq, cp, cq, slot * G, e_end, G, before_s, thr, &seg_last)
+                   : draw_rescan<VEC, false>(a, zp, zq, cp, cq, slot * G, e_end, G, before_s, thr, &seg_last);
       // rounding left no crossing inside the piece: its last token with mass
       if (y < 0) y = seg_last;
       if (y < 0) y = glast;

@@ -68,6 +68,9 @@ def test_golden_cases_on_gpu():
     (64, 4, 128256, 2.0, 0.5, 1.0),         # 70B-vocabulary workload at full size
     (300, 0, 777, 2.0, None, 1.0),          # gamma = 0: bonus token only
     (33, 7, 9000, 2.0, 0.25, 1.0),          # long draft, ~90% acceptance
+    (96, 3, 1001, 2.0, 0.5, 1.0),           # odd vocabulary: 4-byte loads, ragged last entries
+    (40, 2, 3, 1.0, 0.5, 1.0),              # vocabulary smaller than one 16-byte load
+    (20, 4, 1048579, 2.0, 0.5, 1.0),        # over a million entries: several iterations per LDS slot
 ])
 def test_accept_parity(B, gamma, V, std, noise, temp):
     say(f"accept B={B} gamma={gamma} V={V} noise={noise} temp={temp}")
