@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-units", type=int, default=0,
-                    help="(sequence, kv head) units the oracle runs (0 = 96 units, ~13 s)")
+                    help="(sequence, kv head) units the oracle runs (0 = 80 units, about 12 s)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-round", action="store_true",
                     help="skip the round and per-sequence-budget measurements")
@@ -778,7 +778,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        n_units = args.cpu_sample_units or 64
+        n_units = args.cpu_sample_units or 80
         log(f"cpu baseline: oracle on {n_units} units ...")
         cpu = cpu_baseline(wl, n_units)
         log(f"cpu baseline {cpu['value']:.3e} KV tokens/s in {cpu['seconds']} s; select "
