@@ -110,6 +110,7 @@ struct SnapParams {
 constexpr int kRing = 4;       // 16-key K steps per wave in LDS: 3 loading while one is scored
 constexpr int kWinSteps = 64;  // steps per row-id window (lane i holds the first row of step i)
 constexpr int kStageSteps = 32;  // votes staged in LDS and stored every 32 steps
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 constexpr float kHeadroom = 8.f;  // log2 slack of the lazily moved row max in the stats pass
 
 // Two 16-byte LDS reads at byte_off and byte_off + gap (gap an immediate
@@ -467,15 +468,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     // (g, r) holds rows 16*rb + 4g + e of key r, so a key's vote is an in-lane
     // sum over (rb, e) plus a sum over the four lane groups. off[rb][e]: max +
     // log2(sum) of that row (+inf for padding rows: p = 0).
+    // The unit's segment statistics (many slots when a few units are spread
+    // over all waves) are merged by the four lanes of each row, lane group g
+    // taking slots s0 + g, s0 + g + 4, ..., with the loads of kMergeBatch slots
+    // per lane issued together (addresses clamped, values masked), then merged
+    // across the groups; every wave of the unit merges in the same order.
+    constexpr int kMergeBatch = 4;
+    float mm[NB], ll[NB];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      mm[rb] = kNegInf;
+      ll[rb] = 0.f;
+    }
+    const int n_slots = s1 - s0;  // >= 1: this wave holds one of them
+    for (int base = 0; base < n_slots; base += 4 * kMergeBatch) {
+      f32x2 v[kMergeBatch][NB];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int s = s0 + min(base + 4 * i + g, n_slots - 1);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          const int R = min(rb * 16 + r, a.rows - 1);
+          v[i][rb] = *reinterpret_cast<const f32x2 *>(a.stats + ((size_t)s * a.rows + R) * 2);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (base + 4 * i + g < n_slots) {
+#pragma unroll
+          for (int rb = 0; rb < NB; ++rb) merge_ml(mm[rb], ll[rb], v[i][rb].x, v[i][rb].y);
+        }
+      }
+    }
     float off[NB][4];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const int R = rb * 16 + r;
-      float mm = kNegInf, ll = 0.f;
-      if (R < a.rows)
-        for (int s = s0; s < s1; ++s) merge_ml(mm, ll, a.stats[((size_t)s * a.rows + R) * 2],
-                                               a.stats[((size_t)s * a.rows + R) * 2 + 1]);
-      const float o = (ll > 0.f) ? mm + __log2f(ll) : __builtin_inff();  // row R, held by lanes r
+      rows4_merge(mm[rb], ll[rb]);
+      const bool live = rb * 16 + r < a.rows;
+      const float o = (live && ll[rb] > 0.f) ? mm[rb] + __log2f(ll[rb]) : __builtin_inff();  // row 16 rb + r
 #pragma unroll
       for (int e = 0; e < 4; ++e) off[rb][e] = __shfl(o, 4 * g + e, 64);
     }
