@@ -295,7 +295,7 @@ size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab
  * stream must belong to the current device (else SD_ERR_INVALID_ARG).
  * Limits: as sd_spec_accept, and sd_spec_accept_workspace_size(batch, gamma,
  *   vocab) <= SD_SPEC_ACCEPT_SCRATCH_BYTES, else SD_ERR_UNSUPPORTED (about
- *   1800 sequences at gamma = 4 over a 128256-token vocabulary).
+ *   960 sequences at gamma = 4 over a 128256-token vocabulary).
  */
 #define SD_SPEC_ACCEPT_SCRATCH_BYTES (4u << 20)
 

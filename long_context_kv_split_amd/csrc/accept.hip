@@ -5,21 +5,23 @@
 // distributions, correct from the residual target distribution at the first
 // rejection, or draw a bonus token from the target when all are accepted.
 //
-// Two kernels; the logits are streamed once, plus the one or two rows the
+// Three kernels; the logits are streamed once, plus the one or two rows the
 // draw needs:
-//   accept_stats:  one block per (row, vocab chunk) of the 2*gamma+1 rows of
-//                  every sequence: chunk max of z/t and the sum of exp(z/t -
-//                  max) (fp32 exponentials, fp64 sums; each thread keeps its
-//                  own running max, merged once at the end);
-//   accept_finish: one 1024-thread block per sequence: its waves merge the
-//                  chunk statistics of each row into log-normalisers (fp64),
-//                  wave 0 evaluates u_i q_i(x_i) < p_i(x_i) for every draft
-//                  (fp64; n = the first failure), then the block streams the
-//                  drawn row pair once, residual weights max(0, p_n - q_n) (or
-//                  p_gamma) summed per (slot, wave) piece in vocabulary order
-//                  into LDS (fp64), scans the piece sums for the one holding
-//                  u*Z, and the wave owning that piece rescans it for the
-//                  token.
+//   accept_stats:    one block per (row, vocab chunk) of the 2*gamma+1 rows of
+//                    every sequence: chunk max of z/t and the sum of exp(z/t -
+//                    max) (fp32 exponentials, fp64 sums; each thread keeps its
+//                    own running max, merged once at the end);
+//   accept_residual: one block per (sequence, slice of the vocabulary): the
+//                    block merges the sequence's chunk statistics into row
+//                    log-normalisers (fp64), evaluates u_i q_i(x_i) < p_i(x_i)
+//                    for every draft (fp64; n = the first failure), and sums
+//                    the weights of the drawn row pair over its slice, per
+//                    1024-entry piece, in fp64: max(0, p_n - q_n) and p_n, or
+//                    p_gamma. Several blocks per sequence spread the drawn row
+//                    over the CUs (one CU streams a row at a few tens of GB/s);
+//   accept_draw:     one block per sequence scans the piece sums in vocabulary
+//                    order for the piece holding u*Z and rescans that piece for
+//                    the token.
 #include "sd_device.h"
 #include "sd_host.h"
 
@@ -43,7 +45,11 @@ struct AccParams {
   int32_t *n_accepted;
   int32_t *out_tokens;
   double *stats;      // [B, 2*gamma+1, n_chunks, 2]  (max, sum)
+  double *pieces;     // [B, 2, npieces]: weight sums per piece, residual (0) and p_n (1)
+  double *seq_lse;    // [B, 2]: normalisers of the drawn pair (p_n, q_n)
+  int32_t *seq_n;     // [B]: accepted drafts
   int32_t B, gamma, V, n_chunks;
+  int32_t npieces, pps;  // pieces per row, pieces per residual slice
   float inv_temp;
   double inv_temp_d;
 };
@@ -95,6 +101,9 @@ __device__ __forceinline__ void load_chunk(const float *z, int t0, int V, float 
   }
 }
 
+// One block per (row, chunk): the chunk's max of z/t (exact, float), then the
+// sum of exp(z/t - wave max) per wave (fp32 exponentials, fp64 sums), the
+// waves' (max, sum) pairs merged once by thread 0.
 template <int VEC>
 __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) {
   __shared__ float lds_m[kAccThreads / 64];
@@ -109,6 +118,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) 
   float m = kNegInf;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) m = fmaxf(m, x[e]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   double s = 0.0;
   if (m != kNegInf) {
     double s4[4] = {0.0, 0.0, 0.0, 0.0};  // four independent fp64 chains
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) 
     s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) merge_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     lds_m[wave] = m;
@@ -154,57 +165,19 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return v;
 }
 
-// The finishing kernel: one 1024-thread block per sequence. The drawn row is
-// cut into slots of G * kFinSpan entries (G = 1 up to a million entries), and
-// slot k into one piece of G * kWaveSpan consecutive entries per wave: wave
-// wv owns [k G kFinSpan + wv G kWaveSpan, + G kWaveSpan), which it reads in G
-// iterations of kWaveSpan entries (lane l four consecutive ones). Pieces
-// ordered by (slot, wave) are therefore in vocabulary order, and their sums
-// fit in LDS. Entries past the row read as zero weight.
-constexpr int kFinThreads = 1024;
-constexpr int kFinWaves = kFinThreads / 64;
-constexpr int kFinEnt = 4;                       // consecutive entries per lane and iteration
-constexpr int kWaveSpan = 64 * kFinEnt;          // 256
-constexpr int kFinSpan = kFinThreads * kFinEnt;  // 4096
-constexpr int kFinSlots = 256;                   // slots per wave held in LDS
-constexpr int kFinUnroll = 4;                    // iterations per pipelined batch of loads
-
-// Weights of entries t..t+3 (t a multiple of 4) of the drawn row:
-// max(0, p - q) (RESID) or p, p(t) = exp(z_t / T - lse). The fp64 normaliser
-// enters as an fp32 pair (hi + lo = lse to about 2^-48 relative), so it
-// carries no systematic fp32 rounding (that would scale p and q by different
-// constants, an error that does not cancel in p - q); the exponent itself is
-// formed in fp32 with one fused multiply-add, rounded per token like the
-// final exponential.
-// Loads are unconditional (clamped into the row, masked afterwards).
-template <int VEC, bool RESID>
-__device__ __forceinline__ void draw_load(const AccParams &a, const float *zp, const float *zq, int t,
-                                          float (&zpv)[kFinEnt], float (&zqv)[kFinEnt]) {
-  if constexpr (VEC == 4) {
-    const int tc = min(t, a.V - 4);
-    const f32x4 pv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zp + tc));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zpv[j] = pv[j];
-    if constexpr (RESID) {
-      const f32x4 qv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zq + tc));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) zqv[j] = qv[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tc = min(t + j, a.V - 1);
-      zpv[j] = zp[tc];
-      if constexpr (RESID) zqv[j] = zq[tc];
-    }
-  }
-}
-
-// First entry of lane `lane` of wave wv in iteration e (G iterations per slot).
-__device__ __forceinline__ int fin_entry(int e, int G, int wv, int lane) {
-  const int k = e / G;
-  return k * G * kFinSpan + wv * G * kWaveSpan + (e - k * G) * kWaveSpan + kFinEnt * lane;
-}
+// Residual and draw kernels. The drawn row (the residual max(0, p_n - q_n)
+// after a rejection, p_gamma when every draft is accepted) is cut into pieces
+// of kPiece consecutive entries; lane l of the wave that owns a piece reads
+// entries 256 j + 4 l .. 256 j + 4 l + 3 of it (j = 0..3), so each of its
+// loads is one contiguous 1 KB row segment across the wave. Entries past the
+// row weigh zero.
+constexpr int kResThreads = 256;
+constexpr int kResWaves = kResThreads / 64;
+constexpr int kPieceLoads = 4;                // 16-byte loads per lane, row and piece
+constexpr int kPiece = 64 * 4 * kPieceLoads;  // 1024 entries
+constexpr int kTargetBlocks = 1024;           // residual blocks per call (sequences x slices)
+constexpr int kDrawThreads = 256;
+constexpr int kDrawPer = 4;  // piece sums per thread and round of the draw's scan
 
 struct Offset {
   float hi, lo;
@@ -214,121 +187,128 @@ __device__ __forceinline__ Offset split_offset(double c) {
   return Offset{hi, (float)(c - (double)hi)};
 }
 
-template <bool RESID>
-__device__ __forceinline__ void draw_weights(const AccParams &a, Offset cp, Offset cq, int t,
-                                             const float (&zpv)[kFinEnt], const float (&zqv)[kFinEnt],
-                                             float (&w)[kFinEnt]) {
+// Weights of the entries t .. t+3 (t = piece base + 256 j + 4 lane):
+// p = exp(z_t / T - lse_p), and max(0, p - q) (RESID). The fp64 normaliser
+// enters as an fp32 pair (hi + lo = lse to about 2^-48 relative), so it
+// carries no systematic fp32 rounding (that would scale p and q by different
+// constants, an error that does not cancel in p - q); the exponent itself is
+// formed in fp32, rounded per token like the final exponential. Loads are
+// unconditional (clamped into the row, masked afterwards).
+template <int VEC, bool RESID>
+__device__ __forceinline__ void piece_load(const AccParams &a, const float *zp, const float *zq, int t,
+                                           float (&zpv)[4], float (&zqv)[4]) {
+  if constexpr (VEC == 4) {
+    const int tc = min(t, a.V - 4);
+    const f32x4 pv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zp + tc));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float p = __builtin_amdgcn_exp2f((fmaf(zpv[j], a.inv_temp, -cp.hi) - cp.lo) * kLog2e);
+    for (int e = 0; e < 4; ++e) zpv[e] = pv[e];
+    if constexpr (RESID) {
+      const f32x4 qv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(zq + tc));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zqv[e] = qv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tc = min(t + e, a.V - 1);
+      zpv[e] = zp[tc];
+      if constexpr (RESID) zqv[e] = zq[tc];
+    }
+  }
+}
+
+// p weights (pw) and, with RESID, residual weights (rw) of entries t .. t+3.
+template <bool RESID>
+__device__ __forceinline__ void piece_weights(const AccParams &a, Offset cp, Offset cq, int t,
+                                              const float (&zpv)[4], const float (&zqv)[4], float (&pw)[4],
+                                              float (&rw)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p = __builtin_amdgcn_exp2f((fmaf(zpv[e], a.inv_temp, -cp.hi) - cp.lo) * kLog2e);
     float r = p;
     if constexpr (RESID)
-      r = fmaxf(0.f, p - __builtin_amdgcn_exp2f((fmaf(zqv[j], a.inv_temp, -cq.hi) - cq.lo) * kLog2e));
-    w[j] = t + j < a.V ? r : 0.f;
+      r = fmaxf(0.f, p - __builtin_amdgcn_exp2f((fmaf(zqv[e], a.inv_temp, -cq.hi) - cq.lo) * kLog2e));
+    const bool in = t + e < a.V;
+    pw[e] = in ? p : 0.f;
+    rw[e] = in ? r : 0.f;
   }
 }
 
-// One sweep over the drawn row: the (slot, wave) piece sums into seg, and the
-// last entry with mass of this thread. Software-pipelined: the loads of the
-// next kFinUnroll iterations are in flight while the current ones are
-// summed (two register buffers used alternately; loads past the row are
-// clamped into it and their results dropped).
-template <int VEC, bool RESID>
-__device__ __forceinline__ int draw_sweep(const AccParams &a, const float *zp, const float *zq, Offset cp,
-                                          Offset cq, int iters, int G, double *seg) {
+// Row normalisers of sequence b into lse[0 .. 2 gamma] (max of the chunk
+// maxima, then the rescaled sum, fp64). Each row is merged by a group of L
+// lanes (L = the chunk count rounded up to a power of two, at most 64), so a
+// wave merges 64 / L rows at once: the rows' loads go out together and the
+// group reductions are log2(L) steps.
+template <int WAVES>
+__device__ __forceinline__ void row_normalisers(const AccParams &a, int b, double *lse) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-  int last = -1;
-  double gsum = 0.0;
-  struct Buf {
-    float p[kFinUnroll][kFinEnt], q[kFinUnroll][kFinEnt];
-  };
-  auto fetch = [&](int e0, Buf &bf) {
+  const int nrow = 2 * a.gamma + 1;
+  int L = 1;
+  while (L < a.n_chunks && L < 64) L <<= 1;
+  const int rpw = 64 / L, sub = lane & (L - 1);
+  for (int k0 = wv * rpw; k0 < nrow; k0 += WAVES * rpw) {
+    const int k = k0 + lane / L;
+    const double *st = a.stats + ((size_t)b * nrow + min(k, nrow - 1)) * a.n_chunks * 2;
+    double M = -__builtin_inf();
+    for (int c = sub; c < a.n_chunks; c += L) M = fmax(M, st[2 * c]);
+    for (int m = 1; m < L; m <<= 1) M = fmax(M, __shfl_xor(M, m, 64));
+    double l = 0.0;
+    for (int c = sub; c < a.n_chunks; c += L)
+      if (st[2 * c] != -__builtin_inf()) l += st[2 * c + 1] * exp(st[2 * c] - M);
+    for (int m = 1; m < L; m <<= 1) l += __shfl_xor(l, m, 64);
+    if (k < nrow && sub == 0) lse[k] = M + log(l);
+  }
+}
+
+// Pieces [p0, p1) of the drawn row, one wave per piece: the fp64 sum of the
+// p weights of each piece into a.pieces (kind 1) and, with RESID, of the
+// residual weights (kind 0).
+template <int VEC, bool RESID>
+__device__ __forceinline__ void residual_pieces(const AccParams &a, int b, const float *zp, const float *zq,
+                                                Offset cp, Offset cq, int p0, int p1) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  double *pr = a.pieces + ((size_t)b * 2 + 0) * a.npieces;
+  double *pp = a.pieces + ((size_t)b * 2 + 1) * a.npieces;
+  for (int p = p0 + wv; p < p1; p += kResWaves) {
+    const int t0 = p * kPiece + 4 * lane;
+    float zpv[kPieceLoads][4], zqv[kPieceLoads][4];
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) draw_load<VEC, RESID>(a, zp, zq, fin_entry(e0 + u, G, wv, lane), bf.p[u], bf.q[u]);
-  };
-  auto consume = [&](int e0, const Buf &bf) {
+    for (int j = 0; j < kPieceLoads; ++j) piece_load<VEC, RESID>(a, zp, zq, t0 + 256 * j, zpv[j], zqv[j]);
+    double sp = 0.0, sr = 0.0;
 #pragma unroll
-    for (int u = 0; u < kFinUnroll; ++u) {
-      const int e = e0 + u;
-      if (e < iters) {
-        const int t = fin_entry(e, G, wv, lane);
-        float w[kFinEnt];
-        draw_weights<RESID>(a, cp, cq, t, bf.p[u], bf.q[u], w);
-        double s = 0.0;
+    for (int j = 0; j < kPieceLoads; ++j) {
+      float pw[4], rw[4];
+      piece_weights<RESID>(a, cp, cq, t0 + 256 * j, zpv[j], zqv[j], pw, rw);
 #pragma unroll
-        for (int j = 0; j < kFinEnt; ++j) {
-          s += (double)w[j];
-          if (w[j] > 0.f) last = t + j;
-        }
-        gsum += wave_sum_f64(s);
-        if ((e + 1) % G == 0) {
-          if (lane == 0) seg[(e / G) * kFinWaves + wv] = gsum;
-          gsum = 0.0;
-        }
+      for (int e = 0; e < 4; ++e) {
+        sp += (double)pw[e];
+        if constexpr (RESID) sr += (double)rw[e];
       }
     }
-  };
-  Buf A, B;
-  fetch(0, A);
-  for (int e0 = 0; e0 < iters; e0 += 2 * kFinUnroll) {
-    fetch(min(e0 + kFinUnroll, iters), B);
-    consume(e0, A);
-    if (e0 + kFinUnroll >= iters) break;
-    fetch(min(e0 + 2 * kFinUnroll, iters), A);
-    consume(e0 + kFinUnroll, B);
+    // two independent wave sums, interleaved
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      sp += __shfl_xor(sp, m, 64);
+      if constexpr (RESID) sr += __shfl_xor(sr, m, 64);
+    }
+    if (lane == 0) {
+      pp[p] = sp;
+      if constexpr (RESID) pr[p] = sr;
+    }
   }
-  return last;
 }
 
-// The owning wave's rescan of piece (slot, wave): the first token with mass
-// whose cumulative weight exceeds thr, or -1; *seg_last gets the piece's last
-// token with mass.
-template <int VEC, bool RESID>
-__device__ __forceinline__ int draw_rescan(const AccParams &a, const float *zp, const float *zq, Offset cp,
-                                           Offset cq, int e_begin, int e_end, int G, double before, double thr,
-                                           int *seg_last) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  int y = -1, sl = -1;
-  for (int e = e_begin; e < e_end && y < 0; ++e) {
-    const int t = fin_entry(e, G, wv, lane);
-    float zpv[kFinEnt], zqv[kFinEnt], w[kFinEnt];
-    draw_load<VEC, RESID>(a, zp, zq, t, zpv, zqv);
-    draw_weights<RESID>(a, cp, cq, t, zpv, zqv, w);
-    double loc[kFinEnt], r = 0.0;
-#pragma unroll
-    for (int j = 0; j < kFinEnt; ++j) {
-      r += (double)w[j];
-      loc[j] = r;
-      if (w[j] > 0.f) sl = t + j;
-    }
-    const double inc = wave_incl_scan_f64(r);
-    const double exc = before + (inc - r);
-    int hj = kFinEnt;
-#pragma unroll
-    for (int j = kFinEnt - 1; j >= 0; --j)
-      if (w[j] > 0.f && exc + loc[j] > thr) hj = j;
-    const uint64_t h = __ballot(hj < kFinEnt);
-    if (h != 0) {
-      const int l = (int)__builtin_ctzll(h);
-      y = fin_entry(e, G, wv, l) + __shfl(hj, l, 64);
-    }
-    before += __shfl(inc, 63, 64);
-  }
-  *seg_last = wave_max_i32(sl);
-  return y;
-}
-
+// Residual kernel: block (s, b) recomputes sequence b's row normalisers and
+// accept decisions (a few hundred statistics, cheaper than a launch between
+// them), then sums the weights of slice s of the drawn row. Slice 0 writes
+// n, the accepted drafts, the -1 padding and the drawn pair's normalisers.
 template <int VEC>
-__global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a) {
-  __shared__ double seg[kFinSlots * kFinWaves];  // (slot, wave) weight sums, vocabulary order
+__global__ __launch_bounds__(kResThreads) void accept_residual_kernel(AccParams a) {
   __shared__ double lse[2 * kMaxGamma + 1];
-  __shared__ double scan_w[kFinWaves];
-  __shared__ int last_w[kFinWaves];
-  __shared__ int hit_w[kFinWaves];
   __shared__ int n_s;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = a.gamma, nrow = 2 * g + 1;
+  const int b = blockIdx.x, s = blockIdx.y;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int g = a.gamma;
 
   // Draft tokens and their logits depend on the inputs only: wave 0 fetches
   // them first, so their loads overlap the normalisers' merge below.
@@ -339,25 +319,11 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a)
     zpx = row_ptr(a, b, lane)[x];
     zqx = row_ptr(a, b, g + 1 + lane)[x];
   }
-
-  // 1. Row normalisers: one wave per row merges the row's chunk statistics
-  //    (max of the chunk maxima, then the rescaled sum).
-  for (int k = wv; k < nrow; k += kFinWaves) {
-    const double *st = a.stats + ((size_t)b * nrow + k) * a.n_chunks * 2;
-    double M = -__builtin_inf();
-    for (int c = lane; c < a.n_chunks; c += 64) M = fmax(M, st[2 * c]);
-    M = wave_max_f64(M);
-    double l = 0.0;
-    for (int c = lane; c < a.n_chunks; c += 64)
-      if (st[2 * c] != -__builtin_inf()) l += st[2 * c + 1] * exp(st[2 * c] - M);
-    l = wave_sum_f64(l);
-    if (lane == 0) lse[k] = M + log(l);
-  }
+  row_normalisers<kResWaves>(a, b, lse);
   __syncthreads();
 
-  // 2. Accept tests: lane i of wave 0 evaluates u_i q_i(x_i) < p_i(x_i) (fp64);
-  //    n is the first failing lane. Accepted drafts and the -1 padding are
-  //    written here, the drawn token at the end.
+  // Accept tests: lane i of wave 0 evaluates u_i q_i(x_i) < p_i(x_i) (fp64);
+  // n is the first failing lane.
   if (wv == 0) {
     bool acc = false;  // lanes at or past gamma count as rejections (they stop the scan)
     if (lane < g) {
@@ -367,15 +333,20 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a)
     }
     const uint64_t rej = ~__ballot(acc);
     const int n = min(g, rej != 0 ? (int)__builtin_ctzll(rej) : 64);
-    if (lane == 0) {
-      n_s = n;
-      a.n_accepted[b] = n;
-    }
-    for (int t = lane; t <= g; t += 64) {
-      if (t < n)
-        a.out_tokens[(size_t)b * (g + 1) + t] = clampi(a.tokens[(size_t)b * g + t], 0, a.V - 1);
-      else if (t > n)
-        a.out_tokens[(size_t)b * (g + 1) + t] = -1;
+    if (lane == 0) n_s = n;
+    if (s == 0) {
+      if (lane == 0) {
+        a.n_accepted[b] = n;
+        a.seq_n[b] = n;
+        a.seq_lse[2 * (size_t)b] = lse[n];
+        a.seq_lse[2 * (size_t)b + 1] = n < g ? lse[g + 1 + n] : 0.0;
+      }
+      for (int t = lane; t <= g; t += 64) {
+        if (t < n)
+          a.out_tokens[(size_t)b * (g + 1) + t] = clampi(a.tokens[(size_t)b * g + t], 0, a.V - 1);
+        else if (t > n)
+          a.out_tokens[(size_t)b * (g + 1) + t] = -1;
+      }
     }
   }
   __syncthreads();
@@ -384,101 +355,210 @@ __global__ __launch_bounds__(kFinThreads) void accept_finish_kernel(AccParams a)
   const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
   const Offset cp = split_offset(lse[n]);
   const Offset cq = split_offset(n < g ? lse[g + 1 + n] : 0.0);
-  const int row_iters = (a.V + kFinSpan - 1) / kFinSpan;
-  const int G = (row_iters + kFinSlots - 1) / kFinSlots;  // iterations per slot
-  const int nslots = (row_iters + G - 1) / G;
-  const int iters = nslots * G;  // whole slots; entries past the row weigh zero
-  const int npieces = nslots * kFinWaves;
+  const int p0 = s * a.pps, p1 = min(p0 + a.pps, a.npieces);
+  if (n < g)
+    residual_pieces<VEC, true>(a, b, zp, zq, cp, cq, p0, p1);
+  else
+    residual_pieces<VEC, false>(a, b, zp, zq, cp, cq, p0, p1);
+}
 
-  // 3. One sweep over the drawn row: (slot, wave) sums in LDS, and the last
-  //    entry with mass. The residual of a row pair with no mass at all
-  //    (p_n == q_n) is replaced by p_n, as the pages' reading prescribes.
-  bool residual = n < g;
-  int glast = -1;
-  for (int pass = 0; pass < 2; ++pass) {
-    int last = residual ? draw_sweep<VEC, true>(a, zp, zq, cp, cq, iters, G, seg)
-                        : draw_sweep<VEC, false>(a, zp, zq, cp, cq, iters, G, seg);
-    last = wave_max_i32(last);
-    if (lane == 0) last_w[wv] = last;
-    __syncthreads();
-    glast = -1;
-    for (int w2 = 0; w2 < kFinWaves; ++w2) glast = max(glast, last_w[w2]);
-    __syncthreads();
-    if (glast >= 0 || !residual) break;
-    residual = false;  // no residual mass anywhere: draw from p_n
+// Block sums (fp64, any order) of two values per thread.
+__device__ __forceinline__ void block_sum2_f64(double &x, double &y, double (*lds_w)[2]) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    x += __shfl_xor(x, m, 64);
+    y += __shfl_xor(y, m, 64);
   }
+  if (lane == 0) {
+    lds_w[wv][0] = x;
+    lds_w[wv][1] = y;
+  }
+  __syncthreads();
+  x = y = 0.0;
+  for (int w = 0; w < kDrawThreads / 64; ++w) {
+    x += lds_w[w][0];
+    y += lds_w[w][1];
+  }
+  __syncthreads();
+}
 
-  // 4. Scan of the piece sums (fp64, vocabulary order): thread i takes
-  //    pieces 4i .. 4i+3; the first piece whose inclusive sum exceeds u*Z
-  //    holds the token.
-  constexpr int kPer = kFinSlots * kFinWaves / kFinThreads;  // 4
-  double ps[kPer], run = 0.0;
+// One wave's scan of piece p in vocabulary order: the first entry with mass
+// whose cumulative weight (from `before`) exceeds thr, or -1; *last gets the
+// piece's last entry with mass (-1 if none).
+template <int VEC, bool RESID>
+__device__ __forceinline__ int piece_rescan(const AccParams &a, const float *zp, const float *zq, Offset cp,
+                                            Offset cq, int p, double before, double thr, int *last) {
+  const int lane = lane_id();
+  int y = -1, sl = -1;
+  const int t0 = p * kPiece + 4 * lane;
+  float zpv[kPieceLoads][4], zqv[kPieceLoads][4];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = kPer * tid + j;
-    run += i < npieces ? seg[i] : 0.0;
-    ps[j] = run;
-  }
-  const double incl = wave_incl_scan_f64(run);
-  if (lane == 63) scan_w[wv] = incl;
-  __syncthreads();
-  double before_w = 0.0, Z = 0.0;
-  for (int w2 = 0; w2 < kFinWaves; ++w2) {
-    if (w2 < wv) before_w += scan_w[w2];
-    Z += scan_w[w2];
-  }
-  const double excl_t = before_w + incl - run;  // sum of the pieces before 4*tid
-  const double v = (double)a.u_sample[(size_t)b * (g + 1) + n];
-  const double thr = v * Z;
-  int hit = kPer;
+  for (int j = 0; j < kPieceLoads; ++j) piece_load<VEC, RESID>(a, zp, zq, t0 + 256 * j, zpv[j], zqv[j]);
 #pragma unroll
-  for (int j = kPer - 1; j >= 0; --j)
-    if (kPer * tid + j < npieces && excl_t + ps[j] > thr) hit = j;
-  const uint64_t hb = __ballot(hit < kPer);
-  if (lane == 0) hit_w[wv] = hb != 0 ? (64 * wv + (int)__builtin_ctzll(hb)) : 0x7fffffff;
+  for (int j = 0; j < kPieceLoads; ++j) {
+    const int t = t0 + 256 * j;
+    float pw[4], rw[4];
+    piece_weights<RESID>(a, cp, cq, t, zpv[j], zqv[j], pw, rw);
+    double loc[4], r = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r += (double)rw[e];
+      loc[e] = r;
+      if (rw[e] > 0.f) sl = t + e;
+    }
+    const double inc = wave_incl_scan_f64(r);
+    const double exc = before + (inc - r);
+    int hj = 4;
+#pragma unroll
+    for (int e = 3; e >= 0; --e)
+      if (rw[e] > 0.f && exc + loc[e] > thr) hj = e;
+    const uint64_t h = __ballot(hj < 4);
+    if (y < 0 && h != 0) {
+      const int l = (int)__builtin_ctzll(h);
+      y = p * kPiece + 256 * j + 4 * l + __shfl(hj, l, 64);
+    }
+    before += __shfl(inc, 63, 64);
+  }
+  *last = wave_max_i32(sl);
+  return y;
+}
+
+// Draw kernel: one block per sequence. The residual's piece sums (or p_n's,
+// when n = gamma or the residual has no mass at all, the pages' reading for
+// p_n = q_n) give Z; a block scan in vocabulary order finds the first piece
+// whose inclusive sum exceeds u Z, and wave 0 rescans that piece for the
+// token. Rounding that leaves no crossing falls back to the last entry with
+// mass (of the piece, else of the row). Up to kDrawThreads * kDrawPer pieces
+// (vocabularies up to a million entries) the piece sums are loaded once and
+// kept in registers.
+template <int VEC>
+__global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(AccParams a) {
+  constexpr int kRound = kDrawThreads * kDrawPer;
+  __shared__ double lds_w[kDrawThreads / 64][2];
+  __shared__ double scan_w[kDrawThreads / 64];
+  __shared__ int hit_w[kDrawThreads / 64];
+  __shared__ int piece_s, lastp_s;
+  __shared__ double before_s;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = a.gamma;
+  const int n = clampi(a.seq_n[b], 0, g);
+  const bool two = n < g;  // residual piece sums were written
+  const double *pr = a.pieces + ((size_t)b * 2 + 0) * a.npieces;
+  const double *pp = a.pieces + ((size_t)b * 2 + 1) * a.npieces;
+  const int np = a.npieces;
+  const bool inreg = np <= kRound;
+  double vr[kDrawPer], vp[kDrawPer];
+  double Zr = 0.0, Zp = 0.0;
+#pragma unroll
+  for (int j = 0; j < kDrawPer; ++j) {
+    const int i = kDrawPer * tid + j;
+    vr[j] = inreg && two && i < np ? pr[i] : 0.0;
+    vp[j] = inreg && i < np ? pp[i] : 0.0;
+    Zr += vr[j];
+    Zp += vp[j];
+  }
+  if (!inreg) {
+    for (int i = tid; i < np; i += kDrawThreads) {
+      if (two) Zr += pr[i];
+      Zp += pp[i];
+    }
+  }
+  block_sum2_f64(Zr, Zp, lds_w);
+  const bool resid = two && Zr > 0.0;
+  const double *ps = resid ? pr : pp;
+  const double Z = resid ? Zr : Zp;
+  const double thr = (double)a.u_sample[(size_t)b * (g + 1) + n] * Z;
+
+  // first piece with inclusive sum > thr, and the last piece with mass
+  if (tid == 0) {
+    piece_s = -1;
+    lastp_s = -1;
+  }
   __syncthreads();
-  int first_t = 0x7fffffff;
-  for (int w2 = 0; w2 < kFinWaves; ++w2) first_t = min(first_t, hit_w[w2]);
-  int y = -1;
-  if (first_t != 0x7fffffff) {
-    // the thread that found the first crossing publishes its piece and the
-    // sum of the pieces before it
-    __shared__ int piece_s;
-    __shared__ double before_s;
-    if (tid == first_t) {
-      piece_s = kPer * tid + hit;
-      before_s = excl_t + (hit > 0 ? ps[hit - 1] : 0.0);
+  double run = 0.0;  // sum of the pieces before this round
+  for (int base = 0; base < np; base += kRound) {
+    double v[kDrawPer], loc = 0.0;
+    int lastp = -1;
+#pragma unroll
+    for (int j = 0; j < kDrawPer; ++j) {
+      const int i = base + kDrawPer * tid + j;
+      v[j] = inreg ? (resid ? vr[j] : vp[j]) : (i < np ? ps[i] : 0.0);
+      loc += v[j];
+      if (v[j] > 0.0) lastp = i;
+    }
+    lastp = wave_max_i32(lastp);
+    const double incl = wave_incl_scan_f64(loc);
+    if (lane == 63) scan_w[wv] = incl;
+    __syncthreads();
+    double before_w = 0.0, tot = 0.0;
+    for (int w2 = 0; w2 < kDrawThreads / 64; ++w2) {
+      if (w2 < wv) before_w += scan_w[w2];
+      tot += scan_w[w2];
+    }
+    double c = run + before_w + incl - loc;  // sum of the pieces before this thread's first
+    int hit = -1;
+    double hit_before = 0.0;
+#pragma unroll
+    for (int j = 0; j < kDrawPer; ++j) {
+      if (hit < 0 && v[j] > 0.0 && c + v[j] > thr) {
+        hit = j;
+        hit_before = c;
+      }
+      c += v[j];
+    }
+    const uint64_t hb = __ballot(hit >= 0);
+    if (lane == 0) hit_w[wv] = hb != 0 ? 64 * wv + (int)__builtin_ctzll(hb) : 0x7fffffff;
+    if (lane == 0 && lastp >= 0) atomicMax(&lastp_s, lastp);
+    __syncthreads();
+    int first = 0x7fffffff;
+    for (int w2 = 0; w2 < kDrawThreads / 64; ++w2) first = min(first, hit_w[w2]);
+    if (first != 0x7fffffff && tid == first && piece_s < 0) {
+      piece_s = base + kDrawPer * tid + hit;
+      before_s = hit_before;
     }
     __syncthreads();
-    const int piece = piece_s;
-    const int slot = piece / kFinWaves, pw = piece % kFinWaves;
-    if (wv == pw) {
-      // the owning wave reloads its entries of the slot's iterations and
-      // scans them in vocabulary order
-      const int e_end = (slot + 1) * G;
-      int seg_last = -1;
-      y = residual ? draw_rescan<VEC, true>(a, zp, zq, cp, cq, slot * G, e_end, G, before_s, thr, &seg_last)
-                   : draw_rescan<VEC, false>(a, zp, zq, cp, cq, slot * G, e_end, G, before_s, thr, &seg_last);
-      // rounding left no crossing inside the piece: its last token with mass
-      if (y < 0) y = seg_last;
-      if (y < 0) y = glast;
-      if (lane == 0) a.out_tokens[(size_t)b * (g + 1) + n] = max(0, y);
-    }
-  } else if (tid == 0) {
-    // rounding left v*Z at or above the total: the last token with mass
-    a.out_tokens[(size_t)b * (g + 1) + n] = max(0, glast);
+    if (piece_s >= 0) break;
+    run += tot;
   }
+  if (wv != 0) return;
+  const float *zp = row_ptr(a, b, n);
+  const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
+  const Offset cp = split_offset(a.seq_lse[2 * (size_t)b]);
+  const Offset cq = split_offset(a.seq_lse[2 * (size_t)b + 1]);
+  int y = -1, last = -1;
+  const int piece = piece_s >= 0 ? piece_s : lastp_s;  // no crossing: the last piece with mass
+  if (piece >= 0) {
+    const double before = piece_s >= 0 ? before_s : 0.0;
+    const double t = piece_s >= 0 ? thr : __builtin_inf();
+    y = resid ? piece_rescan<VEC, true>(a, zp, zq, cp, cq, piece, before, t, &last)
+              : piece_rescan<VEC, false>(a, zp, zq, cp, cq, piece, before, t, &last);
+    if (y < 0) y = last;
+  }
+  if (lane == 0) a.out_tokens[(size_t)b * (g + 1) + n] = max(0, y);
 }
 
 struct AccPlan {
   int n_chunks;
-  size_t ws_bytes;  // the chunk statistics
+  int npieces, pps, slices;  // pieces per row, per residual slice, slices per sequence
+  size_t pieces_off, lse_off, n_off;
+  size_t ws_bytes;  // chunk statistics, piece sums, the drawn pair's normalisers, n
 };
 
 AccPlan plan_accept(int64_t B, int64_t gamma, int64_t V) {
   AccPlan p;
   p.n_chunks = (int)sdh::ceil_div(V, kChunk);
-  p.ws_bytes = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
+  p.npieces = (int)sdh::ceil_div(V, kPiece);
+  // enough residual blocks to spread each sequence's drawn row over several CUs
+  const int64_t want = std::max<int64_t>(1, sdh::ceil_div((int64_t)kTargetBlocks, B));
+  const int64_t sl = std::min<int64_t>(p.npieces, want);
+  p.pps = (int)sdh::ceil_div(p.npieces, sl);
+  p.slices = (int)sdh::ceil_div(p.npieces, p.pps);
+  p.pieces_off = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
+  p.lse_off = p.pieces_off + sdh::align_up((size_t)B * 2 * p.npieces * 8);
+  p.n_off = p.lse_off + sdh::align_up((size_t)B * 2 * 8);
+  p.ws_bytes = p.n_off + sdh::align_up((size_t)B * 4);
   return p;
 }
 
@@ -509,7 +589,7 @@ sd_status check_accept(const float *target_logits, const float *draft_logits, co
   return SD_OK;
 }
 
-// Enqueue the four kernels with `workspace` (at least plan_accept's ws_bytes).
+// Enqueue the three kernels with `workspace` (at least plan_accept's ws_bytes).
 sd_status launch_accept(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
                         const float *u_accept, const float *u_sample, int32_t batch, int32_t gamma,
                         int32_t vocab, float temperature, int32_t *n_accepted, int32_t *out_tokens,
@@ -522,23 +602,32 @@ sd_status launch_accept(const float *target_logits, const float *draft_logits, c
   a.u_sample = u_sample;
   a.n_accepted = n_accepted;
   a.out_tokens = out_tokens;
-  a.stats = reinterpret_cast<double *>(workspace);
+  char *ws = reinterpret_cast<char *>(workspace);
+  a.stats = reinterpret_cast<double *>(ws);
+  a.pieces = reinterpret_cast<double *>(ws + p.pieces_off);
+  a.seq_lse = reinterpret_cast<double *>(ws + p.lse_off);
+  a.seq_n = reinterpret_cast<int32_t *>(ws + p.n_off);
   a.B = batch;
   a.gamma = gamma;
   a.V = vocab;
   a.n_chunks = p.n_chunks;
+  a.npieces = p.npieces;
+  a.pps = p.pps;
   a.inv_temp = 1.f / temperature;
   a.inv_temp_d = 1.0 / (double)temperature;
   // 16-byte loads need every row 16-byte aligned
   const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                    (gamma == 0 || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
   const dim3 g_stats((unsigned)p.n_chunks, (unsigned)(batch * (2 * gamma + 1)));
+  const dim3 g_res((unsigned)batch, (unsigned)p.slices);
   if (vec) {
     accept_stats_kernel<4><<<g_stats, kAccThreads, 0, st>>>(a);
-    accept_finish_kernel<4><<<(unsigned)batch, kFinThreads, 0, st>>>(a);
+    accept_residual_kernel<4><<<g_res, kResThreads, 0, st>>>(a);
+    accept_draw_kernel<4><<<(unsigned)batch, kDrawThreads, 0, st>>>(a);
   } else {
     accept_stats_kernel<1><<<g_stats, kAccThreads, 0, st>>>(a);
-    accept_finish_kernel<1><<<(unsigned)batch, kFinThreads, 0, st>>>(a);
+    accept_residual_kernel<1><<<g_res, kResThreads, 0, st>>>(a);
+    accept_draw_kernel<1><<<(unsigned)batch, kDrawThreads, 0, st>>>(a);
   }
   return sdh::launch_status();
 }

@@ -71,6 +71,7 @@ def test_golden_cases_on_gpu():
     (96, 3, 1001, 2.0, 0.5, 1.0),           # odd vocabulary: 4-byte loads, ragged last entries
     (40, 2, 3, 1.0, 0.5, 1.0),              # vocabulary smaller than one 16-byte load
     (20, 4, 1048579, 2.0, 0.5, 1.0),        # over a million entries: several iterations per LDS slot
+    (16, 64, 3001, 2.0, 0.05, 1.0),         # gamma = 64, the largest: one decision lane per draft
 ])
 def test_accept_parity(B, gamma, V, std, noise, temp):
     say(f"accept B={B} gamma={gamma} V={V} noise={noise} temp={temp}")
