@@ -767,24 +767,49 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *o
   int s0, s1;
   sched_inline_unit_slots(a.sc.seq_prefix, a.B, a.Hkv, a.sc.waves, b, kvh, s0, s1);
 
+  // Lane j holds the (m, l) of slot s0 + j0 + j, so the slots' statistics
+  // arrive in one round trip; the o partials of four slots are loaded
+  // together before they are summed (slot order, weights by readlane).
+  const int ns = s1 - s0;
   float M = kNegInf;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, a.part_ml[((size_t)s * a.rows + R) * 2]);
+  for (int j0 = 0; j0 < ns; j0 += 64)
+    if (j0 + lane < ns) M = fmaxf(M, a.part_ml[((size_t)(s0 + j0 + lane) * a.rows + R) * 2]);
+  M = wave_max_f32(M);
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int s = s0; s < s1; ++s) {
-      const size_t base = (size_t)s * a.rows + R;
-      const float mc = a.part_ml[base * 2];
-      if (mc == kNegInf) continue;
-      const float wgt = __builtin_amdgcn_exp2f(mc - M);
-      L += wgt * a.part_ml[base * 2 + 1];
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+      float w = 0.f;
+      if (j0 + lane < ns) {
+        const size_t base = (size_t)(s0 + j0 + lane) * a.rows + R;
+        const float mc = a.part_ml[base * 2];
+        w = mc == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+        L += w * a.part_ml[base * 2 + 1];
+      }
+      const int cnt = min(64, ns - j0);
+      for (int k0 = 0; k0 < cnt; k0 += 4) {
+        float v[4][PER];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += wgt * a.part_o[base * D + lane * PER + k];
+        for (int q = 0; q < 4; ++q) {
+          const size_t base = (size_t)(s0 + j0 + min(k0 + q, cnt - 1)) * a.rows + R;
+#pragma unroll
+          for (int k = 0; k < PER; ++k) v[q][k] = a.part_o[base * D + lane * PER + k];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k0 + q < cnt) {
+            const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + q));
+#pragma unroll
+            for (int k = 0; k < PER; ++k) o[k] += wq * v[q][k];
+          }
+        }
+      }
     }
   }
+  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
   const int i = R / a.G, hl = R % a.G;
   const size_t orow = (((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl);
   const bool empty = !(L > 0.f);
