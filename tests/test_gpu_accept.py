@@ -72,6 +72,9 @@ def test_golden_cases_on_gpu():
     (40, 2, 3, 1.0, 0.5, 1.0),              # vocabulary smaller than one 16-byte load
     (20, 4, 1048579, 2.0, 0.5, 1.0),        # over a million entries: several iterations per LDS slot
     (16, 64, 3001, 2.0, 0.05, 1.0),         # gamma = 64, the largest: one decision lane per draft
+    (1, 4, 128256, 2.0, 1.5, 1.0),          # one sequence: its drawn row over 126 one-piece slices
+    (2048, 1, 32000, 2.0, 0.5, 1.0),        # many sequences: one slice of all 32 pieces each
+    (8, 0, 128256, 2.0, None, 1.0),         # bonus only over the full vocabulary
 ])
 def test_accept_parity(B, gamma, V, std, noise, temp):
     say(f"accept B={B} gamma={gamma} V={V} noise={noise} temp={temp}")
