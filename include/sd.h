@@ -63,6 +63,9 @@ typedef enum { SD_BF16 = 0, SD_F32 = 1 } sd_dtype;
  * kv_lens: int32 [batch] valid tokens per sequence (for verify this count
  *   includes the n_q tokens being verified).
  * page_size must be a multiple of 16; head_dim 64 or 128.
+ * k_pages and v_pages must be 16-byte aligned, and so must every query and
+ *   attention output array below (the kernels move rows in 16-byte pieces):
+ *   else SD_ERR_INVALID_ARG.
  */
 typedef struct {
   const void *k_pages;
@@ -317,7 +320,8 @@ sd_status sd_spec_accept_noalloc(const float *target_logits, const float *draft_
  * §3.1-§3.3: each draft step and the verification pass add the K/V of the
  * tokens they process to the cache).
  *
- * k_new, v_new: [batch, n_new, num_kv_heads, head_dim] of kv->dtype, device.
+ * k_new, v_new: [batch, n_new, num_kv_heads, head_dim] of kv->dtype, device,
+ *   16-byte aligned (else SD_ERR_INVALID_ARG).
  * Token j of sequence b goes to position p = kv->kv_lens[b] + j: page
  *   kv->page_table[b, p / page_size], slot p % page_size, of the pools kv
  *   points at. THIS CALL WRITES kv->k_pages and kv->v_pages (the only entry

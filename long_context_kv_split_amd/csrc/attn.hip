@@ -753,76 +753,96 @@ void attn_stream_kernel(AttnParams a) {
   });
 }
 
-// One wave per output row (b, kvh, R): merge the unit's partials by log-sum-exp.
+// Merge each unit's partials by log-sum-exp. One wave takes four output
+// rows (b, kvh, 4 q .. 4 q + 3) of a unit, 16 lanes per row, each lane D / 16
+// elements of o: lane j of a row's group holds the (m, l) of the unit's slot
+// j0 + j, so the slots' statistics arrive in one round trip, and the o
+// partials of four slots are loaded together before they are summed (slot
+// order, each slot's weight taken from the lane that holds it).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams a, void *out, float *lse,
-                                                           int total_rows) {
+                                                           int total_groups) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= total_rows) return;
+  if (wave >= total_groups) return;
   const int lane = lane_id();
-  const int R = wave % a.rows;
-  const int u = wave / a.rows;
+  const int gl = lane >> 4, sub = lane & 15;
+  const int row_groups = (a.rows + 3) / 4;
+  const int u = wave / row_groups;
+  const int R = (wave % row_groups) * 4 + gl;
+  const bool live = R < a.rows;
+  const int Rc = live ? R : a.rows - 1;  // padding lanes repeat the last row, write nothing
   const int kvh = u % a.Hkv;
   const int b = u / a.Hkv;
   int s0, s1;
   sched_inline_unit_slots(a.sc.seq_prefix, a.B, a.Hkv, a.sc.waves, b, kvh, s0, s1);
-
-  // Lane j holds the (m, l) of slot s0 + j0 + j, so the slots' statistics
-  // arrive in one round trip; the o partials of four slots are loaded
-  // together before they are summed (slot order, weights by readlane).
   const int ns = s1 - s0;
+
   float M = kNegInf;
-  for (int j0 = 0; j0 < ns; j0 += 64)
-    if (j0 + lane < ns) M = fmaxf(M, a.part_ml[((size_t)(s0 + j0 + lane) * a.rows + R) * 2]);
-  M = wave_max_f32(M);
-  constexpr int PER = D / 64;
+  for (int j0 = 0; j0 < ns; j0 += 16)
+    if (j0 + sub < ns) M = fmaxf(M, a.part_ml[((size_t)(s0 + j0 + sub) * a.rows + Rc) * 2]);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  constexpr int PER = D / 16;  // elements of o per lane
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int j0 = 0; j0 < ns; j0 += 64) {
+    for (int j0 = 0; j0 < ns; j0 += 16) {
       float w = 0.f;
-      if (j0 + lane < ns) {
-        const size_t base = (size_t)(s0 + j0 + lane) * a.rows + R;
+      if (j0 + sub < ns) {
+        const size_t base = (size_t)(s0 + j0 + sub) * a.rows + Rc;
         const float mc = a.part_ml[base * 2];
         w = mc == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mc - M);
         L += w * a.part_ml[base * 2 + 1];
       }
-      const int cnt = min(64, ns - j0);
+      const int cnt = min(16, ns - j0);
       for (int k0 = 0; k0 < cnt; k0 += 4) {
-        float v[4][PER];
+        f32x4 v[4][PER / 4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const size_t base = (size_t)(s0 + j0 + min(k0 + q, cnt - 1)) * a.rows + R;
+          const size_t base = (size_t)(s0 + j0 + min(k0 + q, cnt - 1)) * a.rows + Rc;
 #pragma unroll
-          for (int k = 0; k < PER; ++k) v[q][k] = a.part_o[base * D + lane * PER + k];
+          for (int c = 0; c < PER / 4; ++c)
+            v[q][c] = *reinterpret_cast<const f32x4 *>(a.part_o + base * D + sub * PER + 4 * c);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const float wq = __shfl(w, 16 * gl + k0 + q, 64);
           if (k0 + q < cnt) {
-            const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + q));
 #pragma unroll
-            for (int k = 0; k < PER; ++k) o[k] += wq * v[q][k];
+            for (int c = 0; c < PER / 4; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[4 * c + e] += wq * v[q][c][e];
           }
         }
       }
     }
   }
-  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) L += __shfl_xor(L, m, 64);
+  if (!live) return;
   const int i = R / a.G, hl = R % a.G;
   const size_t orow = (((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl);
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
+  if constexpr (EltInfo<T>::bytes == 2) {
+    uint32_t pk[PER / 2];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const float v = o[k] * inv;
-    if constexpr (EltInfo<T>::bytes == 2)
-      reinterpret_cast<uint16_t *>(out)[orow * D + lane * PER + k] = (uint16_t)f32_to_bf16_bits(v);
+    for (int k = 0; k < PER / 2; ++k) pk[k] = pack_bf16x2(o[2 * k] * inv, o[2 * k + 1] * inv);
+    uint16_t *dst = reinterpret_cast<uint16_t *>(out) + orow * D + sub * PER;
+    if constexpr (PER == 8)
+      *reinterpret_cast<u32x4 *>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     else
-      reinterpret_cast<float *>(out)[orow * D + lane * PER + k] = v;
+      *reinterpret_cast<u32x2 *>(dst) = u32x2{pk[0], pk[1]};
+  } else {
+    float *dst = reinterpret_cast<float *>(out) + orow * D + sub * PER;
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c)
+      *reinterpret_cast<f32x4 *>(dst + 4 * c) = f32x4{o[4 * c] * inv, o[4 * c + 1] * inv, o[4 * c + 2] * inv,
+                                                      o[4 * c + 3] * inv};
   }
-  if (lse != nullptr && lane == 0) lse[orow] = empty ? kNegInf : (M + __log2f(L)) * kLn2;
+  if (lse != nullptr && sub == 0) lse[orow] = empty ? kNegInf : (M + __log2f(L)) * kLn2;
 }
 
 // Workspace: prefix tables, then the partial slots. Sized for the largest
@@ -853,8 +873,8 @@ sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
     attn_stream_kernel<NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   else
     attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
-  const int total_rows = a.B * a.Hkv * a.rows;
-  attn_combine_kernel<T, D><<<(total_rows + 3) / 4, 256, 0, st>>>(a, out, lse, total_rows);
+  const int total_groups = a.B * a.Hkv * ((a.rows + 3) / 4);
+  attn_combine_kernel<T, D><<<(total_groups + 3) / 4, 256, 0, st>>>(a, out, lse, total_groups);
   return sdh::launch_status();
 }
 
@@ -884,6 +904,7 @@ sd_status common_checks(const sd_kv_cache *kv, const void *q, int32_t batch, int
   sd_status s = sdh::check_kv(kv, true);
   if (s != SD_OK) return s;
   SD_REQUIRE(q != nullptr && out != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(sdh::aligned16(q) && sdh::aligned16(out), SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && n_q > 0 && num_q_heads > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE((int64_t)(num_q_heads / kv->num_kv_heads) * n_q <= 64, SD_ERR_UNSUPPORTED);

@@ -53,6 +53,7 @@ extern "C" sd_status sd_kv_append(const sd_kv_cache *kv, const void *k_new, cons
   sd_status s = sdh::check_kv(kv, true);
   if (s != SD_OK) return s;
   SD_REQUIRE(k_new != nullptr && v_new != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(sdh::aligned16(k_new) && sdh::aligned16(v_new), SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && n_new >= 0, SD_ERR_INVALID_ARG);
   if (n_new == 0) return SD_OK;
   const int row_chunks = kv->head_dim * sdh::dtype_bytes(kv->dtype) / 16;

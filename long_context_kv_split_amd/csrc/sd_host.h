@@ -28,12 +28,16 @@ inline sd_status launch_status() {
 
 inline int dtype_bytes(int32_t dtype) { return dtype == SD_BF16 ? 2 : (dtype == SD_F32 ? 4 : 0); }
 
+// The kernels move K, V and query rows in 16-byte pieces.
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // Checks common to every call that reads the paged cache.
 inline sd_status check_kv(const sd_kv_cache *kv, bool need_v) {
   SD_REQUIRE(kv != nullptr, SD_ERR_INVALID_ARG);
   SD_REQUIRE(kv->k_pages != nullptr && kv->page_table != nullptr && kv->kv_lens != nullptr,
              SD_ERR_INVALID_ARG);
   SD_REQUIRE(!need_v || kv->v_pages != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(aligned16(kv->k_pages) && (!need_v || aligned16(kv->v_pages)), SD_ERR_INVALID_ARG);
   SD_REQUIRE(kv->num_pages > 0 && kv->page_size > 0 && kv->max_pages > 0 && kv->num_kv_heads > 0 &&
                  kv->head_dim > 0,
              SD_ERR_INVALID_ARG);

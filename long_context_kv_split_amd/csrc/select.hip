@@ -1501,6 +1501,7 @@ sd_status snapkv_impl(const sd_kv_cache *kv, const void *q_obs, int32_t batch, i
   sd_status s = sdh::check_kv(kv, false);
   if (s != SD_OK) return s;
   SD_REQUIRE(q_obs != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(sdh::aligned16(q_obs), SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && window >= 1 && num_q_heads > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(budget > window, SD_ERR_INVALID_ARG);
@@ -1619,6 +1620,7 @@ extern "C" sd_status sd_topk_select(const sd_kv_cache *kv, const void *q, int32_
   sd_status s = sdh::check_kv(kv, false);
   if (s != SD_OK) return s;
   SD_REQUIRE(q != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(sdh::aligned16(q), SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && num_q_heads > 0 && budget > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,

@@ -87,6 +87,10 @@ WS = ctypes.c_void_p(0x6000)
 @pytest.mark.parametrize("over,args,want", [
     ({}, dict(q=None), sd.SD_ERR_INVALID_ARG),
     ({"k_pages": None}, {}, sd.SD_ERR_INVALID_ARG),
+    ({"k_pages": 0x1008}, {}, sd.SD_ERR_INVALID_ARG),   # not 16-byte aligned
+    ({"v_pages": 0x2002}, {}, sd.SD_ERR_INVALID_ARG),
+    ({}, dict(q=ctypes.c_void_p(0x5004)), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(out=ctypes.c_void_p(0x5002)), sd.SD_ERR_INVALID_ARG),
     ({"head_dim": 96}, {}, sd.SD_ERR_UNSUPPORTED),
     ({"page_size": 8}, {}, sd.SD_ERR_UNSUPPORTED),
     ({"dtype": 7}, {}, sd.SD_ERR_UNSUPPORTED),
@@ -149,6 +153,8 @@ def test_streaming_rejects_invalid_arguments(L, args, want):
 @no_gpu
 @pytest.mark.parametrize("over,args,want", [
     ({}, dict(budget=8), sd.SD_ERR_INVALID_ARG),      # budget <= window
+    ({"k_pages": 0x1004}, {}, sd.SD_ERR_INVALID_ARG),   # not 16-byte aligned
+    ({}, dict(q=ctypes.c_void_p(0x5008)), sd.SD_ERR_INVALID_ARG),
     ({}, dict(pool=4), sd.SD_ERR_INVALID_ARG),        # even pool kernel
     ({}, dict(pool=0), sd.SD_ERR_INVALID_ARG),
     ({}, dict(window=0), sd.SD_ERR_INVALID_ARG),
@@ -166,7 +172,7 @@ def test_snapkv_rejects_invalid_arguments(L, over, args, want):
     kv = _kv(**over)
     a = dict(window=8, pool=7, budget=32, max_len=64, ws_bytes=1 << 30, scale=1.0)
     a.update(args)
-    st = L.sd_snapkv_select(ctypes.byref(kv), FAKE, 2, a["window"], 8, a["pool"], a["budget"],
+    st = L.sd_snapkv_select(ctypes.byref(kv), a.get("q", FAKE), 2, a["window"], 8, a["pool"], a["budget"],
                             a["max_len"], a["scale"], FAKE, FAKE, WS, a["ws_bytes"], None)
     assert st == want
 
@@ -287,6 +293,7 @@ def test_append_and_advance_reject_invalid_arguments(L):
     assert L.sd_kv_append(ctypes.byref(kv), None, FAKE, 2, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 0, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, -1, None) == sd.SD_ERR_INVALID_ARG
+    assert L.sd_kv_append(ctypes.byref(kv), ctypes.c_void_p(0x5004), FAKE, 2, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_append(ctypes.byref(_kv(v_pages=None)), FAKE, FAKE, 2, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, 0, None) == sd.SD_OK  # nothing to write
     assert L.sd_kv_advance(None, None, 2, 1, None) == sd.SD_ERR_INVALID_ARG
