@@ -15,7 +15,9 @@
 // segment it covers into a slot table of at most waves + units entries. The
 // assignment depends only on shapes and lengths, so results are bitwise
 // reproducible. A combine kernel merges each unit's partials by log-sum-exp;
-// the call is two launches.
+// the call is two launches. Small calls (every unit in one round of the chip,
+// at most 1024 tokens each, one 16-row tile) run one workgroup per unit
+// instead, its waves merging in LDS: one launch.
 //
 // Per step a wave computes S^T = K Q^T with 16x16x32 bf16 MFMA (tokens on M,
 // the G*n_q query rows of the KV head on N, padded to NB tiles of 16), applies
@@ -550,182 +552,193 @@ __device__ __forceinline__ void stream_operands(const lds_u32x4 *ring, int sl, S
   }
 }
 
+// One segment [s_begin, s_end) of unit (b, kvh) through this wave's LDS ring
+// at `lds` (Lay::kBytes): st ends holding the segment's (m, l, o).
 template <int NB, bool SPARSE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB <= 3 ? 2 : 1)))
-void attn_stream_kernel(AttnParams a) {
+__device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *lds, int b, int kvh, int s_begin,
+                                               int s_end, AttnState<__bf16, 128, NB> &st) {
   constexpr int D = 128;
   constexpr int QV = StepRegs<__bf16, D>::kVec;
   constexpr int DPL = D / 16;
   constexpr int kStreamRing = stream_ring<NB>();
   using Lay = StreamLayout<SPARSE, kStreamRing>;
-  __shared__ __attribute__((aligned(16))) char lds_raw[Lay::kBytes];
-  lds_char *lds = (lds_char *)lds_raw;
   lds_u32x4 *ring = (lds_u32x4 *)lds;
   lds_char *table = lds + Lay::kRingBytes;
   const int lane = lane_id();
   const int g = lane >> 4, r = lane & 15;
   const char *kp = reinterpret_cast<const char *>(a.k_pages);
   const char *vp = reinterpret_cast<const char *>(a.v_pages);
+  s_begin = __builtin_amdgcn_readfirstlane(s_begin);
+  s_end = __builtin_amdgcn_readfirstlane(s_end);
+  const int len = __builtin_amdgcn_readfirstlane(attn_len(a, b));
+  const int sel = clampi(a.lens[b], 0, a.len_cap);
+  const int pkvh = kvh / a.unit_div;
+  const int32_t *idx_row = nullptr;
+  if constexpr (SPARSE)
+    idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
 
-  attn_for_each_segment(a, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
-    s_begin = __builtin_amdgcn_readfirstlane(s_begin);
-    s_end = __builtin_amdgcn_readfirstlane(s_end);
-    const int len = __builtin_amdgcn_readfirstlane(attn_len(a, b));
-    const int sel = clampi(a.lens[b], 0, a.len_cap);
-    const int pkvh = kvh / a.unit_div;
-    const int32_t *idx_row = nullptr;
-    if constexpr (SPARSE)
-      idx_row = a.idx + ((size_t)b * a.idx_heads + (a.idx_heads > 1 ? kvh : 0)) * a.max_sel;
-
-    AttnState<__bf16, D, NB> st;
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      const int R = rb * 16 + r;
-      int i = 0, hl = 0;
-      const bool live = R < a.rows;
-      if (live) {
-        i = R / a.G;
-        hl = R % a.G;
-      }
-      st.lim[rb] = SPARSE ? len - 1 : (live ? len - a.n_q + i : len - 1);
-      const char *qb = reinterpret_cast<const char *>(a.q) +
-                       ((((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl) * D) * 2;
-#pragma unroll
-      for (int c = 0; c < QV; ++c) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (live) v = *reinterpret_cast<const u32x4 *>(qb + (32 * c + 8 * g) * 2);
-        st.q[rb][c] = v;
-      }
-      st.m[rb] = kNegInf;
-      st.l[rb] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < DPL; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < NB; ++rb) {
+    const int R = rb * 16 + r;
+    int i = 0, hl = 0;
+    const bool live = R < a.rows;
+    if (live) {
+      i = R / a.G;
+      hl = R % a.G;
     }
-    const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
-    const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
+    st.lim[rb] = SPARSE ? len - 1 : (live ? len - a.n_q + i : len - 1);
+    const char *qb = reinterpret_cast<const char *>(a.q) +
+                     ((((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < QV; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (live) v = *reinterpret_cast<const u32x4 *>(qb + (32 * c + 8 * g) * 2);
+      st.q[rb][c] = v;
+    }
+    st.m[rb] = kNegInf;
+    st.l[rb] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DPL; ++dt) st.o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int lim_min = SPARSE ? len - 1 : len - a.n_q;  // smallest limit of any real row
+  const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
 
-    // this lane's chunk of copy i: token 4i + g, chunk position r (K: global chunk r ^ t)
-    auto issue_rows = [&](int4 rows4, int sl) {
-      lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
-      const int rw[4] = {rows4.x, rows4.y, rows4.z, rows4.w};
+  // this lane's chunk of copy i: token 4i + g, chunk position r (K: global chunk r ^ t)
+  auto issue_rows = [&](int4 rows4, int sl) {
+    lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
+    const int rw[4] = {rows4.x, rows4.y, rows4.z, rows4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * i + g;
-        lds_dma16(kp + (size_t)rw[i] * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + g;
+      lds_dma16(kp + (size_t)rw[i] * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(vp + (size_t)rw[i] * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
-    };
-    // the step's rows are base .. base + 15 (wave-uniform base): per-lane byte
-    // offsets of the eight copies relative to row `base`
-    auto issue_base = [&](int base, int sl) {
-      lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
-      const char *kb = kp + (size_t)base * (D * 2);
-      const char *vb = vp + (size_t)base * (D * 2);
+    for (int i = 0; i < 4; ++i) lds_dma16(vp + (size_t)rw[i] * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
+  };
+  // the step's rows are base .. base + 15 (wave-uniform base): per-lane byte
+  // offsets of the eight copies relative to row `base`
+  auto issue_base = [&](int base, int sl) {
+    lds_u32x4 *kd = ring + sl * 2 * kStreamChunks;
+    const char *kb = kp + (size_t)base * (D * 2);
+    const char *vb = vp + (size_t)base * (D * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * i + g;
-        lds_dma16(kb + t * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + g;
+      lds_dma16(kb + t * (D * 2) + ((r ^ t) & 15) * 16, kd + i * 64);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(vb + (4 * i + g) * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
-    };
-    // one step: start the copies of step `ahead`, wait for step s, compute it
-    auto step = [&](auto masked, int s, int sl, auto &&start_ahead) {
-      start_ahead();
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStreamRing - 1) * 8) : "memory");
-      StepRegs<__bf16, D> cur;
-      stream_operands(ring, sl, cur);
-      compute_step<__bf16, D, NB, SPARSE, decltype(masked)::value>(a, st, cur, s, len);
-    };
-    using Plain = std::integral_constant<bool, false>;
-    using Masked = std::integral_constant<bool, true>;
+    for (int i = 0; i < 4; ++i) lds_dma16(vb + (4 * i + g) * (D * 2) + r * 16, kd + kStreamChunks + i * 64);
+  };
+  // one step: start the copies of step `ahead`, wait for step s, compute it
+  auto step = [&](auto masked, int s, int sl, auto &&start_ahead) {
+    start_ahead();
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStreamRing - 1) * 8) : "memory");
+    StepRegs<__bf16, D> cur;
+    stream_operands(ring, sl, cur);
+    compute_step<__bf16, D, NB, SPARSE, decltype(masked)::value>(a, st, cur, s, len);
+  };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
 
-    if constexpr (!SPARSE) {
-      // ------------------------------------------------------------- verify
-      const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
-      const int P = a.page_size;
-      const int last = s_end - 1;
-      auto entry_ptr = [&](int s) { return pt + clampi(min(s, last) * kStepTokens / P, 0, a.max_pages - 1); };
-      auto row_from = [&](int entry, int s) {
-        return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + min(s, last) * kStepTokens % P;
+  if constexpr (!SPARSE) {
+    // ------------------------------------------------------------- verify
+    const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+    const int P = a.page_size;
+    const int last = s_end - 1;
+    auto entry_ptr = [&](int s) { return pt + clampi(min(s, last) * kStepTokens / P, 0, a.max_pages - 1); };
+    auto row_from = [&](int entry, int s) {
+      return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + min(s, last) * kStepTokens % P;
+    };
+    int wb = s_begin;
+    int rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
+    int rows_b = row_from(*entry_ptr(wb + kStreamWin + lane), wb + kStreamWin + lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table of a previous segment is free
+    lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
+    auto base_of = [&](int s) {
+      const int d = s - wb;
+      return d < kStreamWin ? __builtin_amdgcn_readlane(rows_a, d) : __builtin_amdgcn_readlane(rows_b, d - kStreamWin);
+    };
+    auto issue_step = [&](int s, int sl) { issue_base(base_of(min(s, last)), sl); };
+    auto ahead = [&](int s) {
+      return [&, s] {
+        if (s - wb == kStreamWin) {
+          // entries of this window were requested kStreamWin steps ago and
+          // waited for since (every step waits for its own copies)
+          wb += kStreamWin;
+          rows_a = rows_b;
+          rows_b = row_from(lds_read_i32(table + 4 * lane), wb + kStreamWin + lane);
+          lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
+        }
+        issue_step(s + kStreamRing - 1, (s + kStreamRing - 1) % kStreamRing);
       };
-      int wb = s_begin;
-      int rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
-      int rows_b = row_from(*entry_ptr(wb + kStreamWin + lane), wb + kStreamWin + lane);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table of a previous segment is free
-      lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
-      auto base_of = [&](int s) {
-        const int d = s - wb;
-        return d < kStreamWin ? __builtin_amdgcn_readlane(rows_a, d) : __builtin_amdgcn_readlane(rows_b, d - kStreamWin);
-      };
-      auto issue_step = [&](int s, int sl) { issue_base(base_of(min(s, last)), sl); };
-      auto ahead = [&](int s) {
-        return [&, s] {
-          if (s - wb == kStreamWin) {
-            // entries of this window were requested kStreamWin steps ago and
-            // waited for since (every step waits for its own copies)
-            wb += kStreamWin;
-            rows_a = rows_b;
-            rows_b = row_from(lds_read_i32(table + 4 * lane), wb + kStreamWin + lane);
-            lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
-          }
-          issue_step(s + kStreamRing - 1, (s + kStreamRing - 1) % kStreamRing);
-        };
-      };
+    };
 #pragma unroll
-      for (int i = 0; i < kStreamRing - 1; ++i) issue_step(s_begin + i, (s_begin + i) % kStreamRing);
-      const int plain_end = max(s_begin, min(s_end, first_masked));
-      for (int s = s_begin; s < plain_end; ++s) step(Plain{}, s, s % kStreamRing, ahead(s));
-      for (int s = plain_end; s < s_end; ++s) step(Masked{}, s, s % kStreamRing, ahead(s));
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies into the ring or table have landed
-    } else {
-      // -------------------------------------------------------------- draft
-      const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
-      const int P = a.page_size;
-      const int tail0 = a.tail_begin ? a.tail_begin[b] : 0;
-      const int last_sel = max(sel - 1, 0);
-      const int pos_cap = a.max_pages * P - 1;
-      for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kSparseSubSteps) {
-        const int sc_end = min(s_end, sc_begin + kSparseSubSteps);
-        const int n_tok = (sc_end - sc_begin) * kStepTokens;
-        // rows of the sub-chunk's tokens; token t of step k at table entry
-        // 16k + 4 (t % 4) + t / 4, so lane g reads tokens g, g+4, g+8, g+12 at 16k + 4g
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous copies have landed
-        for (int t0 = 0; t0 < n_tok; t0 += 64 * kResolveBatch) {
-          int pos[kResolveBatch];
+    for (int i = 0; i < kStreamRing - 1; ++i) issue_step(s_begin + i, (s_begin + i) % kStreamRing);
+    const int plain_end = max(s_begin, min(s_end, first_masked));
+    for (int s = s_begin; s < plain_end; ++s) step(Plain{}, s, s % kStreamRing, ahead(s));
+    for (int s = plain_end; s < s_end; ++s) step(Masked{}, s, s % kStreamRing, ahead(s));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies into the ring or table have landed
+  } else {
+    // -------------------------------------------------------------- draft
+    const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
+    const int P = a.page_size;
+    const int tail0 = a.tail_begin ? a.tail_begin[b] : 0;
+    const int last_sel = max(sel - 1, 0);
+    const int pos_cap = a.max_pages * P - 1;
+    for (int sc_begin = s_begin; sc_begin < s_end; sc_begin += kSparseSubSteps) {
+      const int sc_end = min(s_end, sc_begin + kSparseSubSteps);
+      const int n_tok = (sc_end - sc_begin) * kStepTokens;
+      // rows of the sub-chunk's tokens; token t of step k at table entry
+      // 16k + 4 (t % 4) + t / 4, so lane g reads tokens g, g+4, g+8, g+12 at 16k + 4g
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous copies have landed
+      for (int t0 = 0; t0 < n_tok; t0 += 64 * kResolveBatch) {
+        int pos[kResolveBatch];
 #pragma unroll
-          for (int i = 0; i < kResolveBatch; ++i) {
-            const int t = clampi(sc_begin * kStepTokens + t0 + 64 * i + lane, 0, len - 1);
-            const int from_idx = idx_row[min(t, last_sel)];
-            pos[i] = clampi(t < sel ? from_idx : tail0 + (t - sel), 0, pos_cap);
-          }
-          int e[kResolveBatch];
+        for (int i = 0; i < kResolveBatch; ++i) {
+          const int t = clampi(sc_begin * kStepTokens + t0 + 64 * i + lane, 0, len - 1);
+          const int from_idx = idx_row[min(t, last_sel)];
+          pos[i] = clampi(t < sel ? from_idx : tail0 + (t - sel), 0, pos_cap);
+        }
+        int e[kResolveBatch];
 #pragma unroll
-          for (int i = 0; i < kResolveBatch; ++i) e[i] = pt[pos[i] / P];
+        for (int i = 0; i < kResolveBatch; ++i) e[i] = pt[pos[i] / P];
 #pragma unroll
-          for (int i = 0; i < kResolveBatch; ++i) {
-            const int tt = t0 + 64 * i + lane;
-            if (tt < n_tok) {
-              const int k = tt / kStepTokens, t = tt % kStepTokens;
-              lds_write_i32(table + 4 * (k * kStepTokens + 4 * (t % 4) + t / 4),
-                            (clampi(e[i], 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + pos[i] % P);
-            }
+        for (int i = 0; i < kResolveBatch; ++i) {
+          const int tt = t0 + 64 * i + lane;
+          if (tt < n_tok) {
+            const int k = tt / kStepTokens, t = tt % kStepTokens;
+            lds_write_i32(table + 4 * (k * kStepTokens + 4 * (t % 4) + t / 4),
+                          (clampi(e[i], 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + pos[i] % P);
           }
         }
-        const int last_k = sc_end - sc_begin - 1;
-        auto issue_step = [&](int k, int sl) {
-          issue_rows(lds_read_i32x4(table + 4 * (min(k, last_k) * kStepTokens + 4 * g)), sl);
-        };
-        auto ahead = [&](int k) { return [&, k] { issue_step(k + kStreamRing - 1, (k + kStreamRing - 1) % kStreamRing); }; };
-#pragma unroll
-        for (int i = 0; i < kStreamRing - 1; ++i) issue_step(i, i % kStreamRing);
-        const int plain_end = max(0, min(last_k + 1, first_masked - sc_begin));
-        for (int k = 0; k < plain_end; ++k) step(Plain{}, sc_begin + k, k % kStreamRing, ahead(k));
-        for (int k = plain_end; k <= last_k; ++k) step(Masked{}, sc_begin + k, k % kStreamRing, ahead(k));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      const int last_k = sc_end - sc_begin - 1;
+      auto issue_step = [&](int k, int sl) {
+        issue_rows(lds_read_i32x4(table + 4 * (min(k, last_k) * kStepTokens + 4 * g)), sl);
+      };
+      auto ahead = [&](int k) { return [&, k] { issue_step(k + kStreamRing - 1, (k + kStreamRing - 1) % kStreamRing); }; };
+#pragma unroll
+      for (int i = 0; i < kStreamRing - 1; ++i) issue_step(i, i % kStreamRing);
+      const int plain_end = max(0, min(last_k + 1, first_masked - sc_begin));
+      for (int k = 0; k < plain_end; ++k) step(Plain{}, sc_begin + k, k % kStreamRing, ahead(k));
+      for (int k = plain_end; k <= last_k; ++k) step(Masked{}, sc_begin + k, k % kStreamRing, ahead(k));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+  }
+}
+
+template <int NB, bool SPARSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB <= 3 ? 2 : 1)))
+void attn_stream_kernel(AttnParams a) {
+  constexpr int D = 128;
+  constexpr int DPL = D / 16;
+  using Lay = StreamLayout<SPARSE, stream_ring<NB>()>;
+  __shared__ __attribute__((aligned(16))) char lds_raw[Lay::kBytes];
+  const int g = lane_id() >> 4, r = lane_id() & 15;
+
+  attn_for_each_segment(a, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
+    AttnState<__bf16, D, NB> st;
+    stream_segment<NB, SPARSE>(a, (lds_char *)lds_raw, b, kvh, s_begin, s_end, st);
 
     // Partial of this segment: unnormalised o (relative to m), (m, l) in log2 units.
 #pragma unroll
@@ -751,6 +764,80 @@ void attn_stream_kernel(AttnParams a) {
       }
     }
   });
+}
+
+// Small calls (every unit fits one round of the chip and is short): one
+// workgroup per unit, its kUnitWaves waves splitting the unit's steps evenly.
+// Each wave leaves its segment's (m, l, o) in its own LDS region; the waves
+// then merge them by log-sum-exp and write the output. One launch, no length
+// scan across the batch and no partials in global memory. One 16-row tile.
+constexpr int kUnitWaves = 4;
+constexpr int kUnitMaxSteps = 64;  // steps per unit that the unit kernel takes
+
+template <bool SPARSE>
+__global__ __launch_bounds__(64 * kUnitWaves) void attn_unit_kernel(AttnParams a, void *out, float *lse) {
+  constexpr int NB = 1, D = 128, DPL = D / 16;
+  using Lay = StreamLayout<SPARSE, stream_ring<NB>()>;
+  static_assert(16 * (D + 2) * 4 <= Lay::kBytes, "a wave's partial fits its LDS region");
+  __shared__ __attribute__((aligned(16))) char lds_raw[kUnitWaves * Lay::kBytes];
+  const int wv = threadIdx.x >> 6, lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv, kvh = u % a.Hkv;
+  const int n = unit_steps(a, b);
+  const int s0 = n * wv / kUnitWaves, s1 = n * (wv + 1) / kUnitWaves;
+  lds_char *mine = (lds_char *)lds_raw + wv * Lay::kBytes;
+  AttnState<__bf16, D, NB> st;
+  if (s0 < s1) {
+    stream_segment<NB, SPARSE>(a, mine, b, kvh, s0, s1, st);
+  } else {
+    st.m[0] = kNegInf;
+    st.l[0] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DPL; ++dt) st.o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // this wave's partial into its region: row R's o at R * D (the layout of
+  // the global partials), (m, l) after the 16 rows
+  float *po = reinterpret_cast<float *>(lds_raw + wv * Lay::kBytes);
+  const float l = rows4_sum(st.l[0]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int dt = 0; dt < DPL; ++dt) po[r * D + 4 * DPL * g + DPL * e + dt] = st.o[0][dt][e];
+  if (g == 0) {
+    po[16 * D + 2 * r] = st.m[0];
+    po[16 * D + 2 * r + 1] = l;
+  }
+  __syncthreads();
+  // wave wv merges rows 4 wv .. 4 wv + 3: 16 lanes per row, 8 elements each
+  const int R = 4 * wv + g, sub = r;
+  if (R >= a.rows) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < kUnitWaves; ++k) M = fmaxf(M, reinterpret_cast<const float *>(lds_raw + k * Lay::kBytes)[16 * D + 2 * R]);
+  float o[DPL] = {};
+  float L = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < kUnitWaves; ++k) {
+      const float *pk = reinterpret_cast<const float *>(lds_raw + k * Lay::kBytes);
+      const float mk = pk[16 * D + 2 * R];
+      const float w = mk == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+      L += w * pk[16 * D + 2 * R + 1];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] += w * pk[R * D + DPL * sub + j];
+    }
+  }
+  const int i = R / a.G, hl = R % a.G;
+  const size_t orow = (((size_t)b * a.n_q + i) * a.Hq + (size_t)kvh * a.G + hl);
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+  uint32_t pk[DPL / 2];
+#pragma unroll
+  for (int k = 0; k < DPL / 2; ++k) pk[k] = pack_bf16x2(o[2 * k] * inv, o[2 * k + 1] * inv);
+  *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + orow * D + sub * DPL) =
+      u32x4{pk[0], pk[1], pk[2], pk[3]};
+  if (lse != nullptr && sub == 0) lse[orow] = empty ? kNegInf : (M + __log2f(L)) * kLn2;
 }
 
 // Merge each unit's partials by log-sum-exp. One wave takes four output
@@ -867,6 +954,14 @@ sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
   constexpr bool kStream = EltInfo<T>::bytes == 2 && D == 128;
   const void *kernel = kStream ? reinterpret_cast<const void *>(attn_stream_kernel<NB, SPARSE>)
                                : reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>);
+  if constexpr (kStream && NB == 1) {
+    // every unit in one round of the chip, each short: one workgroup per unit
+    const int64_t units = (int64_t)a.B * a.Hkv;
+    if (units <= kNumCUs && (int64_t)a.len_cap + a.tail_cap <= (int64_t)kUnitMaxSteps * kStepTokens) {
+      attn_unit_kernel<SPARSE><<<(unsigned)units, 64 * kUnitWaves, 0, st>>>(a, out, lse);
+      return sdh::launch_status();
+    }
+  }
   static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(kernel, kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
   if constexpr (kStream)
