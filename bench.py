@@ -32,6 +32,7 @@ vocabulary, warm and cold (last-level cache evicted before each call).
 
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
+python bench.py --configs-only --steps 5   # only the other workloads (profiling)
 """
 import argparse
 import json
@@ -61,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-sample-units", type=int, default=0,
                     help="(sequence, kv head) units the oracle runs (0 = 80 units, about 12 s)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="time only the other workloads (for their kernel traces and counters)")
     ap.add_argument("--no-round", action="store_true",
                     help="skip the round and per-sequence-budget measurements")
     return ap.parse_args()
@@ -724,6 +727,13 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.configs_only:
+        from __graft_entry__ import _ensure_built
+
+        _ensure_built()
+        torch.cuda.set_device(0)
+        print(json.dumps({"other_workloads": measure_configs(reps=args.steps)}), flush=True)
         return
     from __graft_entry__ import _ensure_built
 
