@@ -168,14 +168,18 @@ def test_draft_empty_selection_and_full_budget_equals_verify_decode():
     compare_attn(ref, lref, o_ref, l_ref, BF16)
 
 
-def test_one_launch_and_split_paths_agree():
+@pytest.mark.parametrize("Hq,Hkv,n_q,draft_heads", [
+    (8, 2, 4, "shared"),       # G * n_q = 16 rows: one full tile
+    (6, 2, 5, "per-head"),     # G = 3, 15 rows; the draft with one set per query head
+])
+def test_one_launch_and_split_paths_agree(Hq, Hkv, n_q, draft_heads):
     """Calls whose units all fit one round of the chip and hold at most 1024
     tokens run one workgroup per unit (no split, no combine). The same inputs
     with a length bound above that limit (a wider page table, a longer index
     row) take the persistent split + combine path. Both must meet the oracle
     bars, verify and draft alike."""
     lens = [600, 333, 1000, 17, 0, 1024]
-    Hq, Hkv, d, n_q = 8, 2, 128, 4          # G * n_q = 16 rows: one tile
+    d = 128
     kv_t = paged_kv(77, lens, Hkv, d, BF16, "cuda", shuffle=True)
     q = queries(77, 1, (len(lens), n_q, Hq, d), BF16, "cuda", scale=d ** -0.5)
     o_ref, l_ref = oracle.verify_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens, 1.0)
@@ -189,14 +193,17 @@ def test_one_launch_and_split_paths_agree():
     compare_attn(split, split_l, o_ref, l_ref, BF16)
 
     qd = q[:, :1].contiguous()
-    idx_np = np.full((len(lens), 1, 512), -1, dtype=np.int32)
-    sel_np = np.zeros(len(lens), dtype=np.int32)
-    for b, L in enumerate(lens):
-        keep = sorted(set(range(min(64, L))) | set(range(max(0, L - 448), L)))
-        idx_np[b, 0, :len(keep)] = keep
-        sel_np[b] = len(keep)
-    idx, sel = torch.tensor(idx_np).cuda(), torch.tensor(sel_np).cuda()
-    idx_wide = torch.full((len(lens), 1, 2048), -1, dtype=torch.int32, device="cuda")
+    if draft_heads == "shared":
+        idx_np = np.full((len(lens), 1, 512), -1, dtype=np.int32)
+        sel_np = np.zeros(len(lens), dtype=np.int32)
+        for b, L in enumerate(lens):
+            keep = sorted(set(range(min(64, L))) | set(range(max(0, L - 448), L)))
+            idx_np[b, 0, :len(keep)] = keep
+            sel_np[b] = len(keep)
+        idx, sel = torch.tensor(idx_np).cuda(), torch.tensor(sel_np).cuda()
+    else:
+        idx, sel = _random_sets(78, lens, Hq, 512)
+    idx_wide = torch.full((len(lens), idx.shape[1], 2048), -1, dtype=torch.int32, device="cuda")
     idx_wide[:, :, :512] = idx
     d_ref, dl_ref = oracle.sparse_attn(qd, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, idx, sel, 1.0)
     one, one_l = run_draft(kv_t, qd, 1, Hq, idx, sel)
