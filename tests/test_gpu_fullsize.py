@@ -80,6 +80,46 @@ def test_verify_full_size_sampled(name):
                        f"verify {name} (full size)")
 
 
+@pytest.mark.parametrize("name", ["llama8b-b128-l32k-snapkv", "ragged-b256-l4k-32k", "llama70b-b64-l16k"])
+def test_verify_rows_equal_truncated_decodes_every_unit(name):
+    """Every unit at full size, by a property: verify's query row i sees
+    positions 0 .. L - n_q + i, so it must equal a decode (n_q = 1) of query i
+    over the cache truncated to L - n_q + i + 1 tokens. The two calls split
+    the work at different points (other step counts, other wave shares), so a
+    slot, schedule or combine error anywhere in the batch shows; they agree to
+    rounding. The rounding is not only fp32: the PV product takes P in bf16,
+    rounded relative to the running max, which depends on where the work is
+    split, so outputs near zero (cancellation) differ by ~1e-4 between two
+    correct schedules. The two therefore meet the same bf16 bars as against
+    the oracle, on all rows of all units."""
+    w, lens, kv_t, q = build(name)
+    n_q = w.gamma + 1
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    L = max(lens)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, n_q, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, n_q, Hq, Hkv, d, L), "cuda")
+    sd.sd_verify_attn(kv, q, n_q, Hq, L, 1.0, out, lse, ws)
+    worst = np.zeros(3)
+    wsd = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, Hq, Hkv, d, L), "cuda")
+    for i in range(n_q):
+        lens_i = (kv_t.kv_lens - (n_q - 1 - i)).clamp(min=0).to(torch.int32).contiguous()
+        kv_i = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, lens_i)
+        qi = q[:, i:i + 1].contiguous()
+        oi = torch.full_like(qi, float("nan"))
+        li = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        sd.sd_verify_attn(kv_i, qi, 1, Hq, L, 1.0, oi, li, wsd)
+        torch.cuda.synchronize()
+        ref_o = oi[:, 0].double().cpu().numpy()[:, None]
+        ref_l = li[:, 0].double().cpu().numpy()[:, None]
+        err = compare_attn(out[:, i:i + 1], lse[:, i:i + 1], ref_o, ref_l, BF16)
+        worst = np.maximum(worst, err)
+    record(f"verify rows vs truncated decodes {name} (every unit)", units=B * Hkv, rows=B * n_q * Hq,
+           max_abs=float(worst[0]), max_norm=float(worst[1]), max_lse=float(worst[2]))
+    say(f"  {name}: all {B * Hkv} units, worst max|dO|={worst[0]:.2e} norm={worst[1]:.2e} lse={worst[2]:.2e}")
+
+
 @pytest.mark.parametrize("name", ["llama8b-b32-l8k", "ragged-b256-l4k-32k"])
 def test_streaming_draft_full_size_sampled(name):
     w, lens, kv_t, q = build(name)
