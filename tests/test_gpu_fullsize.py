@@ -61,6 +61,42 @@ def check_units_verify(w, lens, kv_t, q, out, lse, units, label):
     say(f"  {label}: {len(units)} units, worst max|dO|={worst[0]:.2e} norm={worst[1]:.2e} lse={worst[2]:.2e}")
 
 
+def gathered_decode(kv_t, idx, sel, qd, num_q_heads):
+    """Dense decode (verify with n_q = 1) over a compact paged cache that holds,
+    for every (sequence, KV head), exactly the rows idx[b, h, :sel[b]] in
+    order (the gather done by torch indexing, not by the library)."""
+    B, H, S = idx.shape
+    _, Hkv, P, d = kv_t.k_pages.shape
+    npg = (S + P - 1) // P
+    pos = idx.clamp(min=0).long().expand(B, Hkv, S) if H == 1 else idx.clamp(min=0).long()
+    page = kv_t.page_table.long().gather(1, (pos // P).reshape(B, -1)).reshape(B, Hkv, S)
+    heads = torch.arange(Hkv, device="cuda").view(1, Hkv, 1).expand(B, Hkv, S)
+    k_sel = torch.zeros((B, Hkv, npg * P, d), dtype=kv_t.k_pages.dtype, device="cuda")
+    v_sel = torch.zeros_like(k_sel)
+    k_sel[:, :, :S] = kv_t.k_pages[page, heads, pos % P]
+    v_sel[:, :, :S] = kv_t.v_pages[page, heads, pos % P]
+    k_c = k_sel.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d).contiguous()
+    v_c = v_sel.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d).contiguous()
+    pt_c = torch.arange(B * npg, dtype=torch.int32, device="cuda").view(B, npg).contiguous()
+    kv_c = sd.KVCache(k_c, v_c, pt_c, sel.to(torch.int32).contiguous())
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, 1, num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, num_q_heads, Hkv, d, S), "cuda")
+    sd.sd_verify_attn(kv_c, qd, 1, num_q_heads, S, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_draft_against_gathered(label, out, lse, kv_t, idx, sel, qd, num_q_heads):
+    """Every unit of a full-size draft against the dense decode over its
+    gathered rows (different kernels and splits: the bf16 bars)."""
+    o_ref, l_ref = gathered_decode(kv_t, idx, sel, qd, num_q_heads)
+    err = compare_attn(out, lse, o_ref.double().cpu().numpy(), l_ref.double().cpu().numpy(), BF16)
+    record(label, rows=int(out.shape[0] * num_q_heads), max_abs=float(err[0]), max_norm=float(err[1]),
+           max_lse=float(err[2]))
+    say(f"  {label}: max|dO|={err[0]:.2e} norm={err[1]:.2e} lse={err[2]:.2e}")
+
+
 @pytest.mark.parametrize("name", ["llama8b-b32-l8k", "llama8b-b128-l32k-snapkv", "ragged-b256-l4k-32k",
                                   "llama70b-b64-l16k"])
 def test_verify_full_size_sampled(name):
@@ -151,6 +187,8 @@ def test_streaming_draft_full_size_sampled(name):
         worst = np.maximum(worst, err)
     record(f"StreamingLLM draft {name} (full size)", units=len(units), max_abs=float(worst[0]),
            max_norm=float(worst[1]), max_lse=float(worst[2]))
+    check_draft_against_gathered(f"StreamingLLM draft {name} vs dense decode over its rows (every unit)",
+                                 out, lse, kv_t, idx, sel, qd, w.num_q_heads)
 
 
 def test_snapkv_select_and_draft_full_size_sampled():
@@ -202,6 +240,8 @@ def test_snapkv_select_and_draft_full_size_sampled():
                  draft_max_norm=float(worst[1]), draft_max_lse=float(worst[2]))
     record("snapkv select + draft B=128 L=32k (full size)", **stats)
     say(f"  {stats}")
+    check_draft_against_gathered("snapkv draft B=128 L=32k vs dense decode over its rows (every unit)",
+                                 out, lse, kv_t, idx, sel, qd, w.num_q_heads)
     # fp32 vs fp64 ordering of pooled votes within 1e-5 of the cut: about one
     # unit in a hundred is expected at this shape
     assert len(units) >= 64 and near <= 3, stats
