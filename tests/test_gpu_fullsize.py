@@ -191,6 +191,27 @@ def test_streaming_draft_full_size_sampled(name):
                                  out, lse, kv_t, idx, sel, qd, w.num_q_heads)
 
 
+def torch_snapkv_pooled(kv_t, q_obs, b, window, pool_kernel, L):
+    """Pooled votes of every KV head of sequence b, by plain PyTorch fp32 on
+    the GPU (the definition: causal window softmax, votes summed over the
+    group's window rows, clipped max pool): [Hkv, L - W]."""
+    _, Hkv, P, d = kv_t.k_pages.shape
+    Hq = q_obs.shape[2]
+    G = Hq // Hkv
+    npg = (L + P - 1) // P
+    pages = kv_t.page_table[b, :npg].long()
+    k = kv_t.k_pages[pages].float().permute(1, 0, 2, 3).reshape(Hkv, npg * P, d)[:, :L]   # [Hkv, L, d]
+    qw = q_obs[b].float().reshape(window, Hkv, G, d).permute(1, 0, 2, 3).reshape(Hkv, window * G, d)
+    s = torch.bmm(qw, k.transpose(1, 2).contiguous())                                      # [Hkv, W*G, L]
+    row_w = torch.arange(window, device="cuda").repeat_interleave(G)                       # window row of each
+    lim = (L - window + row_w).view(1, -1, 1)
+    s = s.masked_fill(torch.arange(L, device="cuda").view(1, 1, L) > lim, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    votes = p[:, :, :L - window].sum(dim=1)                                                  # [Hkv, L - W]
+    half = pool_kernel // 2
+    return torch.nn.functional.max_pool1d(votes.unsqueeze(1), pool_kernel, stride=1, padding=half).squeeze(1)
+
+
 def test_snapkv_select_and_draft_full_size_sampled():
     """B=128, 32k context: SnapKV selection (W=32, pool 7, budget 2048) and the
     sparse draft over it, each compared on sampled units; a unit's draft output
@@ -242,6 +263,27 @@ def test_snapkv_select_and_draft_full_size_sampled():
     say(f"  {stats}")
     check_draft_against_gathered("snapkv draft B=128 L=32k vs dense decode over its rows (every unit)",
                                  out, lse, kv_t, idx, sel, qd, w.num_q_heads)
+    # every unit's selection against a plain PyTorch fp32 reference of the
+    # definition: the kept prefix positions are the budget - W largest pooled
+    # votes (ties to the lower position); fp32 against fp32 in another order,
+    # so positions may differ only within 1e-5 of the cut
+    keep = w.budget - w.window
+    differ_units = 0
+    for b in range(B):
+        pooled = torch_snapkv_pooled(kv_t, q_obs, b, w.window, w.pool_kernel, lens[b])     # [Hkv, L - W]
+        order = torch.sort(-pooled, dim=1, stable=True).indices[:, :keep]
+        thr = torch.gather(pooled, 1, order[:, -1:])
+        ref = torch.sort(order, dim=1).values.cpu().numpy()
+        pooled_np, thr_np = pooled.cpu().numpy(), thr.cpu().numpy()[:, 0]
+        for g in range(Hkv):
+            got = idx_np[b, g, :keep]
+            if np.array_equal(got, ref[g]):
+                continue
+            differ_units += 1
+            for t in set(got.tolist()) ^ set(ref[g].tolist()):
+                assert abs(pooled_np[g, t] - thr_np[g]) <= 1e-5 * thr_np[g], (b, g, t, pooled_np[g, t], thr_np[g])
+    record("snapkv select B=128 L=32k vs PyTorch fp32 (every unit)", units=B * Hkv, near_tie_units=differ_units)
+    say(f"  every unit vs PyTorch fp32: {differ_units} of {B * Hkv} units differ, all within the near-tie band")
     # fp32 vs fp64 ordering of pooled votes within 1e-5 of the cut: about one
     # unit in a hundred is expected at this shape
     assert len(units) >= 64 and near <= 3, stats
