@@ -176,3 +176,36 @@ def check_accept(label, n, out, zt, zd, x, ua, us, temperature=1.0, planted=Fals
     record(label, **stats)
     say(msg)
     return stats
+
+
+def gathered_decode(kv_t, idx, sel, qd, num_q_heads):
+    """Dense decode (verify with n_q = 1) over a compact paged cache that holds,
+    for every index set, exactly the rows idx[b, h, :sel[b]] in order (the
+    gather done by torch indexing, not by the library). idx: [B, H, S] with H
+    = 1 (one set for all KV heads), Hkv (one per KV head) or num_q_heads (one
+    per query head: the compact cache then has one head per query head, read
+    with G = 1)."""
+    B, H, S = idx.shape
+    _, Hkv, P, d = kv_t.k_pages.shape
+    per_q = H == num_q_heads and H != Hkv
+    Hc = H if per_q else Hkv
+    npg = (S + P - 1) // P
+    pos = idx.clamp(min=0).long()
+    pos = pos.expand(B, Hc, S) if H == 1 else pos
+    pool = torch.arange(Hc, device="cuda") // (num_q_heads // Hkv if per_q else 1)
+    page = kv_t.page_table.long().gather(1, (pos // P).reshape(B, -1)).reshape(B, Hc, S)
+    heads = pool.view(1, Hc, 1).expand(B, Hc, S)
+    k_sel = torch.zeros((B, Hc, npg * P, d), dtype=kv_t.k_pages.dtype, device="cuda")
+    v_sel = torch.zeros_like(k_sel)
+    k_sel[:, :, :S] = kv_t.k_pages[page, heads, pos % P]
+    v_sel[:, :, :S] = kv_t.v_pages[page, heads, pos % P]
+    k_c = k_sel.reshape(B, Hc, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hc, P, d).contiguous()
+    v_c = v_sel.reshape(B, Hc, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hc, P, d).contiguous()
+    pt_c = torch.arange(B * npg, dtype=torch.int32, device="cuda").view(B, npg).contiguous()
+    kv_c = sd.KVCache(k_c, v_c, pt_c, sel.to(torch.int32).contiguous())
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, 1, num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, num_q_heads, Hc, d, S), "cuda")
+    sd.sd_verify_attn(kv_c, qd, 1, num_q_heads, S, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse

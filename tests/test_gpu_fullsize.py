@@ -15,7 +15,7 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries, workload_lens
-from tests.gpu_helpers import check_accept, compare_attn, dirty_workspace, ensure_lib, say, unit_cache
+from tests.gpu_helpers import check_accept, compare_attn, dirty_workspace, ensure_lib, gathered_decode, say, unit_cache
 from tests.parity_log import record
 
 pytestmark = pytest.mark.gpu
@@ -59,32 +59,6 @@ def check_units_verify(w, lens, kv_t, q, out, lse, units, label):
         worst = np.maximum(worst, err)
     record(label, units=len(units), max_abs=float(worst[0]), max_norm=float(worst[1]), max_lse=float(worst[2]))
     say(f"  {label}: {len(units)} units, worst max|dO|={worst[0]:.2e} norm={worst[1]:.2e} lse={worst[2]:.2e}")
-
-
-def gathered_decode(kv_t, idx, sel, qd, num_q_heads):
-    """Dense decode (verify with n_q = 1) over a compact paged cache that holds,
-    for every (sequence, KV head), exactly the rows idx[b, h, :sel[b]] in
-    order (the gather done by torch indexing, not by the library)."""
-    B, H, S = idx.shape
-    _, Hkv, P, d = kv_t.k_pages.shape
-    npg = (S + P - 1) // P
-    pos = idx.clamp(min=0).long().expand(B, Hkv, S) if H == 1 else idx.clamp(min=0).long()
-    page = kv_t.page_table.long().gather(1, (pos // P).reshape(B, -1)).reshape(B, Hkv, S)
-    heads = torch.arange(Hkv, device="cuda").view(1, Hkv, 1).expand(B, Hkv, S)
-    k_sel = torch.zeros((B, Hkv, npg * P, d), dtype=kv_t.k_pages.dtype, device="cuda")
-    v_sel = torch.zeros_like(k_sel)
-    k_sel[:, :, :S] = kv_t.k_pages[page, heads, pos % P]
-    v_sel[:, :, :S] = kv_t.v_pages[page, heads, pos % P]
-    k_c = k_sel.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d).contiguous()
-    v_c = v_sel.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d).contiguous()
-    pt_c = torch.arange(B * npg, dtype=torch.int32, device="cuda").view(B, npg).contiguous()
-    kv_c = sd.KVCache(k_c, v_c, pt_c, sel.to(torch.int32).contiguous())
-    out = torch.full_like(qd, float("nan"))
-    lse = torch.full((B, 1, num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
-    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, num_q_heads, Hkv, d, S), "cuda")
-    sd.sd_verify_attn(kv_c, qd, 1, num_q_heads, S, 1.0, out, lse, ws)
-    torch.cuda.synchronize()
-    return out, lse
 
 
 def check_draft_against_gathered(label, out, lse, kv_t, idx, sel, qd, num_q_heads):
