@@ -263,6 +263,60 @@ def test_snapkv_select_and_draft_full_size_sampled():
     assert len(units) >= 64 and near <= 3, stats
 
 
+def test_snapkv_per_sequence_budgets_full_size_every_unit():
+    """The per-sequence-budget workload at full size (B=256, contexts 4096 to
+    32768 on shuffled pages, budget_b = L_b / 16 rounded down to 16, clamped to
+    [256, 2048], window 32, pool 7): every unit's selection against the plain
+    PyTorch fp32 reference (near-ties within 1e-5 of the cut allowed), rows
+    padded with -1 past their own budget, and the draft over the per-sequence
+    sets equal to a dense decode over the gathered rows."""
+    w = WORKLOADS["ragged-b256-l4k-32k"]
+    B, Hq, Hkv, d, W, pool = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, 32, 7
+    lens = workload_lens(w)
+    kv_t = paged_kv(w.seed, lens, Hkv, d, BF16, "cuda", shuffle=True, spike_frac=0.1)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    budgets = [max(256, min(2048, L // 16 // 16 * 16)) for L in lens]
+    Kmax, L = max(budgets), max(lens)
+    bud = torch.tensor(budgets, dtype=torch.int32, device="cuda")
+    q_obs = queries(w.seed, 4, (B, W, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    idx = torch.full((B, Hkv, Kmax), 7, dtype=torch.int32, device="cuda")
+    sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+    ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L), "cuda")
+    sd.sd_snapkv_select_budgets(kv, q_obs, W, Hq, pool, bud, Kmax, L, 1.0, idx, sel, ws)
+    torch.cuda.synchronize()
+    ic, sc = idx.cpu().numpy(), sel.cpu().numpy()
+    assert list(sc) == [min(Lb, Kb) for Lb, Kb in zip(lens, budgets)]
+    differ = 0
+    for b in range(B):
+        Kb, Lb = budgets[b], lens[b]
+        row = ic[b]
+        assert (row[:, Kb:] == -1).all() and (np.diff(row[:, :Kb], axis=1) > 0).all()
+        assert (row[:, Kb - W:Kb] == np.arange(Lb - W, Lb)).all()
+        pooled = torch_snapkv_pooled(kv_t, q_obs, b, W, pool, Lb)
+        keep = Kb - W
+        order = torch.sort(-pooled, dim=1, stable=True).indices[:, :keep]
+        thr = torch.gather(pooled, 1, order[:, -1:]).cpu().numpy()[:, 0]
+        ref = torch.sort(order, dim=1).values.cpu().numpy()
+        pn = pooled.cpu().numpy()
+        for g in range(Hkv):
+            if np.array_equal(row[g, :keep], ref[g]):
+                continue
+            differ += 1
+            for t in set(row[g, :keep].tolist()) ^ set(ref[g].tolist()):
+                assert abs(pn[g, t] - thr[g]) <= 1e-5 * thr[g], (b, g, t, pn[g, t], thr[g])
+    q = queries(w.seed, 1, (B, 1, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    wsd = dirty_workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, Kmax), "cuda")
+    sd.sd_draft_attn_sparse(kv, q, 1, Hq, idx, sel, Hkv, Kmax, 1.0, out, lse, wsd)
+    o_g, l_g = gathered_decode(kv_t, idx, sel, q, Hq)
+    err = compare_attn(out, lse, o_g.double().cpu().numpy(), l_g.double().cpu().numpy(), BF16)
+    record("snapkv per-sequence budgets B=256 ragged (every unit)", units=B * Hkv, near_tie_units=differ,
+           draft_vs_gathered_max_abs=float(err[0]))
+    say(f"  per-sequence budgets: {differ} of {B * Hkv} units differ from torch fp32 (near ties); "
+        f"draft vs gathered decode max|dO|={err[0]:.2e}")
+
+
 def test_accept_bench_shape():
     """B=128, gamma=4 over the 128256-token vocabulary, as in the benchmark."""
     B, gamma, V, seed = 128, 4, 128256, 3
