@@ -62,7 +62,7 @@ struct AttnParams {
   const int32_t *lens;  // kv_lens (verify) or sel_lens (draft)
   const int32_t *idx;   // draft: [B, idx_heads, max_sel]
   const void *q;        // [B, n_q, Hq, D]
-  Sched sc;             // persistent schedule tables (written by the plan kernel)
+  Sched sc;             // schedule: wave count and the per-sequence step prefix (written by wave 0)
   float *part_o;        // [slots, rows, D]
   float *part_ml;       // [slots, rows, 2]
   // Units are (sequence, head) pairs: the KV heads (Hkv = pool heads, G query
