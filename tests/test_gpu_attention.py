@@ -47,6 +47,9 @@ VERIFY_CASES = [
     ("bf16-short", BF16, 8, 2, 128, [4, 3, 0, 1], 4, False, 16),
     ("bf16-decode-exact-pages", BF16, 8, 2, 128, [512, 1024], 1, True, 16),
     ("bf16-2500-sequences", BF16, 8, 2, 128, MANY, 4, True, 16),
+    # one long sequence: each unit spread over about a thousand waves, so the
+    # combine merges ~1000 slots per row (its chunked slot loop)
+    ("bf16-one-300k-sequence", BF16, 8, 2, 128, [300000], 4, True, 16),
 ]
 
 
