@@ -129,6 +129,9 @@ DRAFT_CASES = [
     ("per-head-rows64", BF16, 16, 1, 128, [1800], 4, "per-head", 700),
     ("stream-2500-sequences", BF16, 8, 2, 128, MANY, 1, "streaming", 48),
     ("per-head-2500-sequences", BF16, 8, 2, 128, MANY, 1, "per-head", 40),
+    # one long selection (up to 120k of 250k positions): many resolved
+    # sub-chunks per wave and many slots per unit
+    ("shared-bf16-long-selection", BF16, 8, 2, 128, [250000], 1, "shared", 120000),
 ]
 
 
