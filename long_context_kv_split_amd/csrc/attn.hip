@@ -552,6 +552,15 @@ __device__ __forceinline__ void stream_operands(const lds_u32x4 *ring, int sl, S
   }
 }
 
+// A well-mixed 32-bit hash of a segment (wave-uniform inputs).
+__device__ __forceinline__ uint32_t segment_hash(int b, int kvh, int s_begin) {
+  uint32_t h = (uint32_t)b * 0x9E3779B1u ^ (uint32_t)kvh * 0x85EBCA77u ^ (uint32_t)s_begin * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 13;
+  return h;
+}
+
 // One segment [s_begin, s_end) of unit (b, kvh) through this wave's LDS ring
 // at `lds` (Lay::kBytes): st ends holding the segment's (m, l, o).
 template <int NB, bool SPARSE>
@@ -642,26 +651,43 @@ __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *ld
 
   if constexpr (!SPARSE) {
     // ------------------------------------------------------------- verify
+    // The unmasked steps [s_begin, plain_end) are taken in a permuted order:
+    // position v reads step s_begin + (A v + rot) mod n_plain, with A a
+    // small prime that does not divide n_plain (a bijection) and rot a hash
+    // of the segment. Consecutive steps of a wave are thus A steps apart and
+    // the waves start at unrelated offsets. Walking a sequence's pages in
+    // order, a wave's successive 4 KB blocks sit at one fixed stride, and
+    // pages laid out in order then read about 3% slower than shuffled ones;
+    // the permuted walk reads them as fast. The masked steps follow in
+    // order. Loop indices below are positions v; phys(v) is the step.
     const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
     const int P = a.page_size;
-    const int last = s_end - 1;
-    auto entry_ptr = [&](int s) { return pt + clampi(min(s, last) * kStepTokens / P, 0, a.max_pages - 1); };
-    auto row_from = [&](int entry, int s) {
-      return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + min(s, last) * kStepTokens % P;
+    const int n_tot = s_end - s_begin;  // >= 1
+    const int n_plain = max(0, min(s_end, first_masked) - s_begin);
+    const uint32_t rot = n_plain > 1 ? segment_hash(b, kvh, s_begin) % (uint32_t)n_plain : 0u;
+    const uint32_t A = n_plain % 37 ? 37u : n_plain % 41 ? 41u : n_plain % 43 ? 43u : 1u;
+    auto phys = [&](int v) {
+      v = min(v, n_tot - 1);
+      if (v < n_plain) v = (int)(((uint64_t)v * A + rot) % (uint32_t)n_plain);
+      return s_begin + v;
     };
-    int wb = s_begin;
+    auto entry_ptr = [&](int v) { return pt + clampi(phys(v) * kStepTokens / P, 0, a.max_pages - 1); };
+    auto row_from = [&](int entry, int v) {
+      return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + phys(v) * kStepTokens % P;
+    };
+    int wb = 0;
     int rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
     int rows_b = row_from(*entry_ptr(wb + kStreamWin + lane), wb + kStreamWin + lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table of a previous segment is free
     lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
-    auto base_of = [&](int s) {
-      const int d = s - wb;
+    auto base_of = [&](int v) {
+      const int d = v - wb;
       return d < kStreamWin ? __builtin_amdgcn_readlane(rows_a, d) : __builtin_amdgcn_readlane(rows_b, d - kStreamWin);
     };
-    auto issue_step = [&](int s, int sl) { issue_base(base_of(min(s, last)), sl); };
-    auto ahead = [&](int s) {
-      return [&, s] {
-        if (s - wb == kStreamWin) {
+    auto issue_step = [&](int v, int sl) { issue_base(base_of(min(v, n_tot - 1)), sl); };
+    auto ahead = [&](int v) {
+      return [&, v] {
+        if (v - wb == kStreamWin) {
           // entries of this window were requested kStreamWin steps ago and
           // waited for since (every step waits for its own copies)
           wb += kStreamWin;
@@ -669,14 +695,13 @@ __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *ld
           rows_b = row_from(lds_read_i32(table + 4 * lane), wb + kStreamWin + lane);
           lds_dma4(entry_ptr(wb + 2 * kStreamWin + lane), (__attribute__((address_space(3))) void *)table);
         }
-        issue_step(s + kStreamRing - 1, (s + kStreamRing - 1) % kStreamRing);
+        issue_step(v + kStreamRing - 1, (v + kStreamRing - 1) % kStreamRing);
       };
     };
 #pragma unroll
-    for (int i = 0; i < kStreamRing - 1; ++i) issue_step(s_begin + i, (s_begin + i) % kStreamRing);
-    const int plain_end = max(s_begin, min(s_end, first_masked));
-    for (int s = s_begin; s < plain_end; ++s) step(Plain{}, s, s % kStreamRing, ahead(s));
-    for (int s = plain_end; s < s_end; ++s) step(Masked{}, s, s % kStreamRing, ahead(s));
+    for (int i = 0; i < kStreamRing - 1; ++i) issue_step(i, i);
+    for (int v = 0; v < n_plain; ++v) step(Plain{}, phys(v), v % kStreamRing, ahead(v));
+    for (int v = n_plain; v < n_tot; ++v) step(Masked{}, s_begin + v, v % kStreamRing, ahead(v));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // copies into the ring or table have landed
   } else {
     // -------------------------------------------------------------- draft
