@@ -552,15 +552,6 @@ __device__ __forceinline__ void stream_operands(const lds_u32x4 *ring, int sl, S
   }
 }
 
-// A well-mixed 32-bit hash of a segment (wave-uniform inputs).
-__device__ __forceinline__ uint32_t segment_hash(int b, int kvh, int s_begin) {
-  uint32_t h = (uint32_t)b * 0x9E3779B1u ^ (uint32_t)kvh * 0x85EBCA77u ^ (uint32_t)s_begin * 0xC2B2AE3Du;
-  h ^= h >> 15;
-  h *= 0x2C1B3C6Du;
-  h ^= h >> 13;
-  return h;
-}
-
 // One segment [s_begin, s_end) of unit (b, kvh) through this wave's LDS ring
 // at `lds` (Lay::kBytes): st ends holding the segment's (m, l, o).
 template <int NB, bool SPARSE>
@@ -651,26 +642,15 @@ __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *ld
 
   if constexpr (!SPARSE) {
     // ------------------------------------------------------------- verify
-    // The unmasked steps [s_begin, plain_end) are taken in a permuted order:
-    // position v reads step s_begin + (A v + rot) mod n_plain, with A a
-    // small prime that does not divide n_plain (a bijection) and rot a hash
-    // of the segment. Consecutive steps of a wave are thus A steps apart and
-    // the waves start at unrelated offsets. Walking a sequence's pages in
-    // order, a wave's successive 4 KB blocks sit at one fixed stride, and
-    // pages laid out in order then read about 3% slower than shuffled ones;
-    // the permuted walk reads them as fast. The masked steps follow in
-    // order. Loop indices below are positions v; phys(v) is the step.
+    // The unmasked steps [s_begin, plain_end) are taken in a permuted order
+    // (StepWalk), the masked steps follow in order. Loop indices below are
+    // positions v; phys(v) is the step.
     const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
     const int P = a.page_size;
     const int n_tot = s_end - s_begin;  // >= 1
     const int n_plain = max(0, min(s_end, first_masked) - s_begin);
-    const uint32_t rot = n_plain > 1 ? segment_hash(b, kvh, s_begin) % (uint32_t)n_plain : 0u;
-    const uint32_t A = n_plain % 37 ? 37u : n_plain % 41 ? 41u : n_plain % 43 ? 43u : 1u;
-    auto phys = [&](int v) {
-      v = min(v, n_tot - 1);
-      if (v < n_plain) v = (int)(((uint64_t)v * A + rot) % (uint32_t)n_plain);
-      return s_begin + v;
-    };
+    const StepWalk walk(n_plain, segment_hash(b, kvh, s_begin));
+    auto phys = [&](int v) { return s_begin + walk(min(v, n_tot - 1)); };
     auto entry_ptr = [&](int v) { return pt + clampi(phys(v) * kStepTokens / P, 0, a.max_pages - 1); };
     auto row_from = [&](int entry, int v) {
       return (clampi(entry, 0, a.num_pages - 1) * a.pool_heads + pkvh) * P + phys(v) * kStepTokens % P;

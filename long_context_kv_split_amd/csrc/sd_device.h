@@ -85,6 +85,35 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// A well-mixed 32-bit hash of a stream segment (wave-uniform inputs).
+__device__ __forceinline__ uint32_t segment_hash(int b, int kvh, int s_begin) {
+  uint32_t h = (uint32_t)b * 0x9E3779B1u ^ (uint32_t)kvh * 0x85EBCA77u ^ (uint32_t)s_begin * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 13;
+  return h;
+}
+
+// A permuted walk over n steps: position v reads step (A v + rot) mod n, A a
+// small prime that does not divide n (so the map is a bijection) and rot a
+// hash of the segment. Consecutive reads of a wave land A steps apart and
+// waves start at unrelated offsets: walking a sequence's pages in order puts
+// a wave's successive 4 KB blocks at one fixed stride, and pages laid out in
+// order then read measurably slower than shuffled ones.
+struct StepWalk {
+  int n;
+  uint32_t A, rot;
+  __device__ StepWalk() : n(0), A(1u), rot(0u) {}
+  __device__ StepWalk(int n_, uint32_t hash)
+      : n(n_), A(n_ % 37 ? 37u : n_ % 41 ? 41u : n_ % 43 ? 43u : 1u), rot(n_ > 1 ? hash % (uint32_t)n_ : 0u) {}
+  // step of position v (positions >= n are not permuted)
+  __device__ int operator()(int v) const {
+    if (v >= n) return v;
+    if (n < (1 << 25)) return (int)(((uint32_t)v * A + rot) % (uint32_t)n);  // v A + rot < 2^32
+    return (int)(((uint64_t)v * A + rot) % (uint32_t)n);
+  }
+};
+
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) char lds_char;
 

@@ -192,6 +192,8 @@ struct KStream {
   int Hkv, kvh, P, num_pages, last;
   int lane_off[kInsts];  // byte offset of this lane's chunk inside a step
   int wb, rows_a, rows_b;
+  int s0 = 0;       // first position of the segment
+  StepWalk walk;    // positions s0 + v, v < walk.n, read step s0 + walk(v)
 
   __device__ KStream(const SnapParams &a, int b, int kvh_, int last_step, char *lds)
       : ring((lds_u32x4 *)(__attribute__((address_space(3))) char *)lds),
@@ -206,12 +208,18 @@ struct KStream {
       lane_off[c] = (t * kRowChunks + (p ^ (t & (kRowChunks - 1)))) * 16;
     }
   }
-  __device__ const int32_t *entry_ptr(int s) const { return pt + min(s, last) * kStepTokens / P; }
-  // First token row of step s (16 keys never straddle a page: P % 16 == 0).
+  // Step read at position s (the identity unless permute() was called).
+  __device__ int step_at(int s) const { return s0 + walk(min(s, last) - s0); }
+  __device__ const int32_t *entry_ptr(int s) const { return pt + step_at(s) * kStepTokens / P; }
+  // First token row of the step at position s (16 keys never straddle a
+  // page: P % 16 == 0).
   __device__ int row_from(int entry, int s) const {
-    const int pos = min(s, last) * kStepTokens;
+    const int pos = step_at(s) * kStepTokens;
     return (clampi(entry, 0, num_pages - 1) * Hkv + kvh) * P + pos % P;
   }
+  // Read positions s_begin .. s_begin + n - 1 in a permuted order (before
+  // begin(s_begin); for passes whose result does not depend on the order).
+  __device__ void permute(int n, uint32_t hash) { walk = StepWalk(n, hash); }
   // Copy the page-table entries of window steps w0 + lane into LDS.
   __device__ void fetch_entries(int w0) {
     lds_dma4(entry_ptr(w0 + lane_id()), entries);
@@ -235,6 +243,7 @@ struct KStream {
   }
   __device__ void begin(int s_begin) {
     const int lane = lane_id();
+    s0 = s_begin;
     wb = s_begin;
     rows_a = row_from(*entry_ptr(wb + lane), wb + lane);
     rows_b = row_from(*entry_ptr(wb + kWinSteps + lane), wb + kWinSteps + lane);
@@ -413,10 +422,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
         }
       }
     };
-    KStream<D> ks(a, b, kvh, s_end - 1, lds);
-    ks.begin(s_begin);
     const int first_masked = lim_min >= 0 ? (lim_min + 1) / kStepTokens : 0;
     const int plain_end = max(s_begin, min(s_end, first_masked));
+    KStream<D> ks(a, b, kvh, s_end - 1, lds);
+    ks.permute(plain_end - s_begin, segment_hash(b, kvh, s_begin));  // sums do not depend on the order
+    ks.begin(s_begin);
     for (int s = s_begin; s < plain_end; ++s) {
       ks.advance(s);
       u32x4 k[D / 32];
