@@ -90,6 +90,33 @@ def test_verify_full_size_sampled(name):
                        f"verify {name} (full size)")
 
 
+def test_verify_walk_multiplier_43():
+    """Verify takes a segment's unmasked steps in the order (A v + rot) mod n
+    with A = 37, or 41 when 37 divides n, or 43 when 41 divides n too. Two
+    row tiles run 2048 resident waves on 256 CUs; 2048 units (B = 256, 8 KV
+    heads) of 1518 steps (24288 tokens) give every wave exactly one unit,
+    whose first 1517 = 37 * 41 steps are unmasked at n_q = 5, so every unit
+    walks with A = 43. Any unit would show a broken walk (a step read twice
+    and another skipped); sampled units are checked against the oracle."""
+    class W:
+        num_q_heads, num_kv_heads = 32, 8
+    B, L, n_q, d = 256, 24288, 5, 128
+    lens = [L] * B
+    kv_t = paged_kv(4343, lens, 8, d, BF16, "cuda", shuffle=False)
+    q = queries(4343, 1, (B, n_q, 32, d), BF16, "cuda", scale=d ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, n_q, 32), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, n_q, 32, 8, d, L), "cuda")
+    sd.sd_verify_attn(kv, q, n_q, 32, L, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check_units_verify(W, lens, kv_t, q, out, lse, sample_sequences(lens, 8, 4343, n_seq=4),
+                       "verify 2048 units of 1517 unmasked steps (walk multiplier 43)")
+    del kv_t, kv, q, out, lse, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["llama8b-b128-l32k-snapkv", "ragged-b256-l4k-32k", "llama70b-b64-l16k"])
 def test_verify_rows_equal_truncated_decodes_every_unit(name):
     """Every unit at full size, by a property: verify's query row i sees
