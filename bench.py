@@ -22,7 +22,9 @@ After that, `round` times one whole self-speculative round at the same shape
 (draft steps with KV append and sampling, verify, accept, roll back), eager and
 replayed from a HIP graph, and dense decode as the attention-only target step;
 `per_sequence_budgets` times SnapKV with one budget per sequence and a draft
-step on the ragged B=256 batch; `dynamic_topk` times a top-K attention draft
+step on the ragged B=256 batch; `snapkv_two_calls` times SnapKV split into the
+window's softmax normalisers and the selection given them (one K pass: the
+cost for a caller whose prefill attention returned them); `dynamic_topk` times a top-K attention draft
 step (selection over the whole cache, then the per-head draft);
 `speedup_model` evaluates the analytic speedup model (best speculation length
 and attention-side speedup per draft kind and budget) on measured times;
@@ -454,6 +456,51 @@ def measure_round(wl, reps=10):
             "budget_over_context": w.budget / wl.L}
 
 
+def measure_snapkv_lse(wl, reps=10):
+    """SnapKV in two calls (MagicDec notes, Appendix A.1: the set is built at
+    prefill, whose attention of the window queries yields their softmax
+    normalisers): sd_snapkv_window_lse (pass 1 alone) and
+    sd_snapkv_select_lse (the selection from given normalisers: one K pass).
+    The second is what a caller pays whose prefill attention returned the
+    window's log-sum-exp."""
+    import torch
+
+    sd, w = wl.sd, wl.w
+    B, Hq, Hkv, d, W = wl.B, wl.Hq, wl.Hkv, wl.d, w.window
+    dev = wl.q.device
+    lse = torch.empty((B, W, Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty_like(wl.idx)
+    sel = torch.empty_like(wl.sel)
+
+    def window_lse():
+        sd.sd_snapkv_window_lse(wl.kv, wl.q_obs, W, Hq, wl.L, 1.0, lse, wl.ws_snap)
+
+    def select_lse():
+        sd.sd_snapkv_select_lse(wl.kv, wl.q_obs, lse, W, Hq, w.pool_kernel, w.budget, wl.L, 1.0, idx, sel,
+                                wl.ws_snap)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_lse, t_sel = timed(window_lse), timed(select_lse)
+    idx1 = torch.empty_like(idx)
+    sel1 = torch.empty_like(sel)
+    sd.sd_snapkv_select(wl.kv, wl.q_obs, W, Hq, w.pool_kernel, w.budget, wl.L, 1.0, idx1, sel1, wl.ws_snap)
+    same = int((idx == idx1).all(dim=2).sum().item())
+    k_bytes = B * wl.L * Hkv * d * 2
+    return {"window_lse_ms": t_lse, "select_given_lse_ms": t_sel,
+            "select_given_lse_K_GBps": k_bytes / (t_sel * 1e-3) / 1e9,
+            "units_equal_to_one_call": same, "units": B * Hkv}
+
+
 def measure_topk(wl, reps=10):
     """Dynamic top-K attention draft step at the bench shape (MagicDec notes
     §4.4): per query head, the budget positions with the largest q.k over the
@@ -809,6 +856,13 @@ def main():
         log(f"top-K draft step: select {topk['select_ms']:.3f} ms + attention {topk['attn_ms']:.3f} ms "
             f"= {topk['step_ms']:.3f} ms ({topk['step_over_static_draft']:.1f}x the SnapKV draft step)")
 
+    snap2 = None
+    if not args.no_round:
+        snap2 = measure_snapkv_lse(wl)
+        log(f"snapkv in two calls: window lse {snap2['window_lse_ms']:.3f} ms, selection given it "
+            f"{snap2['select_given_lse_ms']:.3f} ms ({snap2['units_equal_to_one_call']} of {snap2['units']} "
+            f"units as the one-call selection)")
+
     model = None
     if not args.no_round:
         model = measure_model(wl, rnd, topk, float(wl.n_acc.float().mean().item()))
@@ -868,6 +922,7 @@ def main():
         "cpu_baseline": cpu,
         "round": rnd,
         "per_sequence_budgets": het,
+        "snapkv_two_calls": snap2,
         "dynamic_topk": topk,
         "speedup_model": model,
         "other_workloads": cfgs,

@@ -202,6 +202,43 @@ size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window, int32_t nu
                                        int32_t num_kv_heads, int32_t max_kv_len);
 
 /*
+ * The observation window's softmax normalisers, step 1 of sd_snapkv_select
+ * alone (MagicDec notes, Appendix A.1: the SnapKV set is built at prefill,
+ * where the attention of the window queries is computed anyway; a prefill
+ * attention kernel returns these values as its log-sum-exp).
+ * lse: float32 [batch, window, num_q_heads], device: for sequence b with
+ *   L = kv_lens[b], lse[b, w, h] = ln sum_j exp(softmax_scale * q_obs[b, w, h] . k_j)
+ *   over j = 0 .. L - window + w of KV head h / (num_q_heads / num_kv_heads);
+ *   -inf for a row that sees no key (L - window + w < 0). Every sequence is
+ *   scored, whatever its length.
+ * q_obs, softmax_scale, max_kv_len and the limits are those of
+ * sd_snapkv_select (no budget or pool kernel). Workspace:
+ * sd_snapkv_select_workspace_size. One pass over K.
+ */
+sd_status sd_snapkv_window_lse(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                               int32_t window, int32_t num_q_heads, int32_t max_kv_len,
+                               float softmax_scale, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * sd_snapkv_select with the window normalisers of step 1 given instead of
+ * computed (MagicDec notes, §4.4 and Appendix A.1: the window's attention
+ * comes from the prefill): obs_lse float32 [batch, window, num_q_heads],
+ * device, as written by sd_snapkv_window_lse, with p = exp(softmax_scale *
+ * q.k - obs_lse) in step 2. One pass over K instead of two. With the values
+ * sd_snapkv_window_lse returns the selection equals sd_snapkv_select's up to
+ * the fp32 rounding of the normalisers (votes within a few units in the last
+ * place), so only near ties at the cut can differ. Finite values are the
+ * caller's to supply (-inf marks a row that sees no key). Other arguments,
+ * outputs, limits and workspace: as sd_snapkv_select.
+ */
+sd_status sd_snapkv_select_lse(const sd_kv_cache *kv, const void *q_obs, const float *obs_lse,
+                               int32_t batch, int32_t window, int32_t num_q_heads,
+                               int32_t pool_kernel, int32_t budget, int32_t max_kv_len,
+                               float softmax_scale, int32_t *idx, int32_t *sel_lens,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * SnapKV with one budget per sequence (MagicDec notes, §4.3: the best draft
  * budget depends on batch size and context length, so a ragged batch may give
  * each sequence its own): as sd_snapkv_select, with sequence b selected on

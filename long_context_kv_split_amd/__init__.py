@@ -3,7 +3,9 @@
 The computation lives in libsdkv.so, a HIP library with the C ABI of
 include/sd.h: verify attention over a paged bf16 KV cache (split-KV MFMA
 kernel plus combine), sparse draft attention over gathered positions,
-StreamingLLM and SnapKV draft-KV selection (one budget, or one per sequence),
+StreamingLLM and SnapKV draft-KV selection (one budget, or one per sequence;
+or in two calls, the window's softmax normalisers and the selection from
+them),
 per-step top-K attention selection, modified-rejection speculative acceptance,
 the round's cache bookkeeping (KV append, length advance, draft over the
 selection plus the appended tail), and the analytic speedup model (host
@@ -35,7 +37,9 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_kv_cache,
     sd_snapkv_select,
     sd_snapkv_select_budgets,
+    sd_snapkv_select_lse,
     sd_snapkv_select_workspace_size,
+    sd_snapkv_window_lse,
     sd_spec_accept,
     sd_spec_accept_noalloc,
     sd_spec_accept_workspace_size,

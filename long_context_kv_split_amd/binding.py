@@ -62,6 +62,8 @@ _SIGNATURES = {
     "sd_snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_snapkv_select_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "sd_snapkv_select_budgets": (_I, [_KV, _P, _I, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "sd_snapkv_window_lse": (_I, [_KV, _P, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
+    "sd_snapkv_select_lse": (_I, [_KV, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_topk_select": (_I, [_KV, _P, _I, _I, _I, _I, _P, _P, _P, _S, _P]),
     "sd_topk_select_workspace_size": (_S, [_I, _I, _I, _I]),
     "sd_spec_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
@@ -297,6 +299,30 @@ def sd_snapkv_select(kv, q_obs, window, num_q_heads, pool_kernel, budget, max_kv
     wp, wb = _ws(workspace, need)
     _check(lib().sd_snapkv_select(kv.ref, qp, B, window, num_q_heads, pool_kernel, budget, max_kv_len,
                                   softmax_scale, ip, sp, wp, wb, _stream(stream)), "sd_snapkv_select")
+
+
+def sd_snapkv_window_lse(kv, q_obs, window, num_q_heads, max_kv_len, softmax_scale, lse, workspace=None,
+                         stream=None):
+    B, d = kv.batch, kv.head_dim
+    qp = _dev(q_obs, "q_obs", kv.dtype, B * window * num_q_heads * d)
+    lp = _dev(lse, "lse", torch.float32, B * window * num_q_heads)
+    need = sd_snapkv_select_workspace_size(B, window, num_q_heads, kv.num_kv_heads, max_kv_len)
+    wp, wb = _ws(workspace, need)
+    _check(lib().sd_snapkv_window_lse(kv.ref, qp, B, window, num_q_heads, max_kv_len, softmax_scale, lp, wp,
+                                      wb, _stream(stream)), "sd_snapkv_window_lse")
+
+
+def sd_snapkv_select_lse(kv, q_obs, obs_lse, window, num_q_heads, pool_kernel, budget, max_kv_len,
+                         softmax_scale, idx, sel_lens, workspace=None, stream=None):
+    B, d = kv.batch, kv.head_dim
+    qp = _dev(q_obs, "q_obs", kv.dtype, B * window * num_q_heads * d)
+    lp = _dev(obs_lse, "obs_lse", torch.float32, B * window * num_q_heads)
+    ip = _dev(idx, "idx", torch.int32, B * kv.num_kv_heads * budget)
+    sp = _dev(sel_lens, "sel_lens", torch.int32, B)
+    need = sd_snapkv_select_workspace_size(B, window, num_q_heads, kv.num_kv_heads, max_kv_len)
+    wp, wb = _ws(workspace, need)
+    _check(lib().sd_snapkv_select_lse(kv.ref, qp, lp, B, window, num_q_heads, pool_kernel, budget, max_kv_len,
+                                      softmax_scale, ip, sp, wp, wb, _stream(stream)), "sd_snapkv_select_lse")
 
 
 def sd_snapkv_select_budgets(kv, q_obs, window, num_q_heads, pool_kernel, budgets, max_budget, max_kv_len,

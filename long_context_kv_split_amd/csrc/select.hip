@@ -96,6 +96,8 @@ struct SnapParams {
   int32_t len_cap, vote_stride;
   int32_t pool_kernel, budget;  // budget: the largest budget and the width of an idx row
   const int32_t *budgets;       // [B] per-sequence budgets, or null (every sequence uses `budget`)
+  const float *obs_lse;         // [B, W, Hq] window normalisers (natural log) given by the caller, or null
+  float *lse_out;               // [B, W, Hq] window normalisers written by snap_lse_kernel
   float scale_log2;
   // top-K attention
   uint32_t *keys;      // [B*Hq, key_stride] candidate order keys of q.k (per scoring segment)
@@ -453,6 +455,67 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
   KStream<D>::drain();
 }
 
+// Merge the pass-1 statistics of unit u over its segments: lane (g, r) ends
+// with (max, sum) of row 16 rb + r in log2 units. The unit's slots (many when
+// a few units are spread over all waves) are split among the four lanes of
+// each row, lane group g taking slots s0 + g, s0 + g + 4, ..., with the loads
+// of kMergeBatch slots per lane issued together (addresses clamped, values
+// masked), then merged across the groups; every caller merges in the same
+// order.
+template <int NB>
+__device__ __forceinline__ void snap_merge_unit(const SnapParams &a, int u, float (&mm)[NB], float (&ll)[NB]) {
+  constexpr int kMergeBatch = 4;
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const int s0 = a.sc.slot_base[u], n_slots = a.sc.slot_base[u + 1] - s0;
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    mm[rb] = kNegInf;
+    ll[rb] = 0.f;
+  }
+  for (int base = 0; base < n_slots; base += 4 * kMergeBatch) {
+    f32x2 v[kMergeBatch][NB];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int s = s0 + min(base + 4 * i + g, n_slots - 1);
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const int R = min(rb * 16 + r, a.rows - 1);
+        v[i][rb] = *reinterpret_cast<const f32x2 *>(a.stats + ((size_t)s * a.rows + R) * 2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (base + 4 * i + g < n_slots) {
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) merge_ml(mm[rb], ll[rb], v[i][rb].x, v[i][rb].y);
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) rows4_merge(mm[rb], ll[rb]);
+}
+
+// The window normalisers alone: one wave per unit merges its pass-1
+// statistics and writes lse[b, w, h] = ln 2 * (max + log2 sum) of row
+// R = w * G + hl (h = kvh * G + hl), -inf for a row that sees no key.
+template <int NB>
+__global__ __launch_bounds__(64) void snap_lse_kernel(SnapParams a) {
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv, kvh = u % a.Hkv;
+  const int lane = lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  float mm[NB], ll[NB];
+  snap_merge_unit<NB>(a, u, mm, ll);
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int R = rb * 16 + r;
+    if (g == 0 && R < a.rows)
+      a.lse_out[((size_t)b * a.W + R / a.G) * a.Hq + (size_t)kvh * a.G + R % a.G] =
+          ll[rb] > 0.f ? (mm[rb] + __log2f(ll[rb])) * kLn2 : kNegInf;
+  }
+}
+
 // Pass 2: votes of the prefix keys [0, L - W): merge the unit's pass-1
 // statistics into each row's log2 normaliser, recompute the scores, and sum
 // the normalised weights over the window rows of the group.
@@ -473,51 +536,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sn
     const int s_end = __builtin_amdgcn_readfirstlane(min(s_end_all, (npre + kStepTokens - 1) / kStepTokens));
     if (s_begin >= s_end) return;
     const int u = b * a.Hkv + kvh;
-    const int s0 = a.sc.slot_base[u], s1 = a.sc.slot_base[u + 1];
     // Scores are computed as S = Q K^T (window rows on M, keys on N): lane
     // (g, r) holds rows 16*rb + 4g + e of key r, so a key's vote is an in-lane
     // sum over (rb, e) plus a sum over the four lane groups. off[rb][e]: max +
     // log2(sum) of that row (+inf for padding rows: p = 0).
-    // The unit's segment statistics (many slots when a few units are spread
-    // over all waves) are merged by the four lanes of each row, lane group g
-    // taking slots s0 + g, s0 + g + 4, ..., with the loads of kMergeBatch slots
-    // per lane issued together (addresses clamped, values masked), then merged
-    // across the groups; every wave of the unit merges in the same order.
-    constexpr int kMergeBatch = 4;
-    float mm[NB], ll[NB];
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      mm[rb] = kNegInf;
-      ll[rb] = 0.f;
-    }
-    const int n_slots = s1 - s0;  // >= 1: this wave holds one of them
-    for (int base = 0; base < n_slots; base += 4 * kMergeBatch) {
-      f32x2 v[kMergeBatch][NB];
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i) {
-        const int s = s0 + min(base + 4 * i + g, n_slots - 1);
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-          const int R = min(rb * 16 + r, a.rows - 1);
-          v[i][rb] = *reinterpret_cast<const f32x2 *>(a.stats + ((size_t)s * a.rows + R) * 2);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i) {
-        if (base + 4 * i + g < n_slots) {
-#pragma unroll
-          for (int rb = 0; rb < NB; ++rb) merge_ml(mm[rb], ll[rb], v[i][rb].x, v[i][rb].y);
-        }
-      }
-    }
     float off[NB][4];
+    if (a.obs_lse != nullptr) {
+      // normalisers given: row R = w * G + hl is (b, w, kvh * G + hl) of obs_lse
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      rows4_merge(mm[rb], ll[rb]);
-      const bool live = rb * 16 + r < a.rows;
-      const float o = (live && ll[rb] > 0.f) ? mm[rb] + __log2f(ll[rb]) : __builtin_inff();  // row 16 rb + r
+      for (int rb = 0; rb < NB; ++rb) {
+        const int R = rb * 16 + r;
+        float o = __builtin_inff();
+        if (R < a.rows) {
+          const float x = a.obs_lse[((size_t)b * a.W + R / a.G) * a.Hq + (size_t)kvh * a.G + R % a.G];
+          if (x > kNegInf) o = x * kLog2e;
+        }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) off[rb][e] = __shfl(o, 4 * g + e, 64);
+        for (int e = 0; e < 4; ++e) off[rb][e] = __shfl(o, 4 * g + e, 64);
+      }
+    } else {
+      float mm[NB], ll[NB];
+      snap_merge_unit<NB>(a, u, mm, ll);
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const bool live = rb * 16 + r < a.rows;
+        const float o = (live && ll[rb] > 0.f) ? mm[rb] + __log2f(ll[rb]) : __builtin_inff();  // row 16 rb + r
+#pragma unroll
+        for (int e = 0; e < 4; ++e) off[rb][e] = __shfl(o, 4 * g + e, 64);
+      }
     }
     u32x4 q[NB][D / 32];
     snap_load_q<D, NB>(a, b, kvh, q);
@@ -1447,29 +1493,38 @@ void launch_topk_reg(SnapParams &a, unsigned blocks, int64_t npre_cap, hipStream
     snap_topk_kernel<TH, 64><<<blocks, TH, 0, st>>>(a);
 }
 
+// What a SnapKV call computes: the whole selection; the window normalisers
+// alone (pass 1 and a merge); or the selection from normalisers the caller
+// gives (pass 2 and the top-K, no pass 1).
+enum class SnapMode { kSelect, kWindowLse, kSelectFromLse };
+
 template <int D, int NB>
-void launch_snap_pair(SnapParams &a, hipStream_t st) {
+void launch_snap_passes(SnapParams &a, SnapMode mode, hipStream_t st) {
   static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(snap_stats_kernel<D, NB>), 2 * kSimdsPerCU,
                                    cache);
   snap_plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
-  snap_stats_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
-  snap_votes_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  if (mode != SnapMode::kSelectFromLse) snap_stats_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  if (mode == SnapMode::kWindowLse)
+    snap_lse_kernel<NB><<<(unsigned)(a.sc.B * a.Hkv), 64, 0, st>>>(a);
+  else
+    snap_votes_kernel<D, NB><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
 }
 
 template <int D>
-sd_status launch_snap(SnapParams &a, int B, hipStream_t st) {
+sd_status launch_snap(SnapParams &a, int B, SnapMode mode, hipStream_t st) {
   switch ((a.rows + 15) / 16) {
-    case 1: launch_snap_pair<D, 1>(a, st); break;
-    case 2: launch_snap_pair<D, 2>(a, st); break;
-    case 3: launch_snap_pair<D, 3>(a, st); break;
-    case 4: launch_snap_pair<D, 4>(a, st); break;
-    case 5: launch_snap_pair<D, 5>(a, st); break;
-    case 6: launch_snap_pair<D, 6>(a, st); break;
-    case 7: launch_snap_pair<D, 7>(a, st); break;
-    case 8: launch_snap_pair<D, 8>(a, st); break;
+    case 1: launch_snap_passes<D, 1>(a, mode, st); break;
+    case 2: launch_snap_passes<D, 2>(a, mode, st); break;
+    case 3: launch_snap_passes<D, 3>(a, mode, st); break;
+    case 4: launch_snap_passes<D, 4>(a, mode, st); break;
+    case 5: launch_snap_passes<D, 5>(a, mode, st); break;
+    case 6: launch_snap_passes<D, 6>(a, mode, st); break;
+    case 7: launch_snap_passes<D, 7>(a, mode, st); break;
+    case 8: launch_snap_passes<D, 8>(a, mode, st); break;
     default: return SD_ERR_UNSUPPORTED;
   }
+  if (mode == SnapMode::kWindowLse) return sdh::launch_status();
   const unsigned blocks = (unsigned)(B * a.Hkv);
   const int64_t npre_cap = (int64_t)a.len_cap - a.W;
   if (a.pool_kernel / 2 > kMaxPoolHalf || npre_cap > (int64_t)kTopkThreads * 64)
@@ -1504,18 +1559,25 @@ extern "C" size_t sd_snapkv_select_workspace_size(int32_t batch, int32_t window,
 
 namespace {
 
-sd_status snapkv_impl(const sd_kv_cache *kv, const void *q_obs, int32_t batch, int32_t window,
-                      int32_t num_q_heads, int32_t pool_kernel, const int32_t *budgets, int32_t budget,
-                      int32_t max_kv_len, float softmax_scale, int32_t *idx, int32_t *sel_lens,
-                      void *workspace, size_t workspace_bytes, void *stream) {
+sd_status snapkv_impl(SnapMode mode, const sd_kv_cache *kv, const void *q_obs, const float *obs_lse,
+                      int32_t batch, int32_t window, int32_t num_q_heads, int32_t pool_kernel,
+                      const int32_t *budgets, int32_t budget, int32_t max_kv_len, float softmax_scale,
+                      int32_t *idx, int32_t *sel_lens, float *lse_out, void *workspace,
+                      size_t workspace_bytes, void *stream) {
   sd_status s = sdh::check_kv(kv, false);
   if (s != SD_OK) return s;
-  SD_REQUIRE(q_obs != nullptr && idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+  SD_REQUIRE(q_obs != nullptr, SD_ERR_INVALID_ARG);
+  if (mode == SnapMode::kWindowLse) {
+    SD_REQUIRE(lse_out != nullptr, SD_ERR_INVALID_ARG);
+  } else {
+    SD_REQUIRE(idx != nullptr && sel_lens != nullptr, SD_ERR_INVALID_ARG);
+    SD_REQUIRE(mode != SnapMode::kSelectFromLse || obs_lse != nullptr, SD_ERR_INVALID_ARG);
+    SD_REQUIRE(budget > window, SD_ERR_INVALID_ARG);
+    SD_REQUIRE(pool_kernel >= 1 && (pool_kernel & 1) == 1, SD_ERR_INVALID_ARG);
+  }
   SD_REQUIRE(sdh::aligned16(q_obs), SD_ERR_INVALID_ARG);
   SD_REQUIRE(batch > 0 && window >= 1 && num_q_heads > 0, SD_ERR_INVALID_ARG);
   SD_REQUIRE(num_q_heads % kv->num_kv_heads == 0, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(budget > window, SD_ERR_INVALID_ARG);
-  SD_REQUIRE(pool_kernel >= 1 && (pool_kernel & 1) == 1, SD_ERR_INVALID_ARG);
   SD_REQUIRE(max_kv_len >= 0 && (int64_t)max_kv_len <= (int64_t)kv->max_pages * kv->page_size,
              SD_ERR_INVALID_ARG);
   // the scaled scores (and the stats pass's lazily rebased row maxima) are
@@ -1556,10 +1618,12 @@ sd_status snapkv_impl(const sd_kv_cache *kv, const void *q_obs, int32_t batch, i
   a.pool_kernel = pool_kernel;
   a.budget = budget;
   a.budgets = budgets;
+  a.obs_lse = mode == SnapMode::kSelectFromLse ? obs_lse : nullptr;
+  a.lse_out = lse_out;
   a.scale_log2 = softmax_scale * kLog2e;
   hipStream_t st = sdh::as_stream(stream);
-  if (kv->head_dim == 128) return launch_snap<128>(a, batch, st);
-  return launch_snap<64>(a, batch, st);
+  if (kv->head_dim == 128) return launch_snap<128>(a, batch, mode, st);
+  return launch_snap<64>(a, batch, mode, st);
 }
 
 }  // namespace
@@ -1569,8 +1633,28 @@ extern "C" sd_status sd_snapkv_select(const sd_kv_cache *kv, const void *q_obs, 
                                       int32_t budget, int32_t max_kv_len, float softmax_scale,
                                       int32_t *idx, int32_t *sel_lens, void *workspace,
                                       size_t workspace_bytes, void *stream) {
-  return snapkv_impl(kv, q_obs, batch, window, num_q_heads, pool_kernel, nullptr, budget, max_kv_len,
-                     softmax_scale, idx, sel_lens, workspace, workspace_bytes, stream);
+  return snapkv_impl(SnapMode::kSelect, kv, q_obs, nullptr, batch, window, num_q_heads, pool_kernel, nullptr,
+                     budget, max_kv_len, softmax_scale, idx, sel_lens, nullptr, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" sd_status sd_snapkv_window_lse(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
+                                          int32_t window, int32_t num_q_heads, int32_t max_kv_len,
+                                          float softmax_scale, float *lse, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  // budget 0: every sequence with a key is scored
+  return snapkv_impl(SnapMode::kWindowLse, kv, q_obs, nullptr, batch, window, num_q_heads, 1, nullptr, 0,
+                     max_kv_len, softmax_scale, nullptr, nullptr, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" sd_status sd_snapkv_select_lse(const sd_kv_cache *kv, const void *q_obs, const float *obs_lse,
+                                          int32_t batch, int32_t window, int32_t num_q_heads,
+                                          int32_t pool_kernel, int32_t budget, int32_t max_kv_len,
+                                          float softmax_scale, int32_t *idx, int32_t *sel_lens,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+  return snapkv_impl(SnapMode::kSelectFromLse, kv, q_obs, obs_lse, batch, window, num_q_heads, pool_kernel,
+                     nullptr, budget, max_kv_len, softmax_scale, idx, sel_lens, nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 extern "C" sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void *q_obs, int32_t batch,
@@ -1580,8 +1664,9 @@ extern "C" sd_status sd_snapkv_select_budgets(const sd_kv_cache *kv, const void 
                                               int32_t *sel_lens, void *workspace, size_t workspace_bytes,
                                               void *stream) {
   SD_REQUIRE(budgets != nullptr, SD_ERR_INVALID_ARG);
-  return snapkv_impl(kv, q_obs, batch, window, num_q_heads, pool_kernel, budgets, max_budget, max_kv_len,
-                     softmax_scale, idx, sel_lens, workspace, workspace_bytes, stream);
+  return snapkv_impl(SnapMode::kSelect, kv, q_obs, nullptr, batch, window, num_q_heads, pool_kernel, budgets,
+                     max_budget, max_kv_len, softmax_scale, idx, sel_lens, nullptr, workspace, workspace_bytes,
+                     stream);
 }
 
 namespace {

@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 221
+    assert sd.version() == 222
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
@@ -174,6 +174,46 @@ def test_snapkv_rejects_invalid_arguments(L, over, args, want):
     a.update(args)
     st = L.sd_snapkv_select(ctypes.byref(kv), a.get("q", FAKE), 2, a["window"], 8, a["pool"], a["budget"],
                             a["max_len"], a["scale"], FAKE, FAKE, WS, a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(lse=None), sd.SD_ERR_INVALID_ARG),
+    (dict(q=None), sd.SD_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p(0x5008)), sd.SD_ERR_INVALID_ARG),
+    (dict(window=0), sd.SD_ERR_INVALID_ARG),
+    (dict(window=40), sd.SD_ERR_UNSUPPORTED),         # G * window > 128
+    (dict(max_len=1000), sd.SD_ERR_INVALID_ARG),
+    (dict(scale=0.0), sd.SD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), sd.SD_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), sd.SD_ERR_WORKSPACE),
+])
+def test_snapkv_window_lse_rejects_invalid_arguments(L, args, want):
+    kv = _kv()
+    a = dict(q=FAKE, lse=FAKE, window=8, max_len=64, ws_bytes=1 << 30, scale=1.0)
+    a.update(args)
+    st = L.sd_snapkv_window_lse(ctypes.byref(kv), a["q"], 2, a["window"], 8, a["max_len"], a["scale"], a["lse"],
+                                WS, a["ws_bytes"], None)
+    assert st == want
+
+
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    (dict(lse=None), sd.SD_ERR_INVALID_ARG),
+    (dict(idx=None), sd.SD_ERR_INVALID_ARG),
+    (dict(budget=8), sd.SD_ERR_INVALID_ARG),          # budget <= window
+    (dict(pool=4), sd.SD_ERR_INVALID_ARG),
+    (dict(window=40, budget=64), sd.SD_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), sd.SD_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), sd.SD_ERR_WORKSPACE),
+])
+def test_snapkv_select_lse_rejects_invalid_arguments(L, args, want):
+    kv = _kv()
+    a = dict(lse=FAKE, idx=FAKE, window=8, pool=7, budget=32, max_len=64, ws_bytes=1 << 30, scale=1.0)
+    a.update(args)
+    st = L.sd_snapkv_select_lse(ctypes.byref(kv), FAKE, a["lse"], 2, a["window"], 8, a["pool"], a["budget"],
+                                a["max_len"], a["scale"], a["idx"], FAKE, WS, a["ws_bytes"], None)
     assert st == want
 
 

@@ -15,7 +15,8 @@ import torch
 import long_context_kv_split_amd as sd
 import oracle
 from synth import WORKLOADS, dyadic_uniforms, gumbel_tokens, logits, paged_kv, queries, workload_lens
-from tests.gpu_helpers import check_accept, compare_attn, dirty_workspace, ensure_lib, gathered_decode, say, unit_cache
+from tests.gpu_helpers import (BF16_LSE, check_accept, compare_attn, dirty_workspace, ensure_lib, gathered_decode,
+                               say, unit_cache)
 from tests.parity_log import record
 
 pytestmark = pytest.mark.gpu
@@ -288,6 +289,58 @@ def test_snapkv_select_and_draft_full_size_sampled():
     # fp32 vs fp64 ordering of pooled votes within 1e-5 of the cut: about one
     # unit in a hundred is expected at this shape
     assert len(units) >= 64 and near <= 3, stats
+
+
+def test_snapkv_two_calls_full_size():
+    """B=128, 32k context: sd_snapkv_window_lse on sampled units against the
+    oracle's verify attention of the window queries, and the selection from
+    those normalisers (sd_snapkv_select_lse) against the one-call selection on
+    every unit: equal, or different only at near ties of the plain PyTorch
+    fp32 pooled votes (within 1e-5 of the cut)."""
+    w, lens, kv_t, _ = build("llama8b-b128-l32k-snapkv")
+    B, Hq, Hkv, G, d, W = w.batch, w.num_q_heads, w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.head_dim, w.window
+    L = max(lens)
+    q_obs = queries(w.seed, 4, (B, W, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L), "cuda")
+    lse = torch.full((B, W, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    sd.sd_snapkv_window_lse(kv, q_obs, W, Hq, L, 1.0, lse, ws)
+    idx1 = torch.full((B, Hkv, w.budget), 7, dtype=torch.int32, device="cuda")
+    sel1 = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+    sd.sd_snapkv_select(kv, q_obs, W, Hq, w.pool_kernel, w.budget, L, 1.0, idx1, sel1, ws)
+    idx2 = torch.full_like(idx1, 7)
+    sel2 = torch.full_like(sel1, 7)
+    sd.sd_snapkv_select_lse(kv, q_obs, lse, W, Hq, w.pool_kernel, w.budget, L, 1.0, idx2, sel2, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all() and torch.equal(sel1, sel2)
+    worst = 0.0
+    units = sample_sequences(lens, Hkv, w.seed + 5, n_seq=4)
+    for b, g in units:
+        k, v, table, Lb = unit_cache(kv_t, b, g)
+        heads = slice(g * G, (g + 1) * G)
+        _, l_ref = oracle.verify_attn(q_obs[b:b + 1, :, heads].cpu(), k, v, table, Lb, 1.0)
+        worst = max(worst, float(np.abs(lse[b:b + 1, :, heads].double().cpu().numpy() - l_ref).max()))
+    # the lse bar of every attention output (fp32 sums over 32k keys, some
+    # boosted 4x: lse values near 15 carry ~3e-6 relative rounding)
+    assert worst <= BF16_LSE, worst
+    same = (idx1 == idx2).all(dim=2)
+    differ = 0
+    for b in (~same).any(dim=1).nonzero().flatten().tolist():
+        pooled = torch_snapkv_pooled(kv_t, q_obs, b, W, w.pool_kernel, lens[b])
+        keep = w.budget - W
+        thr = torch.sort(pooled, dim=1, descending=True).values[:, keep - 1].cpu().numpy()
+        pn = pooled.cpu().numpy()
+        for g in range(Hkv):
+            if bool(same[b, g]):
+                continue
+            differ += 1
+            a, r = idx1[b, g].cpu().numpy(), idx2[b, g].cpu().numpy()
+            for t in set(a.tolist()) ^ set(r.tolist()):
+                assert abs(pn[g, t] - thr[g]) <= 1e-5 * thr[g], (b, g, t, pn[g, t], thr[g])
+    record("snapkv two calls B=128 L=32k", lse_units=len(units), max_lse=worst, units=B * Hkv,
+           units_differing_from_one_call=differ)
+    say(f"  two calls: window lse worst {worst:.2e} on {len(units)} units; {differ} of {B * Hkv} selections "
+        f"differ from the one-call selection (near ties)")
 
 
 def test_snapkv_per_sequence_budgets_full_size_every_unit():

@@ -294,3 +294,62 @@ def test_snapkv_per_sequence_budgets(name, lens, budgets, Hq, Hkv, W):
         o_ref, l_ref = oracle.sparse_attn(q.cpu(), kv_t.k_pages.cpu(), kv_t.v_pages.cpu(), kv_t.page_table.cpu(),
                                           idx_ref, sel_ref, 1.0)
         compare_attn(out, lse, o_ref, l_ref, BF16)
+
+
+LSE_CASES = [
+    # name, Hq, Hkv, d, lens, window, pool, budget, spike_frac
+    ("g4-w8-rows32", 8, 2, 128, [700, 1500], 8, 7, 64, 0.0),
+    ("g4-w32-rows128-spiky", 32, 8, 128, [3000, 2100], 32, 7, 256, 0.10),
+    ("short-rows-see-no-key", 8, 2, 128, [5, 0, 2000, 40], 8, 7, 200, 0.0),
+    ("d64-pool3", 8, 2, 64, [1234, 517], 4, 3, 100, 0.10),
+    ("rows48-ragged-pages", 24, 2, 128, [1111, 4096, 333], 4, 5, 300, 0.05),
+    ("prefix-40k", 8, 2, 64, [40000, 33000], 8, 5, 2048, 0.10),
+]
+LSE_BAR = 3e-5  # fp32 sums of exact bf16 products over up to 40k keys, lse ~ 10
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[c[0] for c in LSE_CASES])
+def test_snapkv_window_lse_and_select_from_it(case):
+    """sd_snapkv_window_lse against the oracle's verify attention of the window
+    queries (query w of the window attends to 0 .. L - W + w, exactly step 1
+    of the selection), including rows that see no key; then
+    sd_snapkv_select_lse fed (a) those values and (b) the oracle's own
+    normalisers, each against the oracle's selection, and (a) against
+    sd_snapkv_select."""
+    name, Hq, Hkv, d, lens, W, pool, budget, spike = case
+    say(f"snapkv window lse {name}: lens={lens} W={W}")
+    seed = zlib.crc32(("lse-" + name).encode()) % 10000
+    kv_t = paged_kv(seed, lens, Hkv, d, BF16, "cuda", shuffle=True, spike_frac=spike)
+    q_obs = queries(seed, 4, (len(lens), W, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    B, mk = len(lens), max(1, max(lens))
+    ws = dirty_workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, mk), "cuda")
+    lse = torch.full((B, W, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    sd.sd_snapkv_window_lse(kv, q_obs, W, Hq, mk, 1.0, lse, ws)
+    torch.cuda.synchronize()
+    _, l_ref = oracle.verify_attn(q_obs, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens, 1.0)
+    l = lse.double().cpu().numpy()
+    dead = np.isneginf(l_ref)
+    assert (np.isneginf(l) == dead).all(), "rows with no visible key differ"
+    lerr = np.abs(l[~dead] - l_ref[~dead]).max() if (~dead).any() else 0.0
+    say(f"  window lse: max err {lerr:.2e}, rows without keys {int(dead.sum())}")
+    assert lerr <= LSE_BAR, lerr
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    W, pool, budget, 1.0, return_pooled=True)
+    idx_full, sel_full = run_snapkv(kv_t, q_obs, W, Hq, pool, budget)
+    near = {}
+    for tag, given in (("own", lse), ("oracle", torch.from_numpy(l_ref).float().cuda())):
+        idx = torch.full((B, Hkv, budget), 7, dtype=torch.int32, device="cuda")
+        sel = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+        sd.sd_snapkv_select_lse(kv, q_obs, given, W, Hq, pool, budget, mk, 1.0, idx, sel,
+                                dirty_workspace(ws.numel(), "cuda"))
+        torch.cuda.synchronize()
+        near[tag] = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
+        if tag == "own":
+            same = int((idx == idx_full).all(dim=2).sum())
+            say(f"  from own lse: {same} of {B * Hkv} units equal sd_snapkv_select's")
+            assert torch.equal(sel, sel_full)
+    say(f"  near-tie units: {near}")
+    record(f"snapkv window lse {name}", rows=int((~dead).sum()), max_lse=float(lerr), near_tie_own=near["own"],
+           near_tie_oracle=near["oracle"])
+    assert max(near.values()) <= max(1, B * Hkv // 8)
