@@ -18,11 +18,12 @@
  *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and
  *    returns without synchronising. A failed validation returns a non-zero
  *    status before any launch and before any write.
- *  - The library allocates no memory. Its only mutable global state is a
+ *  - The library allocates no memory. Its mutable global state is a
  *    per-device cache of resident-wave counts (an occupancy query made once
- *    per kernel and device; a race stores the same value): it sets launch
+ *    per kernel and device; a race stores the same value), which sets launch
  *    sizes and the split-KV schedule only, so a device always computes the
- *    same bits. Calls are thread-safe and re-entrant. Scratch space is the
+ *    same bits; and the per-device scratch array of sd_spec_accept_noalloc
+ *    (see there). Calls are thread-safe and re-entrant. Scratch space is the
  *    caller's `workspace` of at least the size its *_workspace_size function
  *    returns; concurrent calls need distinct workspaces.
  *  - Device-resident integers (page_table, kv_lens, idx, sel_lens,
