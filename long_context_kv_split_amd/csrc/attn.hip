@@ -14,7 +14,9 @@
 // step whatever the length mix, and writes one (m, l, o) partial per unit
 // segment it covers into a slot table of at most waves + units entries. The
 // assignment depends only on shapes and lengths, so results are bitwise
-// reproducible. A combine kernel merges each unit's partials by log-sum-exp;
+// reproducible. Verify waves take the unmasked steps of a segment in a
+// permuted order (StepWalk), which reads pages laid out in order as fast as
+// shuffled ones. A combine kernel merges each unit's partials by log-sum-exp;
 // the call is two launches. Small calls (every unit in one round of the chip,
 // at most 1024 tokens each, one 16-row tile) run one workgroup per unit
 // instead, its waves merging in LDS: one launch.

@@ -50,37 +50,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
-  return __builtin_bit_cast(float, h << 16);
-}
-
 // Two 16-bit halves taken from two dwords: the low halves (hi_half=false) or
 // the high halves (hi_half=true); x supplies bits 0-15 of the result, y 16-31.
 __device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, bool hi_half) {
   return __builtin_amdgcn_perm(y, x, hi_half ? 0x07060302u : 0x05040100u);
-}
-
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
-
-// Sum over the 16 lanes of each row of the wave (lanes 16k .. 16k+15).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }

@@ -137,14 +137,6 @@ __device__ __forceinline__ void lds_write_f32(const char *lds, int byte_off, flo
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 #endif
 }
-__device__ __forceinline__ float lds_read_f32(const char *lds, int byte_off) {
-  float v = 0.f;
-  const uint32_t addr = (uint32_t)(size_t)((const __attribute__((address_space(3))) char *)lds + byte_off);
-#if __HIP_DEVICE_COMPILE__
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
-#endif
-  return v;
-}
 
 // Budget of sequence b (device-side per-sequence values are clamped into
 // [W + 1, budget]).
@@ -345,16 +337,6 @@ __device__ __forceinline__ void rows4_merge(float &m, float &l) {
   m = __uint_as_float(c[0]);
   l = __uint_as_float(d[0]);
   merge_ml(m, l, __uint_as_float(c[1]), __uint_as_float(d[1]));
-}
-
-// Sum over the 16 lanes of each row with DPP (quad xor 1, quad xor 2, half
-// mirror, mirror): every lane of the row ends with the row sum.
-__device__ __forceinline__ float row16_sum_dpp(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
 }
 
 // Pass 1: per segment of a unit, each window row's (max, sum of exp2) of its
