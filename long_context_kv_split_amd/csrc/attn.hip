@@ -483,13 +483,15 @@ void attn_split_kernel(AttnParams a) {
 // g + 8, g + 12 (the tokens of its four copies) in one 16-byte read.
 // Steps per wave in the LDS ring, and with it the resident waves: a deeper
 // ring keeps more bytes in flight per wave but leaves room for fewer waves
-// per CU. Two 16-step tiles (20 query rows at gamma = 4) measured best with
-// two steps (eight waves per CU); one, three or four tiles with four steps
-// (four waves per CU): e.g. the 8k-context batch 0.186 against 0.207 ms,
-// the 70B shape 0.709 against 0.766 ms.
+// per CU. Four steps (four waves per CU, one per SIMD) for every tile count:
+// e.g. the 8k-context batch 0.186 against 0.207 ms with two steps, the 70B
+// shape 0.709 against 0.766 ms. Two tiles (20 query rows at gamma = 4) ran
+// best with two steps (eight waves per CU) while waves walked their pages in
+// order; with the permuted walk four steps are faster (2.49 against
+// 2.53-2.54 ms at B = 128, 32k).
 template <int NB>
 constexpr int stream_ring() {
-  return NB == 2 ? 2 : 4;
+  return 4;
 }
 constexpr int kStreamChunks = 256;   // 16-byte chunks per 16-token step of one tensor (d = 128, bf16)
 constexpr int kStreamWin = 64;       // steps per row window (verify)
@@ -645,13 +647,14 @@ __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *ld
   if constexpr (!SPARSE) {
     // ------------------------------------------------------------- verify
     // The unmasked steps [s_begin, plain_end) are taken in a permuted order
-    // (StepWalk), the masked steps follow in order. Loop indices below are
-    // positions v; phys(v) is the step.
+    // (StepWalk) when there are at least kWalkMinSteps of them, the masked
+    // steps follow in order. Loop indices below are positions v; phys(v) is
+    // the step.
     const int32_t *pt = a.page_table + (size_t)b * a.max_pages;
     const int P = a.page_size;
     const int n_tot = s_end - s_begin;  // >= 1
     const int n_plain = max(0, min(s_end, first_masked) - s_begin);
-    const StepWalk walk(n_plain, segment_hash(b, kvh, s_begin));
+    const StepWalk walk(n_plain >= kWalkMinSteps ? n_plain : 0, segment_hash(b, kvh, s_begin));
     auto phys = [&](int v) { return s_begin + walk(min(v, n_tot - 1)); };
     auto entry_ptr = [&](int v) { return pt + clampi(phys(v) * kStepTokens / P, 0, a.max_pages - 1); };
     auto row_from = [&](int entry, int v) {

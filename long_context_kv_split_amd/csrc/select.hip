@@ -213,7 +213,7 @@ struct KStream {
   }
   // Read positions s_begin .. s_begin + n - 1 in a permuted order (before
   // begin(s_begin); for passes whose result does not depend on the order).
-  __device__ void permute(int n, uint32_t hash) { walk = StepWalk(n, hash); }
+  __device__ void permute(int n, uint32_t hash) { walk = StepWalk(n >= kWalkMinSteps ? n : 0, hash); }
   // Copy the page-table entries of window steps w0 + lane into LDS.
   __device__ void fetch_entries(int w0) {
     lds_dma4(entry_ptr(w0 + lane_id()), entries);
