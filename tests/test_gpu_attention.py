@@ -50,9 +50,9 @@ VERIFY_CASES = [
     # one long sequence: each unit spread over about a thousand waves, so the
     # combine merges ~1000 slots per row (its chunked slot loop)
     ("bf16-one-300k-sequence", BF16, 8, 2, 128, [300000], 4, True, 16),
-    # 37 sequences x 8 KV heads x 256 steps over 2048 resident waves: shares
-    # of exactly 37 steps, so whole-share segments walk with A = 41 (37
-    # divides their step count) instead of 37
+    # 37 sequences x 8 KV heads x 256 steps: shares of 74 steps over 1024
+    # resident waves, straddling unit boundaries; segments this short take
+    # their steps in order
     ("bf16-37-step-shares", BF16, 32, 8, 128, [4096] * 37, 5, False, 16),
 ]
 

@@ -91,20 +91,24 @@ def test_verify_full_size_sampled(name):
                        f"verify {name} (full size)")
 
 
-def test_verify_walk_multiplier_43():
+@pytest.mark.parametrize("L,mult", [(4752, 41), (24288, 43)])
+def test_verify_walk_fallback_multipliers(L, mult):
     """Verify takes a segment's unmasked steps in the order (A v + rot) mod n
-    with A = 37, or 41 when 37 divides n, or 43 when 41 divides n too. Two
-    row tiles run 2048 resident waves on 256 CUs; 2048 units (B = 256, 8 KV
-    heads) of 1518 steps (24288 tokens) give every wave exactly one unit,
-    whose first 1517 = 37 * 41 steps are unmasked at n_q = 5, so every unit
-    walks with A = 43. Any unit would show a broken walk (a step read twice
-    and another skipped); sampled units are checked against the oracle."""
+    with A = 37, or 41 when 37 divides n, or 43 when 41 divides n too. With
+    2048 units (B = 256, 8 KV heads) of equal length and 1024 or 2048
+    resident waves, every wave owns whole units, whose unmasked steps at
+    n_q = 5 number L / 16 - 1: 296 = 37 * 8 (A = 41) at L = 4752 and
+    1517 = 37 * 41 (A = 43) at L = 24288. Any unit would show a broken walk
+    (a step read twice and another skipped); sampled units are checked
+    against the oracle."""
     class W:
         num_q_heads, num_kv_heads = 32, 8
-    B, L, n_q, d = 256, 24288, 5, 128
+    B, n_q, d = 256, 5, 128
+    n = L // 16 - 1
+    assert n % 37 == 0 and (mult == 41) == (n % 41 != 0)
     lens = [L] * B
-    kv_t = paged_kv(4343, lens, 8, d, BF16, "cuda", shuffle=False)
-    q = queries(4343, 1, (B, n_q, 32, d), BF16, "cuda", scale=d ** -0.5)
+    kv_t = paged_kv(mult, lens, 8, d, BF16, "cuda", shuffle=False)
+    q = queries(mult, 1, (B, n_q, 32, d), BF16, "cuda", scale=d ** -0.5)
     kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, n_q, 32), float("nan"), dtype=torch.float32, device="cuda")
@@ -112,8 +116,8 @@ def test_verify_walk_multiplier_43():
     sd.sd_verify_attn(kv, q, n_q, 32, L, 1.0, out, lse, ws)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    check_units_verify(W, lens, kv_t, q, out, lse, sample_sequences(lens, 8, 4343, n_seq=4),
-                       "verify 2048 units of 1517 unmasked steps (walk multiplier 43)")
+    check_units_verify(W, lens, kv_t, q, out, lse, sample_sequences(lens, 8, mult, n_seq=4),
+                       f"verify 2048 units of {n} unmasked steps (walk multiplier {mult})")
     del kv_t, kv, q, out, lse, ws
     torch.cuda.empty_cache()
 
