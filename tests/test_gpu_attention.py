@@ -131,6 +131,9 @@ DRAFT_CASES = [
     ("shared-bf16-d64", BF16, 8, 2, 64, [999, 1234], 1, "shared", 333),
     ("per-head-f32-d128", F32, 16, 2, 128, [777, 1500], 1, "per-head", 200),
     ("per-head-rows64", BF16, 16, 1, 128, [1800], 4, "per-head", 700),
+    # two and three row tiles in the draft (20 and 40 query rows per unit)
+    ("per-head-rows20", BF16, 32, 8, 128, [2500, 900], 5, "per-head", 640),
+    ("shared-rows40", BF16, 64, 8, 128, [1700, 3100], 5, "shared", 512),
     ("stream-2500-sequences", BF16, 8, 2, 128, MANY, 1, "streaming", 48),
     ("per-head-2500-sequences", BF16, 8, 2, 128, MANY, 1, "per-head", 40),
     # one long selection (up to 120k of 250k positions): many resolved
