@@ -122,6 +122,29 @@ def test_verify_walk_fallback_multipliers(L, mult):
     torch.cuda.empty_cache()
 
 
+def test_verify_walk_threshold_boundary():
+    """Segments at the walk's length threshold: 256 units (B = 32, 8 KV
+    heads) of 1024 steps over 1024 resident waves give shares of exactly 256
+    steps, a quarter unit each. The first three quarters have 256 unmasked
+    steps (permuted walk), the last 255 and the masked step (in order).
+    Sampled units against the oracle."""
+    class W:
+        num_q_heads, num_kv_heads = 32, 8
+    B, L, n_q, d = 32, 16384, 5, 128
+    lens = [L] * B
+    kv_t = paged_kv(256, lens, 8, d, BF16, "cuda", shuffle=False)
+    q = queries(256, 1, (B, n_q, 32, d), BF16, "cuda", scale=d ** -0.5)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, n_q, 32), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, n_q, 32, 8, d, L), "cuda")
+    sd.sd_verify_attn(kv, q, n_q, 32, L, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check_units_verify(W, lens, kv_t, q, out, lse, sample_sequences(lens, 8, 256, n_seq=4),
+                       "verify shares of 256 steps (walk threshold)")
+
+
 @pytest.mark.parametrize("name", ["llama8b-b128-l32k-snapkv", "ragged-b256-l4k-32k", "llama70b-b64-l16k"])
 def test_verify_rows_equal_truncated_decodes_every_unit(name):
     """Every unit at full size, by a property: verify's query row i sees
