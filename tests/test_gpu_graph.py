@@ -1,4 +1,5 @@
-"""HIP-graph capture of the prefill-to-accept calls: SnapKV selection, the
+"""HIP-graph capture of the prefill-to-accept calls: SnapKV selection (in one
+call and in two: the window normalisers, then the selection from them), the
 sparse draft over its sets, verify attention and acceptance (gamma = 4),
 captured once and replayed several times, with eager library calls and torch
 work on the same buffers between the replays. Every replay must reproduce the
@@ -51,6 +52,9 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
 
     idx = torch.empty((B, Hkv, budget), dtype=torch.int32, device="cuda")
     sel = torch.empty((B,), dtype=torch.int32, device="cuda")
+    obs_lse = torch.empty((B, W, Hq), dtype=torch.float32, device="cuda")
+    idx2 = torch.empty_like(idx)
+    sel2 = torch.empty_like(sel)
     o_d = torch.empty_like(q_d)
     o_v, lse_v = torch.empty_like(q_v), torch.empty((B, gamma + 1, Hq), dtype=torch.float32, device="cuda")
     n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
@@ -59,10 +63,13 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
     ws_d = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, budget))
     ws_v = sd.workspace(sd.sd_verify_attn_workspace_size(B, gamma + 1, Hq, Hkv, d, L))
     ws_a = sd.workspace(sd.sd_spec_accept_workspace_size(B, gamma, V))
-    outs = (idx, sel, o_d, o_v, lse_v, n_acc, toks)
+    ws_s2 = sd.workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L))
+    outs = (idx, sel, o_d, o_v, lse_v, n_acc, toks, obs_lse, idx2, sel2)
 
     def calls():
         sd.sd_snapkv_select(kv, q_obs, W, Hq, 7, budget, L, 1.0, idx, sel, ws_s)
+        sd.sd_snapkv_window_lse(kv, q_obs, W, Hq, L, 1.0, obs_lse, ws_s2)
+        sd.sd_snapkv_select_lse(kv, q_obs, obs_lse, W, Hq, 7, budget, L, 1.0, idx2, sel2, ws_s2)
         sd.sd_draft_attn_sparse(kv, q_d, 1, Hq, idx, sel, Hkv, budget, 1.0, o_d, None, ws_d)
         sd.sd_verify_attn(kv, q_v, gamma + 1, Hq, L, 1.0, o_v, lse_v, ws_v)
         sd.sd_spec_accept(zt, zd, x, ua, us, gamma, V, 1.0, n_acc, toks, ws_a)
@@ -85,7 +92,7 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
         # and run the library eagerly on other inputs through the same workspaces
         for t in outs:
             t.fill_(-5 if not t.is_floating_point() else float("nan"))
-        for w in (ws_s, ws_d, ws_v, ws_a):
+        for w in (ws_s, ws_s2, ws_d, ws_v, ws_a):
             w.fill_(0xA5)
         if rep % 2 == 1:
             sd.sd_verify_attn(kv, q_v.flip(0).contiguous(), gamma + 1, Hq, L, 1.0, o_v, lse_v, ws_v)
@@ -95,5 +102,5 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         for name, got, ref in zip(("idx", "sel_lens", "draft_out", "verify_out", "verify_lse", "n_accepted",
-                                   "out_tokens"), outs, want):
+                                   "out_tokens", "window_lse", "idx_from_lse", "sel_lens_from_lse"), outs, want):
             assert _same(got, ref), f"replay {rep}: {name} differs from the eager run"

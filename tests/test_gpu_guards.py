@@ -124,6 +124,24 @@ def test_snapkv_and_its_draft_write_only_their_outputs(per_sequence):
     check(out=out, lse=lse, workspace=wsd)
 
 
+def test_snapkv_two_calls_write_only_their_outputs():
+    """The window normalisers (every sequence scored, short ones included)
+    and the selection from them."""
+    say("guards snapkv two calls")
+    d, Hq, Hkv, W, budget = 128, 8, 2, 8, 96
+    kv_t = cache(torch.bfloat16, d, Hkv, spike=0.1)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    B, L = len(LENS), max(LENS)
+    q_obs = queries(91, 4, (B, W, Hq, d), torch.bfloat16, "cuda", scale=d ** -0.5)
+    lse = Guarded((B, W, Hq), torch.float32)
+    ws = guarded_ws(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L))
+    sd.sd_snapkv_window_lse(kv, q_obs, W, Hq, L, 1.0, lse.t, ws.t)
+    check(lse=lse, workspace=ws)
+    idx, sel = Guarded((B, Hkv, budget), torch.int32), Guarded((B,), torch.int32)
+    sd.sd_snapkv_select_lse(kv, q_obs, lse.t, W, Hq, 7, budget, L, 1.0, idx.t, sel.t, ws.t)
+    check(idx=idx, sel_lens=sel, lse=lse, workspace=ws)
+
+
 def test_topk_selection_and_per_head_draft_write_only_their_outputs():
     say("guards top-K")
     d, Hq, Hkv, budget = 128, 8, 2, 64
