@@ -49,7 +49,7 @@ from oracle.selection import (  # noqa: F401
     topk_lowest_index,
 )
 from oracle.accept import accept_outcomes, accept_valid, softmax, spec_accept  # noqa: F401
-from oracle.round import draft_positions, kv_advance, kv_append, sparse_attn_tail  # noqa: F401
+from oracle.round import draft_positions, kv_advance, kv_append, kv_compact, sparse_attn_tail  # noqa: F401
 from oracle.dynamic import topk_attn, topk_scores, topk_select  # noqa: F401
 from oracle.model import best_gamma, omega, round_time, speedup  # noqa: F401
 from oracle.common import f64  # noqa: F401

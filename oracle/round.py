@@ -19,6 +19,9 @@ bookkeeping open; the plainest reading, used here:
     (sparse_attn_tail).
   * A draft token is drawn from q = softmax(z / T) by inverse CDF, which is
     spec_accept with gamma = 0 (the bonus token from p_0): no separate oracle.
+  * The draft's compressed cache may also be materialised once (kv_compact):
+    the selected rows, in list order, as a cache of their own, whose dense
+    decode is the draft over the selection.
 """
 import numpy as np
 
@@ -99,3 +102,31 @@ def sparse_attn_tail(q, k_pages, v_pages, page_table, idx, sel_lens, tail_begin,
             o[b][:, hs, :] = ob.reshape(n_q, len(hs), d)
             lse[b][:, hs] = lb.reshape(n_q, len(hs))
     return o, lse
+
+
+def kv_compact(k_pages, v_pages, page_table, idx, sel_lens, pages_per_seq):
+    """The draft's compressed cache as a cache of its own (MagicDec notes, §4.4
+    and Appendix A.1: the draft reads a static compressed KV cache built once
+    at prefill). For sequence b and KV head g, the K and V rows of the
+    positions idx[b, g or 0, :sel_lens[b]] (one row per KV head, or one shared
+    row), in list order: list entry t goes to page b * pages_per_seq + t // P,
+    slot t % P. Returns float64 pools [B * pages_per_seq, Hkv, P, d]; slots
+    past sel_lens[b] hold NaN (nothing reads them)."""
+    K = f64(k_pages)
+    V = f64(v_pages)
+    pt = i64(page_table)
+    sel = i64(sel_lens)
+    B = pt.shape[0]
+    _, Hkv, P, d = K.shape
+    Kc = np.full((B * pages_per_seq, Hkv, P, d), np.nan)
+    Vc = np.full((B * pages_per_seq, Hkv, P, d), np.nan)
+    none = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        for g in range(Hkv):
+            pos = draft_positions(idx, sel, none, none, b, g)
+            keys = token_rows(K, pt, b, pos, g)
+            vals = token_rows(V, pt, b, pos, g)
+            for t in range(len(pos)):
+                Kc[b * pages_per_seq + t // P, g, t % P] = keys[t]
+                Vc[b * pages_per_seq + t // P, g, t % P] = vals[t]
+    return Kc, Vc

@@ -117,6 +117,13 @@ MUTATIONS = [
      "t = int(lens[b]) + j", "t = int(lens[b]) + j + 1", ["round"]),
     ("advance-keeps-rejected", "round",
      "lens = i64(kv_lens) + int(add)", "lens = i64(kv_lens)", ["round"]),
+    ("compact-wrong-head", "round",
+     "keys = token_rows(K, pt, b, pos, g)\n            vals = token_rows(V, pt, b, pos, g)\n            for t",
+     "keys = token_rows(K, pt, b, pos, (g + 1) % Hkv)\n            vals = token_rows(V, pt, b, pos, (g + 1) % Hkv)\n            for t",
+     ["round"]),
+    ("compact-page-off-by-one", "round",
+     "Kc[b * pages_per_seq + t // P, g, t % P] = keys[t]",
+     "Kc[b * pages_per_seq + (t + 1) // P, g, (t + 1) % P] = keys[t]", ["round"]),
     ("tail-starts-one-late", "round",
      "np.arange(int(i64(tail_begin)[b]), int(i64(kv_lens)[b]), dtype=np.int64)",
      "np.arange(int(i64(tail_begin)[b]) + 1, int(i64(kv_lens)[b]), dtype=np.int64)", ["round"]),

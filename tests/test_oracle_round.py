@@ -10,7 +10,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from oracle.round import draft_positions, kv_advance, kv_append, sparse_attn_tail
+from oracle.round import draft_positions, kv_advance, kv_append, kv_compact, sparse_attn_tail
 
 
 def build_cache(dense, lens, P, extra_pages, rng):
@@ -168,3 +168,68 @@ def test_tail_with_one_set_per_query_head_matches_sdpa():
             pos = list(sel[b, h, :5]) + list(range(tail_begin[b], lens[b]))
             ref = sdpa(q[b, :, h], dense_k[b, pos, g], dense_v[b, pos, g], 0.3)
             assert np.allclose(o[b, :, h], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("idx_heads,P", [(1, 16), (2, 16), (2, 32)])
+def test_compact_cache_rows_by_hand(idx_heads, P):
+    """Every pool row encodes its own (sequence, position, KV head) as values;
+    the compact cache must hold, at page b * pps + t // P, slot t % P of head g,
+    the row of position idx[b, g or 0, t], and NaN past the selection."""
+    rng = np.random.default_rng(11)
+    B, Hkv, d = 2, 2, 4
+    lens = [90, 45]
+    T = max(lens)
+    dense = np.zeros((B, T, Hkv, d))
+    for b in range(B):
+        for t in range(T):
+            for g in range(Hkv):
+                dense[b, t, g] = [b, t, g, 1000 * b + 10 * t + g]
+    K, table = build_cache(dense, lens, P, 1, np.random.default_rng(5))
+    sel_lens = [7, 3]
+    sel = np.full((B, idx_heads, 8), -1)
+    for b in range(B):
+        for gi in range(idx_heads):
+            sel[b, gi, :sel_lens[b]] = np.sort(rng.choice(lens[b], sel_lens[b], replace=False))
+    pps = 2
+    Kc, Vc = kv_compact(K, -K, table, sel, sel_lens, pps)
+    assert Kc.shape == (B * pps, Hkv, P, d)
+    for b in range(B):
+        for g in range(Hkv):
+            for t in range(pps * P):
+                row = Kc[b * pps + t // P, g, t % P]
+                if t < sel_lens[b]:
+                    pos = sel[b, g if idx_heads > 1 else 0, t]
+                    assert list(row) == [b, pos, g, 1000 * b + 10 * pos + g], (b, g, t)
+                    assert np.array_equal(Vc[b * pps + t // P, g, t % P], -row)
+                else:
+                    assert np.isnan(row).all()
+
+
+@pytest.mark.parametrize("idx_heads", [1, 2])
+def test_decode_over_compact_cache_is_the_sparse_draft(idx_heads):
+    """A dense decode (verify with n_q = 1) over the compact cache, with the
+    identity page table and lengths sel_lens, equals the draft over the
+    selection (SDPA over the gathered rows)."""
+    rng = np.random.default_rng(12)
+    B, Hkv, G, d, P = 3, 2, 3, 8, 16
+    lens = [80, 40, 65]
+    dense_k = rng.standard_normal((B, max(lens), Hkv, d))
+    dense_v = rng.standard_normal((B, max(lens), Hkv, d))
+    K, table = build_cache(dense_k, lens, P, 1, np.random.default_rng(6))
+    V, _ = build_cache(dense_v, lens, P, 1, np.random.default_rng(6))
+    sel_lens = [20, 9, 33]
+    pps = 3
+    sel = np.full((B, idx_heads, pps * P), -1)
+    for b in range(B):
+        for gi in range(idx_heads):
+            sel[b, gi, :sel_lens[b]] = np.sort(rng.choice(lens[b], sel_lens[b], replace=False))
+    Kc, Vc = kv_compact(K, V, table, sel, sel_lens, pps)
+    table_c = np.arange(B * pps).reshape(B, pps)
+    q = rng.standard_normal((B, 1, Hkv * G, d))
+    o, lse = oracle.verify_attn(q, Kc, Vc, table_c, sel_lens, 0.4)
+    for b in range(B):
+        for g in range(Hkv):
+            pos = list(sel[b, g if idx_heads > 1 else 0, :sel_lens[b]])
+            for h in range(g * G, (g + 1) * G):
+                ref = sdpa(q[b, :, h], dense_k[b, pos, g], dense_v[b, pos, g], 0.4)
+                assert np.allclose(o[b, :, h], ref, atol=1e-12)
