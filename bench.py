@@ -24,7 +24,9 @@ replayed from a HIP graph, and dense decode as the attention-only target step;
 `per_sequence_budgets` times SnapKV with one budget per sequence and a draft
 step on the ragged B=256 batch; `snapkv_two_calls` times SnapKV split into the
 window's softmax normalisers and the selection given them (one K pass: the
-cost for a caller whose prefill attention returned them); `dynamic_topk` times a top-K attention draft
+cost for a caller whose prefill attention returned them); `compact_draft_cache` copies the SnapKV rows out once (sd_kv_compact) and times
+the draft as a dense decode over that copy beside the gathered draft;
+`dynamic_topk` times a top-K attention draft
 step (selection over the whole cache, then the per-head draft);
 `speedup_model` evaluates the analytic speedup model (best speculation length
 and attention-side speedup per draft kind and budget) on measured times;
@@ -169,6 +171,15 @@ class Workload:
         self.ws_draft = sd.workspace(sd.sd_draft_attn_sparse_workspace_size(B, 1, Hq, Hkv, d, w.budget), dev)
         self.ws_ver = sd.workspace(sd.sd_verify_attn_workspace_size(B, self.n_q, Hq, Hkv, d, self.L), dev)
         self.ws_acc = sd.workspace(sd.sd_spec_accept_workspace_size(B, g, self.V), dev)
+        # the draft's compressed cache as a cache of its own: the SnapKV rows
+        # copied out once per prefill, then read by dense decodes
+        P = self.kv_t.page_size
+        self.pps = -(-w.budget // P)
+        self.k_c = torch.empty((B * self.pps, Hkv, P, d), dtype=torch.bfloat16, device=dev)
+        self.v_c = torch.empty_like(self.k_c)
+        self.table_c = torch.arange(B * self.pps, dtype=i32, device=dev).view(B, self.pps)
+        self.kvc = sd.KVCache(self.k_c, self.v_c, self.table_c, self.sel)
+        self.ws_dense = sd.workspace(sd.sd_verify_attn_workspace_size(B, 1, Hq, Hkv, d, w.budget), dev)
         self.sd = sd
 
     def step(self, ev=None):
@@ -499,6 +510,54 @@ def measure_snapkv_lse(wl, reps=10):
     return {"window_lse_ms": t_lse, "select_given_lse_ms": t_sel,
             "select_given_lse_K_GBps": k_bytes / (t_sel * 1e-3) / 1e9,
             "units_equal_to_one_call": same, "units": B * Hkv}
+
+
+def measure_compact(wl, reps=10):
+    """The draft over a compact copy of the SnapKV rows (sd_kv_compact once
+    per prefill, then dense decodes, sd_verify_attn with n_q = 1) beside the
+    step's gathered draft over the same selection in the full cache
+    (sd_draft_attn_sparse), with how far the two outputs lie apart at this
+    shape. The copy pays for itself after copy / (gathered - dense) draft
+    steps."""
+    import torch
+
+    sd, w = wl.sd, wl.w
+    Hq, Hkv, d, K = wl.Hq, wl.Hkv, wl.d, w.budget
+    sd.sd_snapkv_select(wl.kv, wl.q_obs, w.window, Hq, w.pool_kernel, K, wl.L, 1.0, wl.idx, wl.sel, wl.ws_snap)
+    q1 = wl.q_draft[0]
+    o_dense = torch.empty_like(q1)
+    o_gather = torch.empty_like(q1)
+
+    def compact():
+        sd.sd_kv_compact(wl.kv, wl.idx, wl.sel, Hkv, K, wl.pps, wl.k_c, wl.v_c)
+
+    def dense():
+        sd.sd_verify_attn(wl.kvc, q1, 1, Hq, K, 1.0, o_dense, None, wl.ws_dense)
+
+    def gather():
+        sd.sd_draft_attn_sparse(wl.kv, q1, 1, Hq, wl.idx, wl.sel, Hkv, K, 1.0, o_gather, None, wl.ws_draft)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_c, t_dense, t_gather = timed(compact), timed(dense), timed(gather)
+    rows = int(wl.sel.sum().item()) * Hkv
+    diff = float((o_dense.float() - o_gather.float()).abs().max().item())
+    return {"compact_once_per_prefill_ms": t_c,
+            "compact_GBps": 4 * rows * d * 2 / (t_c * 1e-3) / 1e9,
+            "dense_draft_ms": t_dense, "gathered_draft_ms": t_gather,
+            "dense_draft_kv_GBps": 2 * rows * d * 2 / (t_dense * 1e-3) / 1e9,
+            "dense_over_gathered": t_dense / t_gather,
+            "break_even_draft_steps": t_c / (t_gather - t_dense) if t_gather > t_dense else None,
+            "max_abs_diff_dense_vs_gathered": diff}
 
 
 def measure_topk(wl, reps=10):
@@ -863,6 +922,13 @@ def main():
             f"{snap2['select_given_lse_ms']:.3f} ms ({snap2['units_equal_to_one_call']} of {snap2['units']} "
             f"units as the one-call selection)")
 
+    compact = None
+    if not args.no_round:
+        compact = measure_compact(wl)
+        log(f"compact draft cache: copy {compact['compact_once_per_prefill_ms']:.3f} ms once, dense draft "
+            f"{compact['dense_draft_ms']:.3f} ms vs gathered {compact['gathered_draft_ms']:.3f} ms "
+            f"(outputs within {compact['max_abs_diff_dense_vs_gathered']:.1e})")
+
     model = None
     if not args.no_round:
         model = measure_model(wl, rnd, topk, float(wl.n_acc.float().mean().item()))
@@ -923,6 +989,7 @@ def main():
         "round": rnd,
         "per_sequence_budgets": het,
         "snapkv_two_calls": snap2,
+        "compact_draft_cache": compact,
         "dynamic_topk": topk,
         "speedup_model": model,
         "other_workloads": cfgs,

@@ -382,6 +382,35 @@ sd_status sd_kv_advance(int32_t *kv_lens, const int32_t *n_accepted, int32_t bat
                         void *stream);
 
 /*
+ * The draft's compressed cache as a cache of its own (MagicDec notes, §4.4
+ * and Appendix A.1: the draft reads a static compressed KV cache built once
+ * at prefill). Copies the K and V rows of each selection, in list order, into
+ * caller-owned pools, so that the draft steps become dense decodes
+ * (sd_verify_attn with n_q = 1) over contiguous pages instead of gathers.
+ * idx: int32 [batch, idx_heads, max_sel], idx_heads = 1 (one set for every KV
+ *   head) or num_kv_heads; sel_lens: int32 [batch] (entries past
+ *   min(sel_lens[b], max_sel) are not read); both device, as for
+ *   sd_draft_attn_sparse.
+ * k_out, v_out: [batch * pages_per_seq, num_kv_heads, page_size, head_dim] of
+ *   kv->dtype, 16-byte aligned, device. List entry t of sequence b and KV
+ *   head h goes to page b * pages_per_seq + t / page_size, head h, slot
+ *   t % page_size; slots past the selection are left as they were.
+ *   pages_per_seq >= ceil(max_sel / page_size) (more leaves room for tokens
+ *   appended later with sd_kv_append).
+ * The compact cache is then {k_out, v_out, page_table[b][j] =
+ *   b * pages_per_seq + j, kv_lens = the selection lengths, num_pages =
+ *   batch * pages_per_seq, max_pages = pages_per_seq, the source's page size,
+ *   heads, head_dim and dtype}; its dense decode equals the draft over the
+ *   selection up to the fp32 summation order.
+ * Errors: SD_ERR_INVALID_ARG for null or misaligned pointers, batch <= 0,
+ *   max_sel < 1, idx_heads not 1 or num_kv_heads, pages_per_seq too small;
+ *   SD_ERR_UNSUPPORTED when the compact pool would exceed the cache limits.
+ */
+sd_status sd_kv_compact(const sd_kv_cache *kv, const int32_t *idx, const int32_t *sel_lens,
+                        int32_t batch, int32_t idx_heads, int32_t max_sel, int32_t pages_per_seq,
+                        void *k_out, void *v_out, void *stream);
+
+/*
  * Analytic speedup model, host only (no GPU call; safe on any thread). The
  * MagicDec summary (jarxiv.com) gives the speedup of speculative decoding as
  * T_T * Omega(gamma, alpha) / (gamma * T_D + T_V(gamma)), where with a

@@ -35,6 +35,7 @@ from long_context_kv_split_amd.binding import (  # noqa: F401
     sd_kv_advance,
     sd_kv_append,
     sd_kv_cache,
+    sd_kv_compact,
     sd_snapkv_select,
     sd_snapkv_select_budgets,
     sd_snapkv_select_lse,

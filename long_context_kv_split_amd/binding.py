@@ -58,6 +58,7 @@ _SIGNATURES = {
     "sd_draft_attn_sparse_tail": (_I, [_KV, _P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _F, _P, _P, _P, _S, _P]),
     "sd_kv_append": (_I, [_KV, _P, _P, _I, _I, _P]),
     "sd_kv_advance": (_I, [_P, _P, _I, _I, _P]),
+    "sd_kv_compact": (_I, [_KV, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "sd_streaming_select": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "sd_snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]),
     "sd_snapkv_select_workspace_size": (_S, [_I, _I, _I, _I, _I]),
@@ -278,6 +279,17 @@ def sd_kv_advance(kv_lens, n_accepted, add, stream=None):
     lp = _dev(kv_lens, "kv_lens", torch.int32, B)
     np_ = _dev(n_accepted, "n_accepted", torch.int32, B, allow_none=True)
     _check(lib().sd_kv_advance(lp, np_, B, add, _stream(stream)), "sd_kv_advance")
+
+
+def sd_kv_compact(kv, idx, sel_lens, idx_heads, max_sel, pages_per_seq, k_out, v_out, stream=None):
+    B = kv.batch
+    n = B * pages_per_seq * kv.num_kv_heads * kv.struct.page_size * kv.head_dim
+    ip = _dev(idx, "idx", torch.int32, B * idx_heads * max_sel)
+    sp = _dev(sel_lens, "sel_lens", torch.int32, B)
+    kp = _dev(k_out, "k_out", kv.dtype, n)
+    vp = _dev(v_out, "v_out", kv.dtype, n)
+    _check(lib().sd_kv_compact(kv.ref, ip, sp, B, idx_heads, max_sel, pages_per_seq, kp, vp, _stream(stream)),
+           "sd_kv_compact")
 
 
 def sd_streaming_select(kv_lens, sink, recent, idx, sel_lens, stream=None):

@@ -12,4 +12,4 @@ extern "C" const char *sd_status_string(sd_status status) {
   return "SD_ERR_UNKNOWN";
 }
 
-extern "C" int32_t sd_version(void) { return 222; }
+extern "C" int32_t sd_version(void) { return 223; }

@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in _declared():
         assert hasattr(L, name), name
-    assert sd.version() == 222
+    assert sd.version() == 223
     for code in range(5):
         assert sd.status_string(code).startswith("SD_")
     assert "UNKNOWN" in sd.status_string(99)
@@ -338,6 +338,30 @@ def test_append_and_advance_reject_invalid_arguments(L):
     assert L.sd_kv_append(ctypes.byref(kv), FAKE, FAKE, 2, 0, None) == sd.SD_OK  # nothing to write
     assert L.sd_kv_advance(None, None, 2, 1, None) == sd.SD_ERR_INVALID_ARG
     assert L.sd_kv_advance(FAKE, None, 0, 1, None) == sd.SD_ERR_INVALID_ARG
+
+
+@no_gpu
+@pytest.mark.parametrize("over,args,want", [
+    ({}, dict(idx=None), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(sel_lens=None), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(k_out=None), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(v_out=ctypes.c_void_p(0x7004)), sd.SD_ERR_INVALID_ARG),   # not 16-byte aligned
+    ({"v_pages": None}, {}, sd.SD_ERR_INVALID_ARG),
+    ({}, dict(batch=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(max_sel=0), sd.SD_ERR_INVALID_ARG),
+    ({}, dict(idx_heads=3), sd.SD_ERR_INVALID_ARG),        # neither 1 nor num_kv_heads
+    ({}, dict(max_sel=33, pps=2), sd.SD_ERR_INVALID_ARG),  # 33 entries need 3 pages of 16
+    ({}, dict(pps=1 << 26), sd.SD_ERR_UNSUPPORTED),        # 2^32 compact rows
+    ({"head_dim": 96}, {}, sd.SD_ERR_UNSUPPORTED),
+])
+def test_kv_compact_rejects_invalid_arguments(L, over, args, want):
+    kv = _kv(**over)
+    a = dict(idx=FAKE, sel_lens=FAKE, batch=2, idx_heads=1, max_sel=32, pps=2, k_out=ctypes.c_void_p(0x7000),
+             v_out=ctypes.c_void_p(0x8000))
+    a.update(args)
+    st = L.sd_kv_compact(ctypes.byref(kv), a["idx"], a["sel_lens"], a["batch"], a["idx_heads"], a["max_sel"],
+                         a["pps"], a["k_out"], a["v_out"], None)
+    assert st == want
 
 
 @no_gpu

@@ -72,6 +72,96 @@ def test_kv_advance_exact():
     assert lens.cpu().tolist() == list(want) == [9, 2, 1, 1, 1]  # the last one clamps at 0 first
 
 
+def _selection(seed, lens, heads, max_sel):
+    """Random selections (sorted, or reversed for odd heads) of up to max_sel
+    positions per sequence; sequence 1 selects nothing."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((len(lens), heads, max_sel), -1, dtype=np.int32)
+    sel = np.zeros(len(lens), dtype=np.int32)
+    for b, L in enumerate(lens):
+        n = 0 if b == 1 else int(min(L, rng.integers(1, max_sel + 1)))
+        sel[b] = n
+        for g in range(heads):
+            pos = np.sort(rng.choice(L, size=n, replace=False))
+            idx[b, g, :n] = pos[::-1] if g % 2 else pos
+    return torch.tensor(idx).cuda(), torch.tensor(sel).cuda()
+
+
+@pytest.mark.parametrize("dtype,d,P,kind,extra", [
+    (BF16, 128, 16, "shared", 0), (BF16, 128, 16, "per-head", 1), (torch.float32, 64, 32, "per-head", 0),
+    (BF16, 64, 32, "shared", 2)])
+def test_kv_compact_bit_exact_and_its_decode_is_the_draft(dtype, d, P, kind, extra):
+    """The compact copy of a selection holds exactly the selected rows in list
+    order (bit-exact against the oracle, untouched slots and the page past the
+    pool keep their NaN), and a dense decode over it (verify with n_q = 1)
+    equals the sparse draft over the original cache."""
+    lens = [900, 40, 1300, 17, 600]
+    B, Hkv, Hq, max_sel = len(lens), 2, 8, 300
+    say(f"kv_compact {dtype} d={d} P={P} {kind} extra={extra}")
+    kv_t = paged_kv(31 + d + P, lens, Hkv, d, dtype, "cuda", shuffle=True, page_size=P)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    heads = Hkv if kind == "per-head" else 1
+    idx, sel = _selection(d + P, lens, heads, max_sel)
+    pps = -(-max_sel // P) + extra
+    k_out = torch.full((B * pps + 1, Hkv, P, d), float("nan"), dtype=dtype, device="cuda")
+    v_out = torch.full_like(k_out, float("nan"))
+    sd.sd_kv_compact(kv, idx, sel, heads, max_sel, pps, k_out, v_out)
+    torch.cuda.synchronize()
+    Kc, Vc = oracle.kv_compact(kv_t.k_pages.cpu(), kv_t.v_pages.cpu(), kv_t.page_table.cpu(), idx.cpu(),
+                               sel.cpu(), pps)
+    assert _bits_equal(k_out[:-1], Kc) and _bits_equal(v_out[:-1], Vc)
+    assert torch.isnan(k_out[-1].float()).all() and torch.isnan(v_out[-1].float()).all()
+
+    table = torch.arange(B * pps, dtype=torch.int32, device="cuda").view(B, pps)
+    kvc = sd.KVCache(k_out, v_out, table, sel)
+    q = queries(77, 1, (B, 1, Hq, d), dtype, "cuda", scale=d ** -0.5)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, Hq, Hkv, d, max_sel), "cuda")
+    sd.sd_verify_attn(kvc, q, 1, Hq, max_sel, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, idx, sel, 1.0)
+    err = compare_attn(out, lse, o_ref, l_ref, dtype)
+    say(f"  compact decode vs draft: max|dO|={err[0]:.3e} norm={err[1]:.3e} lse={err[2]:.3e}")
+
+
+def test_compact_cache_takes_appended_tokens_like_the_tail_draft():
+    """New tokens appended to both the full cache and the compact copy (its
+    spare pages): a dense decode over the compact copy is then the draft over
+    selection + tail, as the oracle computes it on the full cache."""
+    lens0, n_new, max_sel = [700, 260, 333], 3, 96
+    B, Hkv, Hq, d, P = len(lens0), 2, 8, 128, 16
+    say(f"compact + append: lens={lens0} n_new={n_new}")
+    kv_t = paged_kv(85, [L + n_new for L in lens0], Hkv, d, BF16, "cuda", shuffle=True)
+    lens_d = torch.tensor(lens0, dtype=torch.int32, device="cuda")
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, lens_d)
+    idx, sel = _selection(85, lens0, Hkv, max_sel)
+    pps = -(-(max_sel + n_new) // P)
+    k_c = torch.full((B * pps, Hkv, P, d), float("nan"), dtype=BF16, device="cuda")
+    v_c = torch.full_like(k_c, float("nan"))
+    sd.sd_kv_compact(kv, idx, sel, Hkv, max_sel, pps, k_c, v_c)
+    lens_c = sel.clone()
+    kvc = sd.KVCache(k_c, v_c, torch.arange(B * pps, dtype=torch.int32, device="cuda").view(B, pps), lens_c)
+    g = torch.Generator(device="cuda").manual_seed(85)
+    k_new = torch.randn((B, n_new, Hkv, d), generator=g, device="cuda").to(BF16)
+    v_new = torch.randn((B, n_new, Hkv, d), generator=g, device="cuda").to(BF16)
+    sd.sd_kv_append(kv, k_new, v_new, n_new)
+    sd.sd_kv_append(kvc, k_new, v_new, n_new)
+    sd.sd_kv_advance(lens_d, None, n_new)
+    sd.sd_kv_advance(lens_c, None, n_new)
+    q = queries(85, 1, (B, 1, Hq, d), BF16, "cuda", scale=d ** -0.5)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    ws = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, Hq, Hkv, d, pps * P), "cuda")
+    sd.sd_verify_attn(kvc, q, 1, Hq, pps * P, 1.0, out, lse, ws)
+    torch.cuda.synchronize()
+    lens1 = [L + n_new for L in lens0]
+    o_ref, l_ref = oracle.sparse_attn_tail(q.cpu(), kv_t.k_pages.cpu(), kv_t.v_pages.cpu(), kv_t.page_table.cpu(),
+                                           idx.cpu().numpy(), sel.cpu().numpy(), lens0, lens1, 1.0)
+    err = compare_attn(out, lse, o_ref, l_ref, BF16)
+    say(f"  max|dO|={err[0]:.2e} norm={err[1]:.2e} lse={err[2]:.2e}")
+
+
 TAIL_CASES = [
     # name, lens, tail_begin, sel width, idx_heads, n_q
     ("streaming+tail", [500, 300], [480, 290], 64, 1, 1),
