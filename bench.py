@@ -37,6 +37,7 @@ vocabulary, warm and cold (last-level cache evicted before each call).
 python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-round]
 python bench.py --copy-probe     # plain 4 GiB device copy, for counter scaling
 python bench.py --configs-only --steps 5   # only the other workloads (profiling)
+python bench.py --compact-only --steps 5   # only the compact draft cache block (profiling)
 """
 import argparse
 import json
@@ -68,6 +69,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--configs-only", action="store_true",
                     help="time only the other workloads (for their kernel traces and counters)")
+    ap.add_argument("--compact-only", action="store_true",
+                    help="time only the compact draft cache block (for its kernel trace and counters)")
     ap.add_argument("--no-round", action="store_true",
                     help="skip the round and per-sequence-budget measurements")
     return ap.parse_args()
@@ -375,7 +378,8 @@ def measure_round(wl, reps=10):
     sample the next draft token], then append, advance, verify (n_q = gamma + 1
     over L), accept, roll back. The appended K/V are the rows the cache already
     holds at L0 .. L - 1, so the cache is the same after every round. Also
-    times dense decode (n_q = 1 over L) as the attention-only target step T_T."""
+    times, back to back, dense decode (n_q = 1 over L) as the attention-only
+    target step T_T, verify, the draft and the draft with its tail."""
     import torch
 
     sd, w = wl.sd, wl.w
@@ -459,10 +463,25 @@ def measure_round(wl, reps=10):
         sd.sd_draft_attn_sparse(wl.kv, wl.q_draft[0], 1, Hq, wl.idx, wl.sel, Hkv, w.budget, 1.0, wl.o_draft[0],
                                 None, wl.ws_draft)
 
-    decode()
-    t_dec, t_ver, t_dr = timed(decode), timed(verify), timed(draft)
+    def draft_tail():
+        # the selection made at L0 plus the gamma + 1 positions after it
+        sd.sd_draft_attn_sparse_tail(wl.kv, wl.q_draft[0], 1, Hq, wl.idx, wl.sel, Hkv, w.budget, tail_begin,
+                                     g + 1, 1.0, wl.o_draft[0], None, wl.ws_draft)
+
+    def back_to_back(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_dec, t_ver, t_dr, t_tail = (back_to_back(f) for f in (decode, verify, draft, draft_tail))
     return {"L0": L0, "eager_ms": eager_ms, "graph_ms": graph_ms, "mean_accepted": mean_acc,
-            "decode_ms": t_dec, "verify_ms": t_ver, "draft_ms": t_dr,
+            "decode_ms": t_dec, "verify_ms": t_ver, "draft_ms": t_dr, "draft_tail_ms": t_tail,
             "verify_over_decode": t_ver / t_dec, "draft_over_decode": t_dr / t_dec,
             "budget_over_context": w.budget / wl.L}
 
@@ -833,6 +852,14 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.compact_only:
+        from __graft_entry__ import _ensure_built
+
+        _ensure_built()
+        torch.cuda.set_device(0)
+        wl = Workload("cuda:0")
+        print(json.dumps({"compact_draft_cache": measure_compact(wl, reps=args.steps)}), flush=True)
         return
     if args.configs_only:
         from __graft_entry__ import _ensure_built

@@ -40,31 +40,34 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
   reinterpret_cast<u32x4 *>(v_pages)[dst] = reinterpret_cast<const u32x4 *>(v_new)[c];
 }
 
-// One thread per 16-byte chunk of a compact-cache row: (sequence b, list
-// entry t, KV head h, chunk) with the chunk fastest, so a row's chunks are
-// consecutive threads. Entries past the sequence's selection are not written;
-// positions, page ids and lengths are clamped into range.
+// One thread per 16-byte chunk of a compact-cache row, ordered as the output
+// is laid out: (sequence b, output page j, KV head h, slot, chunk) with the
+// chunk fastest, so a workgroup writes whole 4 KB (page, head) blocks and
+// only the reads are gathered. List entry t = j P + slot; entries past the
+// sequence's selection are not written; positions, page ids and lengths are
+// clamped into range.
 __global__ __launch_bounds__(kAppendThreads) void kv_compact_kernel(
     char *k_out, char *v_out, const char *k_pages, const char *v_pages, const int32_t *page_table,
     const int32_t *idx, const int32_t *sel_lens, int64_t n_chunks, int32_t max_sel, int32_t idx_heads,
-    int32_t pages_per_seq, int32_t Hkv, int32_t row_chunks, int32_t page_size, int32_t max_pages,
-    int32_t num_pages) {
+    int32_t pages_per_seq, int32_t used_pages, int32_t Hkv, int32_t row_chunks, int32_t page_size,
+    int32_t max_pages, int32_t num_pages) {
   const int64_t c = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
   if (c >= n_chunks) return;
   const int ch = (int)(c % row_chunks);
   const int64_t row = c / row_chunks;
-  const int h = (int)(row % Hkv);
-  const int64_t bt = row / Hkv;
-  const int t = (int)(bt % max_sel);
-  const int b = (int)(bt / max_sel);
+  const int slot = (int)(row % page_size);
+  const int64_t ph = row / page_size;
+  const int h = (int)(ph % Hkv);
+  const int64_t bj = ph / Hkv;
+  const int j = (int)(bj % used_pages);
+  const int b = (int)(bj / used_pages);
+  const int t = j * page_size + slot;
   if (t >= clampi(sel_lens[b], 0, max_sel)) return;
   const int pos = clampi(idx[((size_t)b * idx_heads + (idx_heads > 1 ? h : 0)) * max_sel + t], 0,
                          max_pages * page_size - 1);
   const int page = clampi(page_table[(size_t)b * max_pages + pos / page_size], 0, num_pages - 1);
   const int64_t src = ((int64_t)(page * Hkv + h) * page_size + pos % page_size) * row_chunks + ch;
-  const int64_t dst =
-      (((int64_t)b * pages_per_seq + t / page_size) * Hkv + h) * page_size * row_chunks +
-      (int64_t)(t % page_size) * row_chunks + ch;
+  const int64_t dst = ((((int64_t)b * pages_per_seq + j) * Hkv + h) * page_size + slot) * row_chunks + ch;
   const u32x4 kv_k = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k_pages) + src);
   const u32x4 kv_v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v_pages) + src);
   reinterpret_cast<u32x4 *>(k_out)[dst] = kv_k;
@@ -124,12 +127,13 @@ extern "C" sd_status sd_kv_compact(const sd_kv_cache *kv, const int32_t *idx, co
   SD_REQUIRE((int64_t)batch * pages_per_seq * kv->num_kv_heads * kv->page_size < ((int64_t)1 << 31),
              SD_ERR_UNSUPPORTED);
   const int row_chunks = kv->head_dim * sdh::dtype_bytes(kv->dtype) / 16;
-  const int64_t n_chunks = (int64_t)batch * max_sel * kv->num_kv_heads * row_chunks;
+  const int used_pages = sdh::ceil_div(max_sel, kv->page_size);  // output pages a selection can fill
+  const int64_t n_chunks = (int64_t)batch * used_pages * kv->num_kv_heads * kv->page_size * row_chunks;
   SD_REQUIRE(n_chunks / kAppendThreads < ((int64_t)1 << 31), SD_ERR_UNSUPPORTED);
   kv_compact_kernel<<<(unsigned)((n_chunks + kAppendThreads - 1) / kAppendThreads), kAppendThreads, 0,
                       sdh::as_stream(stream)>>>(
       reinterpret_cast<char *>(k_out), reinterpret_cast<char *>(v_out), reinterpret_cast<const char *>(kv->k_pages),
       reinterpret_cast<const char *>(kv->v_pages), kv->page_table, idx, sel_lens, n_chunks, max_sel, idx_heads,
-      pages_per_seq, kv->num_kv_heads, row_chunks, kv->page_size, kv->max_pages, kv->num_pages);
+      pages_per_seq, used_pages, kv->num_kv_heads, row_chunks, kv->page_size, kv->max_pages, kv->num_pages);
   return sdh::launch_status();
 }
