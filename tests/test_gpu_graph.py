@@ -64,13 +64,23 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
     ws_v = sd.workspace(sd.sd_verify_attn_workspace_size(B, gamma + 1, Hq, Hkv, d, L))
     ws_a = sd.workspace(sd.sd_spec_accept_workspace_size(B, gamma, V))
     ws_s2 = sd.workspace(sd.sd_snapkv_select_workspace_size(B, W, Hq, Hkv, L))
-    outs = (idx, sel, o_d, o_v, lse_v, n_acc, toks, obs_lse, idx2, sel2)
+    # the selection copied into a cache of its own and a dense decode over it;
+    # slots past the selections stay NaN in the eager run and every replay
+    pps = budget // 16
+    k_c = torch.full((B * pps, Hkv, 16, d), float("nan"), dtype=BF16, device="cuda")
+    v_c = torch.full_like(k_c, float("nan"))
+    kvc = sd.KVCache(k_c, v_c, torch.arange(B * pps, dtype=torch.int32, device="cuda").view(B, pps), sel)
+    o_c = torch.empty_like(q_d)
+    ws_c = sd.workspace(sd.sd_verify_attn_workspace_size(B, 1, Hq, Hkv, d, budget))
+    outs = (idx, sel, o_d, o_v, lse_v, n_acc, toks, obs_lse, idx2, sel2, k_c, v_c, o_c)
 
     def calls():
         sd.sd_snapkv_select(kv, q_obs, W, Hq, 7, budget, L, 1.0, idx, sel, ws_s)
         sd.sd_snapkv_window_lse(kv, q_obs, W, Hq, L, 1.0, obs_lse, ws_s2)
         sd.sd_snapkv_select_lse(kv, q_obs, obs_lse, W, Hq, 7, budget, L, 1.0, idx2, sel2, ws_s2)
         sd.sd_draft_attn_sparse(kv, q_d, 1, Hq, idx, sel, Hkv, budget, 1.0, o_d, None, ws_d)
+        sd.sd_kv_compact(kv, idx, sel, Hkv, budget, pps, k_c, v_c)
+        sd.sd_verify_attn(kvc, q_d, 1, Hq, budget, 1.0, o_c, None, ws_c)
         sd.sd_verify_attn(kv, q_v, gamma + 1, Hq, L, 1.0, o_v, lse_v, ws_v)
         sd.sd_spec_accept(zt, zd, x, ua, us, gamma, V, 1.0, n_acc, toks, ws_a)
 
@@ -92,7 +102,7 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
         # and run the library eagerly on other inputs through the same workspaces
         for t in outs:
             t.fill_(-5 if not t.is_floating_point() else float("nan"))
-        for w in (ws_s, ws_s2, ws_d, ws_v, ws_a):
+        for w in (ws_s, ws_s2, ws_d, ws_v, ws_a, ws_c):
             w.fill_(0xA5)
         if rep % 2 == 1:
             sd.sd_verify_attn(kv, q_v.flip(0).contiguous(), gamma + 1, Hq, L, 1.0, o_v, lse_v, ws_v)
@@ -102,5 +112,6 @@ def test_select_draft_verify_accept_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         for name, got, ref in zip(("idx", "sel_lens", "draft_out", "verify_out", "verify_lse", "n_accepted",
-                                   "out_tokens", "window_lse", "idx_from_lse", "sel_lens_from_lse"), outs, want):
+                                   "out_tokens", "window_lse", "idx_from_lse", "sel_lens_from_lse",
+                                   "compact_k", "compact_v", "draft_over_compact"), outs, want):
             assert _same(got, ref), f"replay {rep}: {name} differs from the eager run"

@@ -142,6 +142,35 @@ def test_snapkv_two_calls_write_only_their_outputs():
     check(idx=idx, sel_lens=sel, lse=lse, workspace=ws)
 
 
+@pytest.mark.parametrize("kind,extra", [("shared", 0), ("per-head", 1)])
+def test_kv_compact_writes_only_its_pools(kind, extra):
+    """The copy of the selections (ragged, one sequence at or under its
+    budget) writes inside its two pools and leaves the source cache as it
+    was."""
+    say(f"guards kv_compact {kind} extra={extra}")
+    d, Hkv, max_sel, P = 128, 2, 96, 16
+    kv_t = cache(torch.bfloat16, d, Hkv)
+    kv = sd.KVCache(kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens)
+    B = len(LENS)
+    heads = Hkv if kind == "per-head" else 1
+    rng = np.random.default_rng(5)
+    idx_np = np.full((B, heads, max_sel), -1, dtype=np.int32)
+    sel_np = np.array([min(L, max_sel) for L in LENS], dtype=np.int32)
+    for b, L in enumerate(LENS):
+        for g in range(heads):
+            idx_np[b, g, :sel_np[b]] = rng.choice(L, sel_np[b], replace=False)
+    idx = torch.tensor(idx_np, device="cuda")
+    sel = torch.tensor(sel_np, device="cuda")
+    pps = max_sel // P + extra
+    k_out = Guarded((B * pps, Hkv, P, d), torch.bfloat16)
+    v_out = Guarded((B * pps, Hkv, P, d), torch.bfloat16)
+    k_src, v_src = kv_t.k_pages.clone(), kv_t.v_pages.clone()
+    sd.sd_kv_compact(kv, idx, sel, heads, max_sel, pps, k_out.t, v_out.t)
+    check(k_out=k_out, v_out=v_out)
+    assert torch.equal(k_src.view(torch.int16), kv_t.k_pages.view(torch.int16))
+    assert torch.equal(v_src.view(torch.int16), kv_t.v_pages.view(torch.int16))
+
+
 def test_topk_selection_and_per_head_draft_write_only_their_outputs():
     say("guards top-K")
     d, Hq, Hkv, budget = 128, 8, 2, 64
