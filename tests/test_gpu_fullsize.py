@@ -317,6 +317,30 @@ def test_snapkv_select_and_draft_full_size_sampled():
     # unit in a hundred is expected at this shape
     assert len(units) >= 64 and near <= 3, stats
 
+    # the same selection copied into a cache of its own: every row of every
+    # unit equals the source row the selection names (a gather by torch
+    # indexing), and the dense decode over the copy is the draft
+    P = kv_t.page_size
+    pps = w.budget // P
+    k_c = torch.full((B * pps, Hkv, P, d), float("nan"), dtype=BF16, device="cuda")
+    v_c = torch.full_like(k_c, float("nan"))
+    sd.sd_kv_compact(kv, idx, sel, Hkv, w.budget, pps, k_c, v_c)
+    pos = idx.long()                                                   # [B, Hkv, budget]
+    pages = torch.gather(kv_t.page_table.long(), 1, (pos // P).view(B, -1)).view(B, Hkv, w.budget)
+    heads_i = torch.arange(Hkv, device="cuda").view(1, Hkv, 1)
+    for pool, copy in ((kv_t.k_pages, k_c), (kv_t.v_pages, v_c)):
+        want = pool[pages, heads_i, pos % P]                           # [B, Hkv, budget, d]
+        got = copy.view(B, pps, Hkv, P, d).permute(0, 2, 1, 3, 4).reshape(B, Hkv, w.budget, d)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    kvc = sd.KVCache(k_c, v_c, torch.arange(B * pps, dtype=torch.int32, device="cuda").view(B, pps), sel)
+    out_c = torch.full_like(qd, float("nan"))
+    lse_c = torch.full_like(lse, float("nan"))
+    wsc = dirty_workspace(sd.sd_verify_attn_workspace_size(B, 1, w.num_q_heads, Hkv, d, w.budget), "cuda")
+    sd.sd_verify_attn(kvc, qd, 1, w.num_q_heads, w.budget, 1.0, out_c, lse_c, wsc)
+    torch.cuda.synchronize()
+    check_draft_against_gathered("snapkv draft as a dense decode over the compact copy (every unit)",
+                                 out_c, lse_c, kv_t, idx, sel, qd, w.num_q_heads)
+
 
 def test_snapkv_two_calls_full_size():
     """B=128, 32k context: sd_snapkv_window_lse on sampled units against the
