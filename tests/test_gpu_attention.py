@@ -80,6 +80,67 @@ def test_verify_softmax_scale_argument():
     compare_attn(out, lse, o_ref, l_ref, BF16)
 
 
+SHARP_CASES = [
+    # name, dtype, softmax_scale, ramp (score added linearly from 0 at position 0)
+    ("sharp-bf16", BF16, 8.0, 0.0),
+    ("sharp-f32", F32, 8.0, 0.0),
+    ("rising-bf16", BF16, 1.0, 80.0),
+    ("falling-bf16", BF16, 1.0, -80.0),
+    ("rising-f32", F32, 1.0, 80.0),
+]
+
+
+@pytest.mark.parametrize("case", SHARP_CASES, ids=[c[0] for c in SHARP_CASES])
+def test_attention_with_sharp_or_trending_scores(case):
+    """Peaked softmax (scale 8 on unit-variance scores) and scores that rise or
+    fall by 80 over each sequence: every query row has a component along one
+    direction u that the keys carry with a weight growing in the position, so
+    the running maximum moves at nearly every step (rising) or is set by the
+    first one (falling). Verify (one sequence long enough for the permuted
+    walk) and the draft over every position, in ascending and in descending
+    order, against the oracle."""
+    name, dtype, scale, ramp = case
+    lens = [5000, 700]
+    B, Hkv, Hq, d, n_q = len(lens), 2, 8, 128, 4
+    say(f"sharp/trending scores {name}")
+    kv_t = paged_kv(71, lens, Hkv, d, dtype, "cuda", shuffle=True)
+    g = torch.Generator(device="cuda").manual_seed(71)
+    u = torch.randn(d, generator=g, device="cuda")
+    u /= u.norm()
+    P = kv_t.page_size
+    for b, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        page = kv_t.page_table[b].long()[t // P]
+        for pool in (kv_t.k_pages,):
+            rows = pool[page, :, t % P, :].float() + (ramp * t / L)[:, None, None] * u
+            pool[page, :, t % P, :] = rows.to(dtype)
+    q = (queries(71, 1, (B, n_q, Hq, d), torch.float32, "cuda", scale=d ** -0.5) + u).to(dtype)
+    # largest |score| of each (sequence, query row, head) over the sequence's keys
+    mag = np.zeros((B, n_q, Hq))
+    for b, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        k = kv_t.k_pages[kv_t.page_table[b].long()[t // P], :, t % P, :].float()      # [L, Hkv, d]
+        k = k.repeat_interleave(Hq // Hkv, dim=1)                                    # [L, Hq, d]
+        s_ = torch.matmul(q[b].float().permute(1, 0, 2).contiguous(), k.permute(1, 2, 0).contiguous()) * scale
+        mag[b] = s_.abs().amax(dim=2).permute(1, 0).cpu().numpy()                   # [n_q, Hq]
+    out, lse = run_verify(kv_t, q, n_q, Hq, scale=scale)
+    o_ref, l_ref = oracle.verify_attn(q, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, kv_t.kv_lens, scale)
+    err = compare_attn(out, lse, o_ref, l_ref, dtype, score_mag=mag)
+    say(f"  verify max|dO|={err[0]:.2e} norm={err[1]:.2e} lse/factor={err[2]:.2e}, "
+        f"|s|max up to {mag.max():.1f}")
+    qd = q[:, :1].contiguous()
+    for order in ("ascending", "descending"):
+        idx_np = np.full((B, 1, max(lens)), -1, dtype=np.int32)
+        for b, L in enumerate(lens):
+            idx_np[b, 0, :L] = np.arange(L) if order == "ascending" else np.arange(L)[::-1]
+        idx = torch.tensor(idx_np).cuda()
+        sel = torch.tensor(lens, dtype=torch.int32).cuda()
+        out_d, lse_d = run_draft(kv_t, qd, 1, Hq, idx, sel, scale=scale)
+        o_ref, l_ref = oracle.sparse_attn(qd, kv_t.k_pages, kv_t.v_pages, kv_t.page_table, idx, sel, scale)
+        err = compare_attn(out_d, lse_d, o_ref, l_ref, dtype, score_mag=mag[:, :1])
+        say(f"  draft {order}: max|dO|={err[0]:.2e} norm={err[1]:.2e} lse={err[2]:.2e}")
+
+
 def test_verify_is_deterministic():
     lens = [2000, 1700, 900]
     kv_t = paged_kv(6, lens, 2, 128, BF16, "cuda", shuffle=True)
