@@ -304,7 +304,11 @@ size_t sd_topk_select_workspace_size(int32_t batch, int32_t num_q_heads, int32_t
  * n_accepted: int32 [batch]; out_tokens: int32 [batch, gamma+1] =
  *   [x_0 .. x_{n-1}, y, -1 ...].
  * Softmax exponentials are float32; normalisers and cumulative sums are
- *   accumulated in float64.
+ *   accumulated in float64. The residual weights are formed as
+ *   p (1 - q/p) from the logit difference and the difference of the two
+ *   normalisers (itself from a float64 sum of p-weighted expm1 of the logit
+ *   differences), so they keep float32's relative accuracy when q is close
+ *   to p.
  * Limits: gamma >= 0, vocab >= 1, 0 < temperature < inf, null pointers
  *   (draft_* and u_accept may be null only when gamma = 0): else
  *   SD_ERR_INVALID_ARG; gamma <= 64, vocab < 2^30,
@@ -336,7 +340,7 @@ size_t sd_spec_accept_workspace_size(int32_t batch, int32_t gamma, int32_t vocab
  * stream must belong to the current device (else SD_ERR_INVALID_ARG).
  * Limits: as sd_spec_accept, and sd_spec_accept_workspace_size(batch, gamma,
  *   vocab) <= SD_SPEC_ACCEPT_SCRATCH_BYTES, else SD_ERR_UNSUPPORTED (about
- *   960 sequences at gamma = 4 over a 128256-token vocabulary).
+ *   864 sequences at gamma = 4 over a 128256-token vocabulary).
  */
 #define SD_SPEC_ACCEPT_SCRATCH_BYTES (4u << 20)
 

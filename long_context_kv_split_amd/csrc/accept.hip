@@ -7,18 +7,23 @@
 //
 // Three kernels; the logits are streamed once, plus the one or two rows the
 // draw needs:
-//   accept_stats:    one block per (row, vocab chunk) of the 2*gamma+1 rows of
-//                    every sequence: chunk max of z/t and the sum of exp(z/t -
-//                    max) (fp32 exponentials, fp64 sums; each thread keeps its
-//                    own running max, merged once at the end);
+//   accept_stats:    one block per (draft position, vocab chunk) of every
+//                    sequence, reading the chunk of p_i and of q_i together
+//                    (p_gamma alone): per row the chunk max of z/t and the sum
+//                    of exp(z/t - max) (fp32 exponentials, fp64 sums), and for
+//                    the pair the sum of p weights times expm1((zq - zp)/t),
+//                    from which the difference of the two normalisers comes out
+//                    to full relative accuracy when q is close to p;
 //   accept_residual: one block per (sequence, slice of the vocabulary): the
 //                    block merges the sequence's chunk statistics into row
 //                    log-normalisers (fp64), evaluates u_i q_i(x_i) < p_i(x_i)
-//                    for every draft (fp64; n = the first failure), and sums
+//                    for every draft (fp64; n = the first failure), forms the
+//                    drawn pair's normaliser gap from the cross sums, and sums
 //                    the weights of the drawn row pair over its slice, per
-//                    1024-entry piece, in fp64: max(0, p_n - q_n) and p_n, or
-//                    p_gamma. Several blocks per sequence spread the drawn row
-//                    over the CUs (one CU streams a row at a few tens of GB/s);
+//                    1024-entry piece, in fp64: max(0, p_n - q_n) (as
+//                    p (1 - q/p)) and p_n, or p_gamma. Several blocks per
+//                    sequence spread the drawn row over the CUs (one CU
+//                    streams a row at a few tens of GB/s);
 //   accept_draw:     one block per sequence scans the piece sums in vocabulary
 //                    order for the piece holding u*Z and rescans that piece for
 //                    the token.
@@ -45,8 +50,9 @@ struct AccParams {
   int32_t *n_accepted;
   int32_t *out_tokens;
   double *stats;      // [B, 2*gamma+1, n_chunks, 2]  (max, sum)
+  double *cross;      // [B, gamma, n_chunks]: sum of p_i weights (relative to the chunk max) x expm1(d)
   double *pieces;     // [B, 2, npieces]: weight sums per piece, residual (0) and p_n (1)
-  double *seq_lse;    // [B, 2]: normalisers of the drawn pair (p_n, q_n)
+  double *seq_lse;    // [B, 2]: the drawn row's normaliser lse_p and lse_q - lse_p (residual draws)
   int32_t *seq_n;     // [B]: accepted drafts
   int32_t B, gamma, V, n_chunks;
   int32_t npieces, pps;  // pieces per row, pieces per residual slice
@@ -60,87 +66,196 @@ __device__ __forceinline__ const float *row_ptr(const AccParams &a, int b, int k
   return a.zd + ((size_t)b * a.gamma + (k - a.gamma - 1)) * a.V;
 }
 
-// Merge (m, s) pairs: s is relative to m; m = -inf means empty.
-__device__ __forceinline__ void merge_ms(float &m, double &s, float m2, double s2) {
-  const float M = fmaxf(m, m2);
-  if (M == kNegInf) return;
-  s = (m == kNegInf ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - M) * kLog2e)) +
-      (m2 == kNegInf ? 0.0 : s2 * (double)__builtin_amdgcn_exp2f((m2 - M) * kLog2e));
-  m = M;
+// expm1(d) for |d| < 1/8: its Taylor series to degree 5 (relative error
+// below 5e-8, under fp32's own rounding).
+__device__ __forceinline__ float expm1_small(float d) {
+  return d * fmaf(d, fmaf(d, fmaf(d, fmaf(d, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
 }
 
-// VEC = 4: 16-byte loads (rows 16-byte aligned, V a multiple of 4), else
-// 4-byte loads. Addresses past the row are clamped onto its last entries and
-// the values masked, so every load is issued unconditionally and all of a
-// thread's loads are in flight together.
+// Raw logits of one row's chunk (entries past the row clamped onto its last
+// ones; the caller masks them).
 template <int VEC>
-__device__ __forceinline__ void load_chunk(const float *z, int t0, int V, float inv_temp,
-                                           float (&x)[kPerThread]) {
+__device__ __forceinline__ void load_raw(const float *z, int t0, int V, float (&v)[kPerThread]) {
   if constexpr (VEC == 4) {
-    f32x4 v[kPerThread / 4];
+    f32x4 w[kPerThread / 4];
 #pragma unroll
     for (int e = 0; e < kPerThread / 4; ++e) {
       const int t = t0 + (e * kAccThreads + (int)threadIdx.x) * 4;
-      v[e] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + min(t, V - 4)));
+      w[e] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z + min(t, V - 4)));
     }
 #pragma unroll
-    for (int e = 0; e < kPerThread / 4; ++e) {
-      const int t = t0 + (e * kAccThreads + (int)threadIdx.x) * 4;
+    for (int e = 0; e < kPerThread / 4; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[4 * e + j] = t + j < V ? v[e][j] * inv_temp : kNegInf;
-    }
+      for (int j = 0; j < 4; ++j) v[4 * e + j] = w[e][j];
   } else {
-    float v[kPerThread];
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) v[e] = z[min(t0 + e * kAccThreads + (int)threadIdx.x, V - 1)];
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int t = t0 + e * kAccThreads + (int)threadIdx.x;
-      x[e] = t < V ? v[e] * inv_temp : kNegInf;
-    }
   }
 }
 
-// One block per (row, chunk): the chunk's max of z/t (exact, float), then the
-// sum of exp(z/t - wave max) per wave (fp32 exponentials, fp64 sums), the
-// waves' (max, sum) pairs merged once by thread 0.
-template <int VEC>
-__global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) {
-  __shared__ float lds_m[kAccThreads / 64];
-  __shared__ double lds_s[kAccThreads / 64];
-  const int c = blockIdx.x;
-  const int rowid = blockIdx.y;  // b * (2*gamma+1) + k
-  const int nrow = 2 * a.gamma + 1;
-  const int b = rowid / nrow, k = rowid % nrow;
-  const float *z = row_ptr(a, b, k);
-  float x[kPerThread];
-  load_chunk<VEC>(z, c * kChunk, a.V, a.inv_temp, x);
-  float m = kNegInf;
+// Wave max of x, then the wave's sum of exp(x - max) (fp64 over pairs summed
+// in fp32); m = -inf for a wave with no entry.
+__device__ __forceinline__ void wave_max_sum(const float (&x)[kPerThread], float &m, double &s) {
+  m = kNegInf;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) m = fmaxf(m, x[e]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  double s = 0.0;
+  s = 0.0;
   if (m != kNegInf) {
-    double s4[4] = {0.0, 0.0, 0.0, 0.0};  // four independent fp64 chains
+    double s2[2] = {0.0, 0.0};  // pairs of weights summed in fp32, then in fp64
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) s4[e & 3] += (double)__builtin_amdgcn_exp2f((x[e] - m) * kLog2e);
-    s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    for (int e = 0; e < kPerThread; e += 2)
+      s2[(e >> 1) & 1] += (double)(__builtin_amdgcn_exp2f((x[e] - m) * kLog2e) +
+                                   __builtin_amdgcn_exp2f((x[e + 1] - m) * kLog2e));
+    s = s2[0] + s2[1];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+}
+
+// One block per (sequence, draft position i, chunk): rows p_i and q_i of the
+// chunk (i < gamma), or p_gamma alone. Per row the chunk's max of z/t (exact,
+// float) and the sum of exp(z/t - max) (wave max first, fp32 exponentials,
+// fp64 sums, the waves' pairs merged by thread 0). For a pair also
+//   T = sum_t exp(zp_t/t - M_p) expm1(d_t),  d_t = (zq_t - zp_t)/t,
+// with the same p weights as the p sum: summed over the chunks with weight
+// exp(M_p - lse_p) it is E_p[exp(d)] - 1 = exp(lse_q - lse_p) - 1, so the
+// normalisers' difference is known to the relative accuracy of T, not to the
+// absolute accuracy of either normaliser. d_t is formed from the raw logits
+// (their difference is exact when they are close). Where the p weight
+// underflows, the entry adds its q weight exp(zq_t/t - M_p) instead (the same
+// quantity, w expm1(d) = exp(zq/t - M_p) - w with w = 0); where a wave's p
+// entries are all -inf and its q entries are not, T is +inf, and so is the
+// chunk's if every p entry is -inf: the relative form does not exist there
+// and the plain difference of the normalisers is used.
+template <int VEC, bool PAIR>
+__device__ __forceinline__ void stats_chunk(const AccParams &a, int b, int i, int c) {
+  __shared__ float lds_m[2][kAccThreads / 64];
+  __shared__ double lds_s[3][kAccThreads / 64];
+  const int nrow = 2 * a.gamma + 1;
+  const int t0 = c * kChunk;
+  float zp[kPerThread], zq[kPerThread];
+  load_raw<VEC>(row_ptr(a, b, i), t0, a.V, zp);
+  if constexpr (PAIR) load_raw<VEC>(row_ptr(a, b, a.gamma + 1 + i), t0, a.V, zq);
+  float xp[kPerThread], xq[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int t = VEC == 4 ? t0 + ((e / 4) * kAccThreads + (int)threadIdx.x) * 4 + e % 4
+                           : t0 + e * kAccThreads + (int)threadIdx.x;
+    xp[e] = t < a.V ? zp[e] * a.inv_temp : kNegInf;
+    if constexpr (PAIR) xq[e] = t < a.V ? zq[e] * a.inv_temp : kNegInf;
+  }
+  float mp, mq = kNegInf;
+  double sp, sq = 0.0, tx = 0.0;
+  if constexpr (!PAIR) {
+    wave_max_sum(xp, mp, sp);
+  } else {
+    mp = kNegInf;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      mp = fmaxf(mp, xp[e]);
+      mq = fmaxf(mq, xq[e]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mp = fmaxf(mp, __shfl_xor(mp, o, 64));
+      mq = fmaxf(mq, __shfl_xor(mq, o, 64));
+    }
+    sp = 0.0;
+    if (mp != kNegInf) {
+      // q weight relative to mp = wq * exp(mq - mp) (inf where q lies far above p)
+      const float qp = mq == kNegInf ? 0.f : __builtin_amdgcn_exp2f((mq - mp) * kLog2e);
+      // an entry's term of T: wp expm1(d) = wq qp - wp. Below |d| = 1/8 it is
+      // wp times expm1(d) from its Taylor series; above, the difference loses
+      // at most a factor ~10 of fp32's precision. With wp = 0 (p's weight
+      // underflows) it is q's weight alone.
+      auto term = [&](int e, float wp, float wq) {
+        const float d = (zq[e] - zp[e]) * a.inv_temp;
+        return fabsf(d) < 0.125f ? wp * expm1_small(d) : fmaf(wq, qp, -wp);
+      };
+      // two entries summed in fp32 per fp64 addition: the pair sums of the
+      // weights are exact to ~6e-8 relative, less than each weight's own
+      // error; a pair of T terms that cancels loses absolute accuracy of
+      // ~6e-8 of its terms only, which moves the normalisers' gap by far
+      // less than it moves the residual weights
+      double s2[2] = {0.0, 0.0}, q2[2] = {0.0, 0.0}, t2[2] = {0.0, 0.0};
+#pragma unroll
+      for (int e = 0; e < kPerThread; e += 2) {
+        const float wp0 = __builtin_amdgcn_exp2f((xp[e] - mp) * kLog2e);
+        const float wq0 = __builtin_amdgcn_exp2f((xq[e] - mq) * kLog2e);
+        const float wp1 = __builtin_amdgcn_exp2f((xp[e + 1] - mp) * kLog2e);
+        const float wq1 = __builtin_amdgcn_exp2f((xq[e + 1] - mq) * kLog2e);
+        s2[(e >> 1) & 1] += (double)(wp0 + wp1);
+        q2[(e >> 1) & 1] += (double)(wq0 + wq1);
+        t2[(e >> 1) & 1] += (double)(term(e, wp0, wq0) + term(e + 1, wp1, wq1));
+      }
+      sp = s2[0] + s2[1];
+      sq = q2[0] + q2[1];
+      tx = t2[0] + t2[1];
+    } else if (mq != kNegInf) {
+      double q2[2] = {0.0, 0.0};
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) q2[e & 1] += (double)__builtin_amdgcn_exp2f((xq[e] - mq) * kLog2e);
+      sq = q2[0] + q2[1];
+      tx = __builtin_inf();  // q mass where p has none
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      sp += __shfl_xor(sp, o, 64);
+      sq += __shfl_xor(sq, o, 64);
+      tx += __shfl_xor(tx, o, 64);
+    }
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
-    lds_m[wave] = m;
-    lds_s[wave] = s;
+    lds_m[0][wave] = mp;
+    lds_s[0][wave] = sp;
+    lds_m[1][wave] = mq;
+    lds_s[1][wave] = sq;
+    lds_s[2][wave] = tx;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kAccThreads / 64; ++w) merge_ms(m, s, lds_m[w], lds_s[w]);
-    double *st = a.stats + (((size_t)b * nrow + k) * a.n_chunks + c) * 2;
-    st[0] = (double)m;
-    st[1] = s;
+    // the block max of each row, then every wave's sums rescaled to it (T
+    // with the p factors)
+    float Mp = kNegInf, Mq = kNegInf;
+    for (int w = 0; w < kAccThreads / 64; ++w) {
+      Mp = fmaxf(Mp, lds_m[0][w]);
+      Mq = fmaxf(Mq, lds_m[1][w]);
+    }
+    double Sp = 0.0, Sq = 0.0, Tx = 0.0;
+    for (int w = 0; w < kAccThreads / 64; ++w) {
+      if (lds_m[0][w] != kNegInf) {
+        const double f = (double)__builtin_amdgcn_exp2f((lds_m[0][w] - Mp) * kLog2e);
+        Sp += lds_s[0][w] * f;
+        Tx += lds_s[2][w] * f;
+      } else if (lds_s[2][w] != 0.0) {
+        Tx = __builtin_inf();
+      }
+      if (PAIR && lds_m[1][w] != kNegInf)
+        Sq += lds_s[1][w] * (double)__builtin_amdgcn_exp2f((lds_m[1][w] - Mq) * kLog2e);
+    }
+    double *st = a.stats + (((size_t)b * nrow + i) * a.n_chunks + c) * 2;
+    st[0] = (double)Mp;
+    st[1] = Sp;
+    if constexpr (PAIR) {
+      double *sq_ = a.stats + (((size_t)b * nrow + a.gamma + 1 + i) * a.n_chunks + c) * 2;
+      sq_[0] = (double)Mq;
+      sq_[1] = Sq;
+      a.cross[((size_t)b * a.gamma + i) * a.n_chunks + c] = Tx;
+    }
   }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kAccThreads) void accept_stats_kernel(AccParams a) {
+  const int c = blockIdx.x;
+  const int b = blockIdx.y / (a.gamma + 1), i = blockIdx.y % (a.gamma + 1);
+  if (i < a.gamma)
+    stats_chunk<VEC, true>(a, b, i, c);
+  else
+    stats_chunk<VEC, false>(a, b, i, c);
 }
 
 __device__ __forceinline__ double wave_incl_scan_f64(double v) {
@@ -184,9 +299,14 @@ __device__ __forceinline__ Offset split_offset(double c) {
 // Weights of the entries t .. t+3 (t = piece base + 256 j + 4 lane):
 // p = exp(z_t / T - lse_p), and max(0, p - q) (RESID). The fp64 normaliser
 // enters as an fp32 pair (hi + lo = lse to about 2^-48 relative), so it
-// carries no systematic fp32 rounding (that would scale p and q by different
-// constants, an error that does not cancel in p - q); the exponent itself is
-// formed in fp32, rounded per token like the final exponential. Loads are
+// carries no systematic fp32 rounding; the exponent itself is formed in fp32,
+// rounded per token like the final exponential. The residual is not formed
+// as the difference of two rounded probabilities: where q is close to p that
+// difference loses most of its digits, and the draw then lands on other
+// tokens than the exact residual's. It is p (1 - q/p) = -p expm1(e) with
+// e = ln(q/p) = (zq - zp) / T - (lse_q - lse_p), whose logit difference is
+// exact when the two logits are close and whose normaliser difference enters
+// as an fp32 pair as well, so r keeps the relative accuracy of p. Loads are
 // unconditional (clamped into the row, masked afterwards).
 template <int VEC, bool RESID>
 __device__ __forceinline__ void piece_load(const AccParams &a, const float *zp, const float *zq, int t,
@@ -212,16 +332,22 @@ __device__ __forceinline__ void piece_load(const AccParams &a, const float *zp, 
 }
 
 // p weights (pw) and, with RESID, residual weights (rw) of entries t .. t+3.
+// cp: lse_p; cd: lse_q - lse_p (both as fp32 pairs).
 template <bool RESID>
-__device__ __forceinline__ void piece_weights(const AccParams &a, Offset cp, Offset cq, int t,
+__device__ __forceinline__ void piece_weights(const AccParams &a, Offset cp, Offset cd, int t,
                                               const float (&zpv)[4], const float (&zqv)[4], float (&pw)[4],
                                               float (&rw)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float p = __builtin_amdgcn_exp2f((fmaf(zpv[e], a.inv_temp, -cp.hi) - cp.lo) * kLog2e);
     float r = p;
-    if constexpr (RESID)
-      r = fmaxf(0.f, p - __builtin_amdgcn_exp2f((fmaf(zqv[e], a.inv_temp, -cq.hi) - cq.lo) * kLog2e));
+    if constexpr (RESID) {
+      // ln(q/p); NaN (both logits -inf) and e >= 0 (q >= p) give no residual;
+      // expm1 from its series below 1/8, else exp - 1 (no cancellation there)
+      const float lr = fmaf(zqv[e] - zpv[e], a.inv_temp, -cd.hi) - cd.lo;
+      const float em1 = fabsf(lr) < 0.125f ? expm1_small(lr) : __builtin_amdgcn_exp2f(lr * kLog2e) - 1.f;
+      r = lr < 0.f ? -p * em1 : 0.f;
+    }
     const bool in = t + e < a.V;
     pw[e] = in ? p : 0.f;
     rw[e] = in ? r : 0.f;
@@ -254,12 +380,35 @@ __device__ __forceinline__ void row_normalisers(const AccParams &a, int b, doubl
   }
 }
 
+// lse_q_i - lse_p_i for draft position i (one wave; the result in every
+// lane): log1p(S) with S = sum over the chunks of exp(M_p - lse_p) T
+// (= E_p[exp(d)] - 1), which keeps the relative accuracy of T; where S is not
+// in (-1/2, 2^1000) (far-apart or degenerate distributions, where the plain
+// difference loses nothing that matters) the plain difference.
+__device__ __forceinline__ double normaliser_gap(const AccParams &a, int b, int i, const double *lse) {
+  const int lane = lane_id();
+  const int nrow = 2 * a.gamma + 1;
+  const double *st = a.stats + ((size_t)b * nrow + i) * a.n_chunks * 2;
+  const double *cr = a.cross + ((size_t)b * a.gamma + i) * a.n_chunks;
+  const double lp = lse[i];
+  double S = 0.0;
+  for (int c = lane; c < a.n_chunks; c += 64) {
+    if (st[2 * c] != -__builtin_inf())
+      S += cr[c] * exp(st[2 * c] - lp);
+    else if (cr[c] != 0.0)
+      S = __builtin_inf();  // q mass in a chunk where p has none
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) S += __shfl_xor(S, m, 64);
+  return S > -0.5 && S < 0x1p1000 ? log1p(S) : lse[a.gamma + 1 + i] - lp;
+}
+
 // Pieces [p0, p1) of the drawn row, one wave per piece: the fp64 sum of the
 // p weights of each piece into a.pieces (kind 1) and, with RESID, of the
 // residual weights (kind 0).
 template <int VEC, bool RESID>
 __device__ __forceinline__ void residual_pieces(const AccParams &a, int b, const float *zp, const float *zq,
-                                                Offset cp, Offset cq, int p0, int p1) {
+                                                Offset cp, Offset cd, int p0, int p1) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   double *pr = a.pieces + ((size_t)b * 2 + 0) * a.npieces;
   double *pp = a.pieces + ((size_t)b * 2 + 1) * a.npieces;
@@ -272,7 +421,7 @@ __device__ __forceinline__ void residual_pieces(const AccParams &a, int b, const
 #pragma unroll
     for (int j = 0; j < kPieceLoads; ++j) {
       float pw[4], rw[4];
-      piece_weights<RESID>(a, cp, cq, t0 + 256 * j, zpv[j], zqv[j], pw, rw);
+      piece_weights<RESID>(a, cp, cd, t0 + 256 * j, zpv[j], zqv[j], pw, rw);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sp += (double)pw[e];
@@ -299,6 +448,7 @@ __device__ __forceinline__ void residual_pieces(const AccParams &a, int b, const
 template <int VEC>
 __global__ __launch_bounds__(kResThreads) void accept_residual_kernel(AccParams a) {
   __shared__ double lse[2 * kMaxGamma + 1];
+  __shared__ double gap_s;  // lse_q_n - lse_p_n of the drawn pair
   __shared__ int n_s;
   const int b = blockIdx.x, s = blockIdx.y;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -327,13 +477,17 @@ __global__ __launch_bounds__(kResThreads) void accept_residual_kernel(AccParams 
     }
     const uint64_t rej = ~__ballot(acc);
     const int n = min(g, rej != 0 ? (int)__builtin_ctzll(rej) : 64);
-    if (lane == 0) n_s = n;
+    const double gap = n < g ? normaliser_gap(a, b, n, lse) : 0.0;
+    if (lane == 0) {
+      n_s = n;
+      gap_s = gap;
+    }
     if (s == 0) {
       if (lane == 0) {
         a.n_accepted[b] = n;
         a.seq_n[b] = n;
         a.seq_lse[2 * (size_t)b] = lse[n];
-        a.seq_lse[2 * (size_t)b + 1] = n < g ? lse[g + 1 + n] : 0.0;
+        a.seq_lse[2 * (size_t)b + 1] = gap;
       }
       for (int t = lane; t <= g; t += 64) {
         if (t < n)
@@ -348,12 +502,12 @@ __global__ __launch_bounds__(kResThreads) void accept_residual_kernel(AccParams 
   const float *zp = row_ptr(a, b, n);
   const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
   const Offset cp = split_offset(lse[n]);
-  const Offset cq = split_offset(n < g ? lse[g + 1 + n] : 0.0);
+  const Offset cd = split_offset(gap_s);
   const int p0 = s * a.pps, p1 = min(p0 + a.pps, a.npieces);
   if (n < g)
-    residual_pieces<VEC, true>(a, b, zp, zq, cp, cq, p0, p1);
+    residual_pieces<VEC, true>(a, b, zp, zq, cp, cd, p0, p1);
   else
-    residual_pieces<VEC, false>(a, b, zp, zq, cp, cq, p0, p1);
+    residual_pieces<VEC, false>(a, b, zp, zq, cp, cd, p0, p1);
 }
 
 // Block sums (fp64, any order) of two values per thread.
@@ -382,7 +536,7 @@ __device__ __forceinline__ void block_sum2_f64(double &x, double &y, double (*ld
 // piece's last entry with mass (-1 if none).
 template <int VEC, bool RESID>
 __device__ __forceinline__ int piece_rescan(const AccParams &a, const float *zp, const float *zq, Offset cp,
-                                            Offset cq, int p, double before, double thr, int *last) {
+                                            Offset cd, int p, double before, double thr, int *last) {
   const int lane = lane_id();
   int y = -1, sl = -1;
   const int t0 = p * kPiece + 4 * lane;
@@ -393,7 +547,7 @@ __device__ __forceinline__ int piece_rescan(const AccParams &a, const float *zp,
   for (int j = 0; j < kPieceLoads; ++j) {
     const int t = t0 + 256 * j;
     float pw[4], rw[4];
-    piece_weights<RESID>(a, cp, cq, t, zpv[j], zqv[j], pw, rw);
+    piece_weights<RESID>(a, cp, cd, t, zpv[j], zqv[j], pw, rw);
     double loc[4], r = 0.0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -520,14 +674,14 @@ __global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(AccParams a) 
   const float *zp = row_ptr(a, b, n);
   const float *zq = n < g ? row_ptr(a, b, g + 1 + n) : zp;
   const Offset cp = split_offset(a.seq_lse[2 * (size_t)b]);
-  const Offset cq = split_offset(a.seq_lse[2 * (size_t)b + 1]);
+  const Offset cd = split_offset(a.seq_lse[2 * (size_t)b + 1]);
   int y = -1, last = -1;
   const int piece = piece_s >= 0 ? piece_s : lastp_s;  // no crossing: the last piece with mass
   if (piece >= 0) {
     const double before = piece_s >= 0 ? before_s : 0.0;
     const double t = piece_s >= 0 ? thr : __builtin_inf();
-    y = resid ? piece_rescan<VEC, true>(a, zp, zq, cp, cq, piece, before, t, &last)
-              : piece_rescan<VEC, false>(a, zp, zq, cp, cq, piece, before, t, &last);
+    y = resid ? piece_rescan<VEC, true>(a, zp, zq, cp, cd, piece, before, t, &last)
+              : piece_rescan<VEC, false>(a, zp, zq, cp, cd, piece, before, t, &last);
     if (y < 0) y = last;
   }
   if (lane == 0) a.out_tokens[(size_t)b * (g + 1) + n] = max(0, y);
@@ -536,8 +690,8 @@ __global__ __launch_bounds__(kDrawThreads) void accept_draw_kernel(AccParams a) 
 struct AccPlan {
   int n_chunks;
   int npieces, pps, slices;  // pieces per row, per residual slice, slices per sequence
-  size_t pieces_off, lse_off, n_off;
-  size_t ws_bytes;  // chunk statistics, piece sums, the drawn pair's normalisers, n
+  size_t cross_off, pieces_off, lse_off, n_off;
+  size_t ws_bytes;  // chunk statistics, cross sums, piece sums, the drawn row's normalisers, n
 };
 
 AccPlan plan_accept(int64_t B, int64_t gamma, int64_t V) {
@@ -549,7 +703,8 @@ AccPlan plan_accept(int64_t B, int64_t gamma, int64_t V) {
   const int64_t sl = std::min<int64_t>(p.npieces, want);
   p.pps = (int)sdh::ceil_div(p.npieces, sl);
   p.slices = (int)sdh::ceil_div(p.npieces, p.pps);
-  p.pieces_off = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
+  p.cross_off = sdh::align_up((size_t)B * (2 * gamma + 1) * p.n_chunks * 2 * 8);
+  p.pieces_off = p.cross_off + sdh::align_up((size_t)B * gamma * p.n_chunks * 8);
   p.lse_off = p.pieces_off + sdh::align_up((size_t)B * 2 * p.npieces * 8);
   p.n_off = p.lse_off + sdh::align_up((size_t)B * 2 * 8);
   p.ws_bytes = p.n_off + sdh::align_up((size_t)B * 4);
@@ -598,6 +753,7 @@ sd_status launch_accept(const float *target_logits, const float *draft_logits, c
   a.out_tokens = out_tokens;
   char *ws = reinterpret_cast<char *>(workspace);
   a.stats = reinterpret_cast<double *>(ws);
+  a.cross = reinterpret_cast<double *>(ws + p.cross_off);
   a.pieces = reinterpret_cast<double *>(ws + p.pieces_off);
   a.seq_lse = reinterpret_cast<double *>(ws + p.lse_off);
   a.seq_n = reinterpret_cast<int32_t *>(ws + p.n_off);
@@ -612,7 +768,7 @@ sd_status launch_accept(const float *target_logits, const float *draft_logits, c
   // 16-byte loads need every row 16-byte aligned
   const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0 &&
                    (gamma == 0 || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
-  const dim3 g_stats((unsigned)p.n_chunks, (unsigned)(batch * (2 * gamma + 1)));
+  const dim3 g_stats((unsigned)p.n_chunks, (unsigned)(batch * (gamma + 1)));
   const dim3 g_res((unsigned)batch, (unsigned)p.slices);
   if (vec) {
     accept_stats_kernel<4><<<g_stats, kAccThreads, 0, st>>>(a);

@@ -75,6 +75,9 @@ def test_golden_cases_on_gpu():
     (1, 4, 128256, 2.0, 1.5, 1.0),          # one sequence: its drawn row over 126 one-piece slices
     (2048, 1, 32000, 2.0, 0.5, 1.0),        # many sequences: one slice of all 32 pieces each
     (8, 0, 128256, 2.0, None, 1.0),         # bonus only over the full vocabulary
+    (256, 4, 32000, 30.0, 0.5, 1.0),        # peaked logits: p and q nearly one-hot
+    (256, 4, 32000, 2.0, 0.002, 1.0),       # q within 0.2% of p: rare rejections, tiny residual mass
+    (256, 4, 32000, 2.0, 0.5, 0.05),        # low temperature: peaked softmaxes from ordinary logits
 ])
 def test_accept_parity(B, gamma, V, std, noise, temp):
     say(f"accept B={B} gamma={gamma} V={V} noise={noise} temp={temp}")
@@ -111,6 +114,27 @@ def test_identical_and_disjoint_distributions():
     n, out = run_accept(zt2, zd2, x2, ua, us)
     assert (n == 0).all() and (out[:, 0] < V // 2).all() and (out[:, 1:] == -1).all()
     check_accept("accept disjoint supports", n, out, zt2, zd2, x2, ua, us)
+
+
+@pytest.mark.parametrize("noise", [0.002, 0.0002])
+def test_rejections_with_tiny_residual_mass(noise):
+    """q within a fraction of a percent of p, and accept uniforms just under 1
+    at the first draft: about half the sequences reject there although p and q
+    barely differ, so the correction is drawn from a residual max(0, p - q)
+    whose total mass is ~1e-4 to 1e-3 of the distribution, spread over
+    thousands of tokens. Each residual weight is a difference of two nearly
+    equal probabilities."""
+    B, gamma, V = 512, 4, 32000
+    seed = 4242 + int(noise * 1e5)
+    zt = logits(seed, 8, (B, gamma + 1, V), 2.0, "cuda")
+    zd = logits(seed, 9, (B, gamma, V), noise, "cuda", base=zt[:, :gamma]).contiguous()
+    x = gumbel_tokens(seed, zd)
+    ua = dyadic_uniforms(seed, 11, (B, gamma), "cuda")
+    ua[:, 0] = 1.0 - 2.0 ** -16
+    us = dyadic_uniforms(seed, 12, (B, gamma + 1), "cuda")
+    n, out = run_accept(zt, zd, x, ua, us)
+    stats = check_accept(f"accept tiny residual noise={noise}", n, out, zt, zd, x, ua, us)
+    assert (n == 0).sum() > B // 4, stats
 
 
 def test_uniforms_planted_next_to_thresholds():
