@@ -116,24 +116,26 @@ def test_identical_and_disjoint_distributions():
     check_accept("accept disjoint supports", n, out, zt2, zd2, x2, ua, us)
 
 
-@pytest.mark.parametrize("noise", [0.002, 0.0002])
-def test_rejections_with_tiny_residual_mass(noise):
+@pytest.mark.parametrize("noise,temp,V", [(0.002, 1.0, 32000), (0.0002, 1.0, 32000), (0.0002, 0.5, 32000),
+                                          (0.0002, 1.0, 32001)])
+def test_rejections_with_tiny_residual_mass(noise, temp, V):
     """q within a fraction of a percent of p, and accept uniforms just under 1
     at the first draft: about half the sequences reject there although p and q
     barely differ, so the correction is drawn from a residual max(0, p - q)
     whose total mass is ~1e-4 to 1e-3 of the distribution, spread over
     thousands of tokens. Each residual weight is a difference of two nearly
-    equal probabilities."""
-    B, gamma, V = 512, 4, 32000
-    seed = 4242 + int(noise * 1e5)
+    equal probabilities. Also at temperature 0.5 and with an odd vocabulary
+    (4-byte loads)."""
+    B, gamma = 512, 4
+    seed = 4242 + int(noise * 1e5) + V % 7 + int(temp * 10)
     zt = logits(seed, 8, (B, gamma + 1, V), 2.0, "cuda")
     zd = logits(seed, 9, (B, gamma, V), noise, "cuda", base=zt[:, :gamma]).contiguous()
-    x = gumbel_tokens(seed, zd)
+    x = gumbel_tokens(seed, zd, temp)
     ua = dyadic_uniforms(seed, 11, (B, gamma), "cuda")
     ua[:, 0] = 1.0 - 2.0 ** -16
     us = dyadic_uniforms(seed, 12, (B, gamma + 1), "cuda")
-    n, out = run_accept(zt, zd, x, ua, us)
-    stats = check_accept(f"accept tiny residual noise={noise}", n, out, zt, zd, x, ua, us)
+    n, out = run_accept(zt, zd, x, ua, us, temp)
+    stats = check_accept(f"accept tiny residual noise={noise} T={temp} V={V}", n, out, zt, zd, x, ua, us, temp)
     assert (n == 0).sum() > B // 4, stats
 
 
