@@ -116,8 +116,9 @@ __device__ __forceinline__ void wave_max_sum(const float (&x)[kPerThread], float
 
 // One block per (sequence, draft position i, chunk): rows p_i and q_i of the
 // chunk (i < gamma), or p_gamma alone. Per row the chunk's max of z/t (exact,
-// float) and the sum of exp(z/t - max) (wave max first, fp32 exponentials,
-// fp64 sums, the waves' pairs merged by thread 0). For a pair also
+// float) and the sum of exp(z/t - max) (wave max first, fp32 exponentials
+// added in pairs in fp32, then in fp64; the waves' sums merged by thread 0).
+// For a pair also
 //   T = sum_t exp(zp_t/t - M_p) expm1(d_t),  d_t = (zq_t - zp_t)/t,
 // with the same p weights as the p sum: summed over the chunks with weight
 // exp(M_p - lse_p) it is E_p[exp(d)] - 1 = exp(lse_q - lse_p) - 1, so the
@@ -125,7 +126,8 @@ __device__ __forceinline__ void wave_max_sum(const float (&x)[kPerThread], float
 // absolute accuracy of either normaliser. d_t is formed from the raw logits
 // (their difference is exact when they are close). Where the p weight
 // underflows, the entry adds its q weight exp(zq_t/t - M_p) instead (the same
-// quantity, w expm1(d) = exp(zq/t - M_p) - w with w = 0); where a wave's p
+// quantity, w expm1(d) = exp(zq/t - M_p) - w with w = 0; its |d| is large, so
+// the term is formed as that difference); where a wave's p
 // entries are all -inf and its q entries are not, T is +inf, and so is the
 // chunk's if every p entry is -inf: the relative form does not exist there
 // and the plain difference of the normalisers is used.
