@@ -121,6 +121,35 @@ def test_snapkv_select_parity(case):
     assert near <= max(1, len(lens) * Hkv // 8)
 
 
+@pytest.mark.parametrize("ramp", [16.0, -16.0])
+def test_snapkv_with_trending_scores(ramp):
+    """Scores that rise (or fall) by 16 over each sequence: every window query
+    has a component along one direction u that the keys carry with a weight
+    growing in the position, so the statistics pass's running maximum keeps
+    moving up through the sequence (rising) or is set at its start (falling),
+    and the votes span some seven orders of magnitude."""
+    Hq, Hkv, d, W, pool, budget = 8, 2, 128, 8, 7, 256
+    lens = [3000, 1200]
+    say(f"snapkv trending scores ramp={ramp}")
+    kv_t = paged_kv(77, lens, Hkv, d, BF16, "cuda", shuffle=True)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    u = torch.randn(d, generator=g, device="cuda")
+    u /= u.norm()
+    P = kv_t.page_size
+    for b, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        page = kv_t.page_table[b].long()[t // P]
+        rows = kv_t.k_pages[page, :, t % P, :].float() + (ramp * t / L)[:, None, None] * u
+        kv_t.k_pages[page, :, t % P, :] = rows.to(BF16)
+    q_obs = (queries(77, 4, (len(lens), W, Hq, d), torch.float32, "cuda", scale=d ** -0.5) + u).to(BF16)
+    idx, sel = run_snapkv(kv_t, q_obs, W, Hq, pool, budget)
+    idx_ref, sel_ref, pooled = oracle.snapkv_select(q_obs, kv_t.k_pages, kv_t.page_table, kv_t.kv_lens,
+                                                    W, pool, budget, 1.0, return_pooled=True)
+    near = check_selection(idx.cpu().numpy(), idx_ref, sel.cpu().numpy(), sel_ref, pooled, W, budget)
+    record(f"snapkv trending scores ramp={ramp}", units=len(lens) * Hkv, near_tie=near)
+    assert near <= 1
+
+
 SCALE_CASES = [
     # name, q_obs scale folded in, softmax_scale passed
     ("unscaled-q-inv-sqrt-d", 1.0, 128 ** -0.5),
