@@ -117,6 +117,32 @@ def test_topk_select_parity(case):
     assert torch.equal(idx, idx2)
 
 
+@pytest.mark.parametrize("ramp", [30.0, -30.0])
+def test_topk_select_with_trending_scores(ramp):
+    """Scores rising (or falling) by 30 over each sequence along one direction
+    u of every query: the budget's keys crowd at one end of the sequence, far
+    from where a uniform sample of the scores would put the threshold."""
+    Hq, Hkv, d, budget = 8, 2, 128, 256
+    lens = [6000, 2500]
+    say(f"topk select trending scores ramp={ramp}")
+    kv_t = paged_kv(78, lens, Hkv, d, BF16, "cuda", shuffle=True)
+    g = torch.Generator(device="cuda").manual_seed(78)
+    u = torch.randn(d, generator=g, device="cuda")
+    u /= u.norm()
+    P = kv_t.page_size
+    for b, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        page = kv_t.page_table[b].long()[t // P]
+        rows = kv_t.k_pages[page, :, t % P, :].float() + (ramp * t / L)[:, None, None] * u
+        kv_t.k_pages[page, :, t % P, :] = rows.to(BF16)
+    q = (queries(78, 2, (len(lens), 1, Hq, d), torch.float32, "cuda", scale=d ** -0.5) + u).to(BF16)
+    idx, sel = run_topk(kv_t, q, Hq, budget)
+    rows = [(b, h) for b in range(len(lens)) for h in range(Hq)]
+    near = check_selection(kv_t, q, idx, sel, budget, lens, rows)
+    say(f"  rows={len(rows)} near-tie rows={near}")
+    assert near <= 1
+
+
 def test_topk_select_max_len_above_lengths_and_exact_ties():
     """max_kv_len larger than every length; a cache whose keys repeat one row
     (every score tied) keeps the lowest positions."""
