@@ -557,14 +557,14 @@ __device__ __forceinline__ void stream_operands(const lds_u32x4 *ring, int sl, S
 }
 
 // One segment [s_begin, s_end) of unit (b, kvh) through this wave's LDS ring
-// at `lds` (Lay::kBytes): st ends holding the segment's (m, l, o).
-template <int NB, bool SPARSE>
+// of RING steps at `lds` (Lay::kBytes): st ends holding the segment's (m, l, o).
+template <int NB, bool SPARSE, int RING>
 __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *lds, int b, int kvh, int s_begin,
                                                int s_end, AttnState<__bf16, 128, NB> &st) {
   constexpr int D = 128;
   constexpr int QV = StepRegs<__bf16, D>::kVec;
   constexpr int DPL = D / 16;
-  constexpr int kStreamRing = stream_ring<NB>();
+  constexpr int kStreamRing = RING;
   using Lay = StreamLayout<SPARSE, kStreamRing>;
   lds_u32x4 *ring = (lds_u32x4 *)lds;
   lds_char *table = lds + Lay::kRingBytes;
@@ -737,18 +737,18 @@ __device__ __forceinline__ void stream_segment(const AttnParams &a, lds_char *ld
   }
 }
 
-template <int NB, bool SPARSE>
+template <int NB, bool SPARSE, int RING>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB <= 3 ? 2 : 1)))
 void attn_stream_kernel(AttnParams a) {
   constexpr int D = 128;
   constexpr int DPL = D / 16;
-  using Lay = StreamLayout<SPARSE, stream_ring<NB>()>;
+  using Lay = StreamLayout<SPARSE, RING>;
   __shared__ __attribute__((aligned(16))) char lds_raw[Lay::kBytes];
   const int g = lane_id() >> 4, r = lane_id() & 15;
 
   attn_for_each_segment(a, [&](int b, int kvh, int s_begin, int s_end, size_t slot) {
     AttnState<__bf16, D, NB> st;
-    stream_segment<NB, SPARSE>(a, (lds_char *)lds_raw, b, kvh, s_begin, s_end, st);
+    stream_segment<NB, SPARSE, RING>(a, (lds_char *)lds_raw, b, kvh, s_begin, s_end, st);
 
     // Partial of this segment: unnormalised o (relative to m), (m, l) in log2 units.
 #pragma unroll
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(64 * kUnitWaves) void attn_unit_kernel(AttnParams a
   lds_char *mine = (lds_char *)lds_raw + wv * Lay::kBytes;
   AttnState<__bf16, D, NB> st;
   if (s0 < s1) {
-    stream_segment<NB, SPARSE>(a, mine, b, kvh, s0, s1, st);
+    stream_segment<NB, SPARSE, stream_ring<NB>()>(a, mine, b, kvh, s0, s1, st);
   } else {
     st.m[0] = kNegInf;
     st.l[0] = 0.f;
@@ -962,7 +962,8 @@ sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
   // bf16 with head_dim 128 streams K/V through the LDS ring; fp32 caches and
   // head_dim 64 use the register ring
   constexpr bool kStream = EltInfo<T>::bytes == 2 && D == 128;
-  const void *kernel = kStream ? reinterpret_cast<const void *>(attn_stream_kernel<NB, SPARSE>)
+  constexpr int kRing = stream_ring<NB>();
+  const void *kernel = kStream ? reinterpret_cast<const void *>(attn_stream_kernel<NB, SPARSE, kRing>)
                                : reinterpret_cast<const void *>(attn_split_kernel<T, D, NB, SPARSE>);
   if constexpr (kStream && NB == 1) {
     // every unit in one round of the chip, each short: one workgroup per unit
@@ -974,8 +975,23 @@ sd_status launch_nb(AttnParams &a, void *out, float *lse, hipStream_t st) {
   }
   static int cache[sdh::kMaxDevices] = {};  // resident waves of this instantiation per device
   a.sc.waves = sdh::resident_waves(kernel, kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache);
-  if constexpr (kStream)
-    attn_stream_kernel<NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+  if constexpr (kStream && NB == 1 && SPARSE) {
+    // Drafts with more units than the four-step ring has resident waves (the
+    // ragged batch's 2048 units and more) run with two-step rings: twice the
+    // waves fit, one unit each where the four-step grid would give a wave
+    // two. One tile at four steps stays for the rest (1024 units of the
+    // 32k batch: every wave one unit either way).
+    const int64_t units = (int64_t)a.B * a.Hkv;
+    if (units > a.sc.waves) {
+      static int cache2[sdh::kMaxDevices] = {};
+      a.sc.waves = sdh::resident_waves(reinterpret_cast<const void *>(attn_stream_kernel<1, true, 2>),
+                                       kSimdsPerCU * AttnTuning<T, NB>::kWavesPerEU, cache2);
+      attn_stream_kernel<1, true, 2><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+    } else {
+      attn_stream_kernel<1, true, kRing><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
+    }
+  } else if constexpr (kStream)
+    attn_stream_kernel<NB, SPARSE, kRing><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   else
     attn_split_kernel<T, D, NB, SPARSE><<<(unsigned)a.sc.waves, 64, 0, st>>>(a);
   const int total_groups = a.B * a.Hkv * ((a.rows + 3) / 4);
