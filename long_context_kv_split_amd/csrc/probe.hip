@@ -2,7 +2,7 @@
 //
 // MagicDec (deep notes on papercache.org, §3.2) argues that at long context
 // verification and drafting are bound by loading the KV cache, so the ceiling
-// every attention kernel here is judged against is the read bandwidth HBM can
+// every attention kernel here is measured against is the read bandwidth HBM can
 // actually deliver, next to the nominal figure. This kernel measures that
 // ceiling: every wave streams one contiguous slice of the buffer with 16-byte
 // vector loads, eight per lane in flight (8 KB per wave and round, each load
